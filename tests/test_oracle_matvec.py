@@ -1,0 +1,65 @@
+"""Pins of oracle/matvec.py against codec-free brute force and closed forms."""
+from itertools import product
+
+import numpy as np
+
+from oracle import codec as C
+from oracle import matvec as M
+from sub_bit_moe_amd import synth
+
+
+def test_all_2x4_ternary_matrices(odict):
+    mats = np.array(list(product(range(3), repeat=8)), dtype=np.uint8).reshape(-1, 2, 4)
+    sym = mats.reshape(-1, 4)                       # 2*6561 rows, 4 cols
+    codes, row_off = C.encode_matrix(sym, odict["child"])
+    rng = np.random.default_rng(7)
+    scales = synth.row_scales(rng, sym.shape[0])
+    x = synth.activations(rng, 1, 4)
+    y = M.matvec(codes, row_off, scales, odict["sym28"], odict["lens"], 4, x)
+    ref = M.dense_ternary_matvec(synth.symbols_to_ternary(sym), scales, x)
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=0)
+
+
+def _enc(odict, sym):
+    return C.encode_matrix(sym, odict["child"])
+
+
+def test_unit_vector_ones_zero_and_linearity(odict):
+    rng = np.random.default_rng(9)
+    rows, cols = 37, 210
+    sym = synth.ternary_symbols(rng, rows, cols, 0.886)
+    tern = synth.symbols_to_ternary(sym).astype(np.float64)
+    s = synth.row_scales(rng, rows)
+    codes, row_off = _enc(odict, sym)
+    args = (codes, row_off, s, odict["sym28"], odict["lens"], cols)
+    for j in (0, 1, 101, cols - 1):
+        e = np.zeros((1, cols))
+        e[0, j] = 1.0
+        assert np.array_equal(M.matvec(*args, e)[0], s.astype(np.float64) * tern[:, j])
+    ones = np.ones((1, cols))
+    npos = (sym == 2).sum(1)
+    nneg = (sym == 1).sum(1)
+    assert np.array_equal(M.matvec(*args, ones)[0], s.astype(np.float64) * (npos - nneg))
+    zc, zo = _enc(odict, np.zeros((rows, cols), np.uint8))
+    assert not M.matvec(zc, zo, s, odict["sym28"], odict["lens"], cols, ones).any()
+    a = synth.activations(rng, 1, cols).astype(np.float64)
+    b = synth.activations(rng, 1, cols).astype(np.float64)
+    np.testing.assert_allclose(M.matvec(*args, 2 * a - b),
+                               2 * M.matvec(*args, a) - M.matvec(*args, b), rtol=1e-12, atol=1e-12)
+
+
+def test_rows_subset_matches_full(odict):
+    rng = np.random.default_rng(10)
+    sym = synth.ternary_symbols(rng, 20, 64, 0.886)
+    s = synth.row_scales(rng, 20)
+    x = synth.activations(rng, 3, 64)
+    codes, row_off = _enc(odict, sym)
+    full = M.matvec(codes, row_off, s, odict["sym28"], odict["lens"], 64, x)
+    sub = M.matvec_rows(codes, row_off, s, odict["sym28"], odict["lens"], 64, x, [0, 5, 19])
+    np.testing.assert_allclose(sub, full[:, [0, 5, 19]], rtol=1e-13)
+
+
+def test_dequantize_symbol_map():
+    sym = np.array([[0, 1, 2]], np.uint8)
+    w = C.dequantize(sym, np.array([0.5], np.float16))
+    assert w.tolist() == [[0.0, -0.5, 0.5]]
