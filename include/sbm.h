@@ -1,0 +1,174 @@
+/*
+ * sbm.h -- C ABI of libsbm: dictionary-coded ternary MoE expert weights,
+ * decoded on the fly inside a fused decode + matrix-vector kernel on gfx950.
+ *
+ * Sources (by page title and section):
+ *   [QMoE]  "QMoE: Practical Sub-1-Bit Compression of Trillion-Parameter
+ *           Models", sections "The Fixed-to-Variable Dictionary Code"
+ *           (Algorithm 1, Eq. 2, Figure 4) and "The GPU Decoding Kernel"
+ *           (row offsets, ternary grid, fused decode-and-multiply, trie
+ *           encoder, skipping experts without tokens).
+ *   [M8.5]  "M8.5 - Extreme Weight Compression and Representations",
+ *           0x08A (reference decoder: expand a row's codewords, map symbols
+ *           through [zero, negative, positive]) and 0x08B (operator contract,
+ *           codebook checksum).
+ *
+ * Conventions
+ *   Symbols: 0 = zero, 1 = negative (w_min = -s_r), 2 = positive (+s_r).
+ *   Dictionary: 65536 entries, entry c = words[2c] (pair count k in bits 0-3,
+ *     symbol i in bits 4+2i, i = 0..13) and words[2c+1] (k again, symbols
+ *     14..27).  Entries are ordered from most to least probable under the
+ *     i.i.d. model P(0)=p0, P(1)=P(2)=(1-p0)/2; equally probable entries (same
+ *     length and nonzero count) are ordered by the colexicographic rank of the
+ *     nonzero positions, then by the sign index sum_i [symbol at p_i==2]*2^i.
+ *   Encoded matrix (rows x cols, cols even):
+ *     codes   uint16  row streams concatenated in row order (greedy longest
+ *                     prefix, rows independent, no codeword spans two rows)
+ *     row_off uint32  rows+1 matrix-local codeword offsets, row_off[0] = 0
+ *     bstart  uint32  ceil(n_codes/SBM_BLOCK) entries: the linear symbol
+ *                     position row*cols+col where codeword b*SBM_BLOCK starts
+ *     scales  fp16    one per row (stored as uint16 bit patterns)
+ *   Operator contract ([M8.5] 0x08A/0x08B): input fp16; decoded operand
+ *   ternary; fp32 accumulation; scale applied in fp32 in the epilogue; output
+ *   fp16 or fp32.
+ *
+ * Ownership: the caller allocates and frees every buffer; the library keeps
+ * no pointer after a call returns.  GPU calls are enqueued on the caller's
+ * stream (a hipStream_t passed as void*; NULL = the null stream) and return
+ * before the work completes.  Host-checkable errors return a negative status
+ * synchronously and sbm_last_error() (thread-local) describes it.  Device
+ * resident data (codes, offsets, ids) is trusted by the fused kernel, which
+ * bounds every index it derives; out-of-range expert ids are skipped and
+ * counted in the workspace error word.
+ */
+#ifndef SBM_H
+#define SBM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SBM_DICT_ENTRIES 65536
+#define SBM_DICT_WORDS   131072
+#define SBM_MAX_RUN      28
+#define SBM_BLOCK        512      /* codewords per block-offset entry */
+#define SBM_CODE_ALIGN   8        /* matrix code bases must be multiples of this */
+
+typedef enum {
+  SBM_OK = 0,
+  SBM_EINVAL = -1,      /* null pointer, bad size or parameter */
+  SBM_EODD_WIDTH = -2,  /* cols is odd: codewords expand to pairs */
+  SBM_ECORRUPT = -3,    /* a code stream does not decode to its row widths */
+  SBM_EDICT = -4,       /* dictionary is malformed or not in canonical order */
+  SBM_ERANGE = -5,      /* a size exceeds what the layout can address */
+  SBM_ENOSPACE = -6,    /* output capacity or workspace too small */
+  SBM_EHIP = -7         /* a HIP runtime call failed (message in sbm_last_error) */
+} sbm_status;
+
+/* Flags of sbm_moe_fused_decode_matvec. */
+#define SBM_F_RELU    1u  /* y = max(y, 0) after scaling (Switch experts are ReLU FFNs) */
+#define SBM_F_OUT_F32 2u  /* y is float32 (default fp16) */
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* sbm_last_error(void);
+const char* sbm_version(void);
+
+/* ------------------------------------------------------------ dictionary */
+
+/* [QMoE] Algorithm 1 / Figure 4: the canonical 65536-entry dictionary for
+ * zero probability p0 (0.5 <= p0 < 1; the page's static table uses 0.885).
+ * out_words: host, SBM_DICT_WORDS uint32.  out_checksum (may be NULL):
+ * FNV-1a 64 over the words' little-endian bytes. */
+int sbm_build_dictionary(double p0, uint32_t* out_words, uint64_t* out_checksum);
+
+/* FNV-1a 64 of the 512 KB packed table (the [M8.5] 0x08B codebook checksum). */
+int sbm_dictionary_checksum(const uint32_t* words, uint64_t* out_checksum);
+
+/* Compact decode image for the fused kernel, derived from a canonical
+ * dictionary (every entry has at most 3 nonzeros; classes contiguous; in-class
+ * order as above).  Host in, host out; the caller uploads the image to the
+ * device.  Returns SBM_EDICT if the dictionary does not have that structure. */
+size_t sbm_dict_image_bytes(void);
+int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes);
+
+/* ----------------------------------------------------------- host codec */
+
+/* [QMoE] "Encoding": greedy longest-prefix walk of each row over a trie of the
+ * dictionary.  sym: host uint8 [rows x cols] row-major, values 0/1/2.
+ * Size query: n_codes receives the number of codewords. */
+int sbm_encode_size(const uint8_t* sym, int32_t rows, int32_t cols,
+                    const uint32_t* words, uint64_t* n_codes);
+
+/* Fill codes (capacity entries), row_off (rows+1) and, if bstart is not NULL,
+ * the ceil(n/SBM_BLOCK) block start positions.  n_codes receives the count. */
+int sbm_encode_matrix(const uint8_t* sym, int32_t rows, int32_t cols,
+                      const uint32_t* words, uint16_t* codes, uint64_t capacity,
+                      uint32_t* row_off, uint32_t* bstart, uint64_t* n_codes);
+
+/* Block start positions of an existing stream (host). */
+int sbm_block_starts(const uint16_t* codes, uint64_t n_codes, const uint32_t* words,
+                     uint32_t* bstart);
+
+/* Host check that every row of a stream decodes to exactly cols symbols and
+ * that row_off is monotone and ends at n_codes.  SBM_ECORRUPT otherwise. */
+int sbm_validate_stream(const uint16_t* codes, uint64_t n_codes, const uint32_t* row_off,
+                        int32_t rows, int32_t cols, const uint32_t* words);
+
+/* -------------------------------------------------------------- GPU path */
+
+/* One matrix of an expert stack, as the fused kernel sees it (device table). */
+typedef struct {
+  uint64_t code_base;   /* first codeword in `codes` (multiple of SBM_CODE_ALIGN) */
+  uint64_t off_base;    /* first of the matrix's rows+1 entries in `row_off` */
+  uint64_t scale_base;  /* first of the matrix's `rows` entries in `scales` */
+  uint64_t blk_base;    /* first of the matrix's block starts in `bstart` */
+  uint32_t n_codes;     /* codewords of the matrix */
+  int32_t rows;
+  int32_t cols;
+  int32_t reserved;
+} sbm_matrix_desc;
+
+/* [M8.5] 0x08A reference decode on the GPU: one matrix to symbols.
+ * codes, row_off, words, out_sym: device.  out_sym: uint8 [rows x cols].
+ * One thread per row expands its codewords from the packed words; a row whose
+ * stream does not total cols symbols is written as far as it goes and the
+ * count of such rows is added to *bad_rows (device uint32, may be NULL). */
+int sbm_decode_ref(const uint16_t* codes, const uint32_t* row_off, int32_t rows, int32_t cols,
+                   const uint32_t* words, uint8_t* out_sym, uint32_t* bad_rows, void* stream);
+
+/* Workspace bytes needed by sbm_moe_fused_decode_matvec. */
+size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
+
+/* [QMoE] "The GPU Decoding Kernel", grouped over experts: for every token t,
+ *   y[t, r] = act( s_r * sum_j W_e[r, j] * x[t, j] ),  e = expert_ids[t],
+ * where W_e is expert e's ternary matrix (rows x cols, the same shape for all
+ * experts of the call) decoded from its code stream without materialising it.
+ * Experts without tokens are skipped.  Tokens with an id outside [0, n_experts)
+ * produce no output row and are counted in the workspace error word.
+ *   codes/row_off/bstart/scales: device arrays addressed through `experts`
+ *   experts:    device sbm_matrix_desc[n_experts]
+ *   dict_image: device copy of sbm_dict_image() output
+ *   x:          device fp16 [n_tokens x cols];  expert_ids: device int32 [n_tokens]
+ *   y:          device [n_tokens x rows], fp16 (or fp32 with SBM_F_OUT_F32)
+ *   workspace:  device, at least sbm_workspace_bytes(n_experts, n_tokens)
+ * n_tokens may be 0 (nothing is launched).  cols must be even, 2..65536;
+ * rows 1..2^24; rows*cols*6 < 2^30. */
+int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
+                                const uint32_t* bstart, const uint16_t* scales,
+                                const sbm_matrix_desc* experts, int32_t n_experts,
+                                int32_t rows, int32_t cols, const void* dict_image,
+                                const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens,
+                                void* y, uint32_t flags, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Workspace error word of the last fused call (device read; synchronises the stream). */
+int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBM_H */

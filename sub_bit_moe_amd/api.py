@@ -1,0 +1,194 @@
+"""Python front end of libsbm: argument marshalling only.
+
+Every step of the codec and of the fused decode + matvec runs in libsbm.so
+(host C++ for dictionary/encoding, HIP kernels on the GPU).  numpy arrays are
+used for host buffers, torch tensors for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _native as N
+from ._native import check, lib
+
+
+def _ptr(a) -> int:
+    if a is None:
+        return 0
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return int(a.data_ptr())
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+# ------------------------------------------------------------------ dictionary
+
+def build_dictionary(p0: float = 0.885):
+    """(words uint32[131072], checksum) of the canonical dictionary."""
+    words = np.zeros(N.SBM_DICT_WORDS, np.uint32)
+    cs = C.c_uint64()
+    check(lib().sbm_build_dictionary(C.c_double(p0), words.ctypes.data, C.addressof(cs)))
+    return words, int(cs.value)
+
+
+def dictionary_checksum(words: np.ndarray) -> int:
+    words = np.ascontiguousarray(words, np.uint32)
+    cs = C.c_uint64()
+    check(lib().sbm_dictionary_checksum(words.ctypes.data, C.addressof(cs)))
+    return int(cs.value)
+
+
+def dict_image(words: np.ndarray) -> np.ndarray:
+    """Compact decode image (uint8 bytes) for the fused kernel."""
+    words = np.ascontiguousarray(words, np.uint32)
+    n = int(lib().sbm_dict_image_bytes())
+    out = np.zeros(n, np.uint8)
+    check(lib().sbm_dict_image(words.ctypes.data, out.ctypes.data, n))
+    return out
+
+# ------------------------------------------------------------------ host codec
+
+def encode_matrix(sym: np.ndarray, words: np.ndarray):
+    """Greedy trie encoding of a symbol matrix uint8 [rows, cols] (0/1/2).
+    Returns (codes uint16[n], row_off uint32[rows+1], bstart uint32[nblk])."""
+    sym = np.ascontiguousarray(sym, np.uint8)
+    rows, cols = sym.shape
+    words = np.ascontiguousarray(words, np.uint32)
+    n = C.c_uint64()
+    check(lib().sbm_encode_size(sym.ctypes.data, rows, cols, words.ctypes.data, C.addressof(n)))
+    codes = np.zeros(max(int(n.value), 1), np.uint16)
+    row_off = np.zeros(rows + 1, np.uint32)
+    nblk = (int(n.value) + N.SBM_BLOCK - 1) // N.SBM_BLOCK
+    bstart = np.zeros(max(nblk, 1), np.uint32)
+    check(lib().sbm_encode_matrix(sym.ctypes.data, rows, cols, words.ctypes.data, codes.ctypes.data,
+                                  codes.size, row_off.ctypes.data, bstart.ctypes.data, C.addressof(n)))
+    return codes[:int(n.value)], row_off, bstart[:nblk]
+
+
+def block_starts(codes: np.ndarray, words: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint16)
+    nblk = (codes.size + N.SBM_BLOCK - 1) // N.SBM_BLOCK
+    out = np.zeros(max(nblk, 1), np.uint32)
+    check(lib().sbm_block_starts(codes.ctypes.data, codes.size,
+                                 np.ascontiguousarray(words, np.uint32).ctypes.data, out.ctypes.data))
+    return out[:nblk]
+
+
+def validate_stream(codes, row_off, rows: int, cols: int, words) -> None:
+    codes = np.ascontiguousarray(codes, np.uint16)
+    row_off = np.ascontiguousarray(row_off, np.uint32)
+    check(lib().sbm_validate_stream(codes.ctypes.data, codes.size, row_off.ctypes.data, rows, cols,
+                                    np.ascontiguousarray(words, np.uint32).ctypes.data))
+
+# ------------------------------------------------------------------ device data
+
+@dataclass
+class ExpertStack:
+    """Encoded matrices of one shape (one projection of all experts), resident
+    on the device in the layout the fused kernel reads."""
+    rows: int
+    cols: int
+    n_experts: int
+    codes: object      # torch.int16 [total codes] (uint16 bit patterns)
+    row_off: object    # torch.int32 [E*(rows+1)] (uint32 values)
+    bstart: object     # torch.int32 [total blocks]
+    scales: object     # torch.float16 [E*rows]
+    desc: object       # torch.uint8 [E*sizeof(MatrixDesc)]
+    host_desc: list
+    code_bytes: int    # bytes of codes actually used (without alignment padding)
+
+    def matrix_bytes(self, e: int) -> int:
+        """Bytes the fused kernel must read for expert e: codes + block starts
+        + scales (row offsets are read once per slice)."""
+        d = self.host_desc[e]
+        nblk = (d.n_codes + N.SBM_BLOCK - 1) // N.SBM_BLOCK
+        return 2 * d.n_codes + 4 * nblk + 2 * self.rows
+
+    @staticmethod
+    def from_host(mats, rows: int, cols: int, device="cuda"):
+        """mats: list of (codes uint16, row_off uint32, bstart uint32, scales fp16)."""
+        import torch
+        descs = []
+        code_parts, off_parts, blk_parts, sc_parts = [], [], [], []
+        cb = ob = sb = bb = 0
+        used = 0
+        for codes, row_off, bstart, scales in mats:
+            n = int(codes.size)
+            assert row_off.size == rows + 1 and scales.size == rows
+            d = N.MatrixDesc(code_base=cb, off_base=ob, scale_base=sb, blk_base=bb, n_codes=n,
+                             rows=rows, cols=cols, reserved=0)
+            descs.append(d)
+            pad = (-n) % N.SBM_CODE_ALIGN
+            code_parts.append(np.concatenate([codes.astype(np.uint16), np.zeros(pad, np.uint16)]))
+            off_parts.append(row_off.astype(np.uint32))
+            blk_parts.append(bstart.astype(np.uint32))
+            sc_parts.append(scales.astype(np.float16))
+            cb += n + pad
+            ob += rows + 1
+            sb += rows
+            bb += bstart.size
+            used += 2 * n
+        codes = np.concatenate(code_parts) if code_parts else np.zeros(8, np.uint16)
+        desc_arr = (N.MatrixDesc * len(descs))(*descs)
+        desc_bytes = np.frombuffer(bytes(desc_arr), np.uint8).copy()
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        return ExpertStack(rows, cols, len(descs), t(codes, np.int16),
+                           t(np.concatenate(off_parts), np.int32),
+                           t(np.concatenate(blk_parts) if blk_parts else np.zeros(1, np.uint32), np.int32),
+                           t(np.concatenate(sc_parts), np.float16), t(desc_bytes, np.uint8), descs, used)
+
+
+def device_image(words: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(dict_image(words)).to(device)
+
+# ------------------------------------------------------------------ GPU calls
+
+def decode_ref(codes_t, row_off_t, rows: int, cols: int, words_t, stream=None):
+    """GPU reference decode of one matrix -> (symbols uint8 [rows, cols], bad_rows)."""
+    import torch
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=codes_t.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=codes_t.device)
+    check(lib().sbm_decode_ref(_ptr(codes_t), _ptr(row_off_t), rows, cols, _ptr(words_t), _ptr(out),
+                               _ptr(bad), _stream(stream)))
+    return out, bad
+
+
+def workspace_bytes(n_experts: int, n_tokens: int) -> int:
+    return int(lib().sbm_workspace_bytes(n_experts, n_tokens))
+
+
+def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
+    import torch
+    return torch.empty(max(workspace_bytes(n_experts, n_tokens), 16), dtype=torch.uint8, device=device)
+
+
+def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
+                            out_f32: bool = False, workspace=None, y=None, stream=None):
+    """y[t] = act(s * W_{expert_ids[t]} x[t]) for one projection of an MoE layer."""
+    import torch
+    T = int(x.shape[0]) if x is not None else 0
+    if y is None:
+        y = torch.empty((T, stack.rows), dtype=torch.float32 if out_f32 else torch.float16,
+                        device=stack.codes.device)
+    if workspace is None:
+        workspace = alloc_workspace(stack.n_experts, T, device=stack.codes.device)
+    flags = (N.SBM_F_RELU if relu else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0)
+    check(lib().sbm_moe_fused_decode_matvec(
+        _ptr(stack.codes), _ptr(stack.row_off), _ptr(stack.bstart), _ptr(stack.scales), _ptr(stack.desc),
+        stack.n_experts, stack.rows, stack.cols, _ptr(image_t), _ptr(x), _ptr(expert_ids), T, _ptr(y),
+        flags, _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return y
+
+
+def workspace_error(workspace, stream=None) -> int:
+    v = C.c_uint32()
+    check(lib().sbm_workspace_error(_ptr(workspace), C.addressof(v), _stream(stream)))
+    return int(v.value)

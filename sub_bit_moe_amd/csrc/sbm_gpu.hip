@@ -1,0 +1,639 @@
+// GPU side of libsbm (gfx950 / CDNA4): reference decode, token grouping and
+// the fused grouped decode + matrix-vector kernel.
+//
+// [QMoE] = "QMoE: Practical Sub-1-Bit Compression of Trillion-Parameter Models",
+// section "The GPU Decoding Kernel" (fused decode-and-multiply, per-row
+// offsets, ternary grid, skipping experts without tokens) and "The Fixed-to-
+// Variable Dictionary Code" (Figure 4 entry layout).
+// [M8.5] = "M8.5 - Extreme Weight Compression and Representations", 0x08A
+// (reference decoder semantics).
+//
+// Fused kernel design (gfx950, wave64):
+//  * Work: the output rows of every (expert, token chunk) item form one index
+//    space; each persistent workgroup owns a contiguous, row-aligned slice, so
+//    every output row is finished inside one workgroup (no global atomics).
+//  * Stream fetch: a wave handles one block of SBM_BLOCK = 512 codewords, 8
+//    per lane, read as one 16-byte load per lane (1 KiB per wave, coalesced).
+//    The block's start position comes from the per-block offset table.
+//  * Decode: the dictionary is held in LDS as a compact image (class per
+//    codeword, class table, colex position table); every entry has at most 3
+//    nonzeros, so a codeword yields its length and 3 "slots" (byte offsets of
+//    signed activations, or of a zero).  Work scales with nonzeros, never with
+//    the 28 symbols of a run.
+//  * Positions: lane-local prefix of run lengths plus one wave scan (DPP).
+//  * Accumulate: activations live in LDS as triples [-x, +x, 0] per column
+//    (fp16), so each nonzero is one LDS read and one fp32 add; zeros are never
+//    touched.  A lane spans < one row (cols >= 256), so it splits its sum at
+//    most once; row sums are formed from a wave-wide prefix of lane sums.
+//  * Epilogue: y = act(s_r * acc) per row and token, fp16 or fp32.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "sbm_internal.h"
+
+namespace sbm {
+
+// ------------------------------------------------------------ constants
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kK = 8;                 // codewords per lane per block
+static_assert(kK * 64 == SBM_BLOCK, "block = 64 lanes x kK codewords");
+constexpr int kXPad = 256;            // wrap columns: > (kK-1)*28 + 255/6, any slot byte stays inside
+constexpr int kXPadSmall = 48;        // narrow rows: > 255/6 columns past the row end
+constexpr int kSmallCols = 256;       // below this a lane may span several rows
+constexpr uint32_t kLdsCls = 0;                                   // u8[65536]
+constexpr uint32_t kLdsCtab = 65536;                              // uint2[64]
+constexpr uint32_t kLdsPost = kLdsCtab + kMaxClasses * 8;         // u32[kPostEntries+1]
+constexpr uint32_t kLdsFixed = kLdsPost + (kPostEntries + 1) * 4; // = 80784
+static_assert(kLdsFixed % 16 == 0, "align");
+
+// workspace layout (uint32 words)
+constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items
+struct WsLayout {
+  uint64_t cnt, start, chunk, perm, items, total_words;
+};
+__host__ __device__ inline WsLayout ws_layout(int64_t E, int64_t T) {
+  WsLayout L;
+  L.cnt = kWsHdr;
+  L.start = L.cnt + E;
+  L.chunk = L.start + E + 1;
+  L.perm = L.chunk + E + 1;
+  L.items = (L.perm + T + 3) & ~3ull;              // uint4 aligned
+  L.total_words = L.items + 4 * (E + T);
+  return L;
+}
+
+struct FusedArgs {
+  const uint16_t* codes;
+  const uint32_t* row_off;
+  const uint32_t* bstart;
+  const uint16_t* scales;
+  const sbm_matrix_desc* experts;
+  const DictImage* image;
+  const uint16_t* x;
+  void* y;
+  uint32_t* ws;
+  int32_t rows, cols, n_experts, n_tokens;
+  uint32_t flags;
+  uint32_t colsB;       // 6 * cols
+  uint32_t magic_s;
+  uint64_t magic_m;     // exact division by colsB for numerators < 2^30
+  int32_t rmax;         // rows per chunk (LDS accumulators)
+  int32_t tcmax;        // tokens per item
+  int32_t xcols;        // staged columns per token (cols + pad)
+  uint32_t lds_racc;    // byte offsets in LDS
+  uint32_t lds_x;
+};
+
+// ------------------------------------------------------------ wave helpers
+// Inclusive scan over the 64 lanes of a wave (DPP row shifts, then the row
+// broadcasts of lane 15 and lane 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ float wave_incl_scan_f(float f) {
+  int v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));
+  v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));
+  v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));
+  v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));
+  v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));
+  v = __float_as_int(f);
+  f += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));
+  return f;
+}
+
+__device__ __forceinline__ uint32_t div_magic_dev(uint32_t n, uint64_t m, uint32_t s) {
+  return (uint32_t)(((uint64_t)n * m) >> s);
+}
+
+// ------------------------------------------------------------ decode_ref
+// One thread per row: expand the row's codewords from the packed Figure-4
+// words in order ([M8.5] 0x08A), writing symbols 0/1/2.
+__global__ void decode_ref_kernel(const uint16_t* __restrict__ codes,
+                                  const uint32_t* __restrict__ row_off, int32_t rows, int32_t cols,
+                                  const uint32_t* __restrict__ words, uint8_t* __restrict__ out,
+                                  uint32_t* __restrict__ bad_rows) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const uint32_t b = row_off[r], e = row_off[r + 1];
+  uint8_t* o = out + r * (int64_t)cols;
+  int64_t pos = 0;
+  bool ok = e >= b;
+  for (uint32_t i = b; ok && i < e; ++i) {
+    const uint32_t c = codes[i];
+    const uint32_t w0 = words[2 * c], w1 = words[2 * c + 1];
+    const uint32_t k = w0 & 0xFu;
+    if (k == 0 || k > 14 || (w1 & 0xFu) != k) { ok = false; break; }
+    for (uint32_t j = 0; j < 2 * k; ++j) {
+      const uint32_t w = j < 14 ? w0 : w1;
+      const uint32_t sh = 4 + 2 * (j < 14 ? j : j - 14);
+      if (pos < cols) o[pos] = (uint8_t)((w >> sh) & 3u);
+      ++pos;
+    }
+  }
+  if (!ok || pos != cols) {
+    if (bad_rows) atomicAdd(bad_rows, 1u);
+  }
+}
+
+// ------------------------------------------------------------ grouping
+// Single workgroup: histogram of expert ids, exclusive scans, scatter of token
+// indices by expert, and the item list (expert, first token, token count) with
+// at most tcmax tokens per item.  Experts without tokens get no item ([QMoE]:
+// calls for experts that receive no tokens are skipped).
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) sh_tot[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t t = sh_tot[w];
+      sh_tot[w] = run;
+      run += t;
+    }
+    sh_tot[kWaves] = run;
+  }
+  __syncthreads();
+  const uint32_t out = sh_tot[wave] + inc - v;
+  *total = sh_tot[kWaves];
+  __syncthreads();
+  return out;
+}
+
+__global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
+                                                         int32_t E, int32_t tcmax,
+                                                         uint32_t* __restrict__ ws) {
+  __shared__ uint32_t sh_tot[kWaves + 1];
+  const WsLayout L = ws_layout(E, T);
+  uint32_t* hdr = ws;
+  uint32_t* cnt = ws + L.cnt;
+  uint32_t* start = ws + L.start;
+  uint32_t* chunk = ws + L.chunk;
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  uint4* items = (uint4*)(ws + L.items);
+  for (int i = threadIdx.x; i < (int)kWsHdr; i += kThreads) hdr[i] = 0;
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < T; t += kThreads) {
+    const int32_t e = ids[t];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1u);
+    else atomicAdd(&hdr[0], 1u);
+  }
+  __syncthreads();
+  uint32_t carry_t = 0, carry_c = 0;
+  for (int base = 0; base < E; base += kThreads) {
+    const int e = base + threadIdx.x;
+    const uint32_t c = e < E ? cnt[e] : 0u;
+    const uint32_t nch = (c + tcmax - 1) / tcmax;
+    uint32_t tot_c, tot_n;
+    const uint32_t ex_c = block_excl_scan(c, sh_tot, &tot_c);
+    const uint32_t ex_n = block_excl_scan(nch, sh_tot, &tot_n);
+    if (e < E) {
+      start[e] = carry_t + ex_c;
+      chunk[e] = carry_c + ex_n;
+    }
+    carry_t += tot_c;
+    carry_c += tot_n;
+  }
+  if (threadIdx.x == 0) {
+    start[E] = carry_t;
+    chunk[E] = carry_c;
+    hdr[1] = carry_c;
+  }
+  __syncthreads();
+  // scatter: reuse cnt as the per-expert cursor
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = start[e];
+  __syncthreads();
+  for (int t = threadIdx.x; t < T; t += kThreads) {
+    const int32_t e = ids[t];
+    if (e >= 0 && e < E) perm[atomicAdd(&cnt[e], 1u)] = t;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const uint32_t s0 = start[e], n = start[e + 1] - s0;
+    uint32_t q = chunk[e];
+    for (uint32_t k = 0; k < n; k += (uint32_t)tcmax, ++q) {
+      const uint32_t nt = (n - k) < (uint32_t)tcmax ? (n - k) : (uint32_t)tcmax;
+      items[q] = make_uint4((uint32_t)e, s0 + k, nt, 0u);
+    }
+  }
+}
+
+// ------------------------------------------------------------ fused kernel
+__device__ __forceinline__ void stage_tables(const DictImage* __restrict__ im, unsigned char* smem) {
+  const uint32_t nk = im->n_classes;
+  // class per codeword: thread t fills codewords [64t, 64t + 64)
+  {
+    const uint32_t c0 = threadIdx.x * 64u;
+    uint32_t k = 0;
+    while (k + 1 < nk && im->cls_base[k + 1] <= c0) ++k;
+    uint32_t* dst = (uint32_t*)(smem + kLdsCls + c0);
+    for (int w = 0; w < 16; ++w) {
+      uint32_t word = 0;
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t c = c0 + 4 * w + b;
+        while (k + 1 < nk && im->cls_base[k + 1] <= c) ++k;
+        word |= k << (8 * b);
+      }
+      dst[w] = word;
+    }
+  }
+  uint2* ctab = (uint2*)(smem + kLdsCtab);
+  for (int k = threadIdx.x; k < kMaxClasses; k += kThreads)
+    ctab[k] = make_uint2(im->ctabA[k], im->ctabB[k]);
+  uint32_t* post = (uint32_t*)(smem + kLdsPost);
+  for (int i = threadIdx.x; i < (int)kPostEntries + 1; i += kThreads) post[i] = im->postab[i];
+}
+
+// Decode one codeword: returns the slot word (3 byte offsets with signs folded
+// in) and the run length in bytes of the triple layout (6 per symbol).
+__device__ __forceinline__ void decode_cw(const unsigned char* smem, uint32_t c, uint32_t& slots,
+                                          uint32_t& lbytes) {
+  const uint32_t k = smem[kLdsCls + c];
+  const uint2 ab = *(const uint2*)(smem + kLdsCtab + 8 * k);
+  const uint32_t off = c - (ab.x & 0xFFFFu);
+  const uint32_t combo = off >> ((ab.x >> 16) & 0xFFu);
+  const uint32_t sg = off & (ab.x >> 24);
+  const uint32_t e = *(const uint32_t*)(smem + kLdsPost + (ab.y & 0xFFFFu) + 4 * combo);
+  slots = e + ((sg * 0x8102u) & 0x20202u);   // sign bit i -> +2 in byte i
+  lbytes = (ab.y >> 16) & 0xFFu;
+}
+
+__device__ __forceinline__ float lds_h2f(const unsigned char* smem, uint32_t byte_addr) {
+  return (float)(*(const _Float16*)(smem + byte_addr));
+}
+
+template <int TC, bool SMALL>
+__device__ void process_block(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
+                              uint32_t b, int32_t ra, int32_t R) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t idx0 = b * SBM_BLOCK + lane * kK;
+  uint32_t w[kK / 2];
+  if (idx0 + kK <= d.n_codes) {
+    const uint4 v = *(const uint4*)(a.codes + d.code_base + idx0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    for (int j = 0; j < kK / 2; ++j) {
+      const uint32_t i0 = idx0 + 2 * j, i1 = i0 + 1;
+      const uint32_t lo = i0 < d.n_codes ? a.codes[d.code_base + i0] : 0u;
+      const uint32_t hi = i1 < d.n_codes ? a.codes[d.code_base + i1] : 0u;
+      w[j] = lo | (hi << 16);
+    }
+  }
+  // phase 1: decode, lane-local run-length prefix
+  uint32_t slots[kK], ls[kK];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    const uint32_t c = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    uint32_t lb;
+    decode_cw(smem, c, slots[j], lb);
+    ls[j] = tot;
+    tot += lb;
+  }
+  const uint32_t excl = wave_incl_scan(tot) - tot;
+  const uint32_t pl = 6u * a.bstart[d.blk_base + b] + excl;   // lane start, bytes
+  float* racc = (float*)(smem + a.lds_racc);
+  const uint32_t xs = a.lds_x;
+  if constexpr (!SMALL) {
+    const uint32_t rl = div_magic_dev(pl, a.magic_m, a.magic_s);
+    const uint32_t colB = pl - rl * a.colsB;
+    const uint32_t thr = a.colsB - colB;
+    float acc[TC], snap[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) { acc[t] = 0.f; snap[t] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      const uint32_t base = colB + ls[j];
+      const uint32_t s = slots[j];
+      const uint32_t a0 = (base + (s & 0xFFu)) * TC + xs;
+      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + xs;
+      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + xs;
+      const bool first_row = ls[j] < thr;
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {
+        acc[t] += lds_h2f(smem, a0 + 2 * t);
+        acc[t] += lds_h2f(smem, a1 + 2 * t);
+        acc[t] += lds_h2f(smem, a2 + 2 * t);
+        snap[t] = first_row ? acc[t] : snap[t];
+      }
+    }
+    // Row sums from a wave prefix of lane sums: a lane whose span reaches the
+    // next row start closes row rl with E = prefix - (part past the boundary).
+    const bool closes = tot >= thr;
+    const int32_t i0 = (int32_t)rl - ra + 1;
+    const int32_t ia = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
+    const int32_t ib = (i0 + 1) < 0 ? 0 : ((i0 + 1) > R + 1 ? R + 1 : i0 + 1);
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      const float S = wave_incl_scan_f(acc[t]);
+      float* rt = racc + t * (a.rmax + 2);
+      if (closes) {
+        const float Ev = S - (acc[t] - snap[t]);
+        atomicAdd(rt + ia, Ev);
+        atomicAdd(rt + ib, -Ev);
+      }
+      if (lane == 63) atomicAdd(rt + (closes ? ib : ia), S);
+    }
+  } else {
+    // narrow rows: locate every codeword's row separately
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      const uint32_t p = pl + ls[j];
+      const uint32_t r = div_magic_dev(p, a.magic_m, a.magic_s);
+      const uint32_t base = p - r * a.colsB;
+      const uint32_t s = slots[j];
+      const uint32_t a0 = (base + (s & 0xFFu)) * TC + xs;
+      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + xs;
+      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + xs;
+      const int32_t i0 = (int32_t)r - ra + 1;
+      const int32_t ii = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {
+        const float v = lds_h2f(smem, a0 + 2 * t) + lds_h2f(smem, a1 + 2 * t) + lds_h2f(smem, a2 + 2 * t);
+        atomicAdd(racc + t * (a.rmax + 2) + ii, v);
+      }
+    }
+  }
+}
+
+// Stage the activations of an item's tokens as triples [-x, +x, 0] per column,
+// tokens interleaved: element (col, k, t) at byte ((3*col + k) * TC + t) * 2.
+// Columns cols..xcols-1 repeat columns 0.. (the next row's start).
+template <int TC>
+__device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
+                        uint32_t nt) {
+  _Float16* xs = (_Float16*)(smem + a.lds_x);
+  const int32_t total = a.xcols * TC;
+  for (int32_t i = threadIdx.x; i < total; i += kThreads) {
+    const int32_t col = i / TC, t = i - col * TC;
+    const int32_t src = col < a.cols ? col : (a.cols >= kSmallCols ? col - a.cols : a.cols);
+    _Float16 v = (_Float16)0.0f;
+    if ((uint32_t)t < nt && src < a.cols) {
+      const int32_t tok = perm[tb + t];
+      v = *(const _Float16*)(a.x + (int64_t)tok * a.cols + src);
+    }
+    xs[(3 * col + 0) * TC + t] = -v;
+    xs[(3 * col + 1) * TC + t] = v;
+    xs[(3 * col + 2) * TC + t] = (_Float16)0.0f;
+  }
+}
+
+template <int TC, bool SMALL>
+__device__ void process_item_rows(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
+                                  const int32_t* perm, uint32_t tb, uint32_t nt, int32_t r0, int32_t r1) {
+  stage_x<TC>(a, smem, perm, tb, nt);
+  float* racc = (float*)(smem + a.lds_racc);
+  for (int32_t i = threadIdx.x; i < TC * (a.rmax + 2); i += kThreads) racc[i] = 0.f;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int32_t ra = r0; ra < r1; ra += a.rmax) {
+    const int32_t rb = (ra + a.rmax) < r1 ? (ra + a.rmax) : r1;
+    const int32_t R = rb - ra;
+    const uint32_t c0 = a.row_off[d.off_base + ra], c1 = a.row_off[d.off_base + rb];
+    if (c1 > c0) {
+      const uint32_t b0 = c0 / SBM_BLOCK, b1 = (c1 - 1) / SBM_BLOCK;
+      for (uint32_t b = b0 + wave; b <= b1; b += kWaves) process_block<TC, SMALL>(a, d, smem, b, ra, R);
+    }
+    __syncthreads();
+    // epilogue: scale, activation, convert, scatter to token order
+    for (int32_t i = threadIdx.x; i < R * (int32_t)nt; i += kThreads) {
+      const int32_t t = i / R, r = i - t * R;
+      float v = racc[t * (a.rmax + 2) + r + 1];
+      const float s = (float)(*(const _Float16*)(a.scales + d.scale_base + ra + r));
+      v *= s;
+      if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+      const int64_t o = (int64_t)perm[tb + t] * a.rows + ra + r;
+      if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+      else ((_Float16*)a.y)[o] = (_Float16)v;
+    }
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < TC * (a.rmax + 2); i += kThreads) racc[i] = 0.f;
+    __syncthreads();
+  }
+}
+
+template <bool SMALL>
+__device__ void dispatch_tc(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
+                            const int32_t* perm, uint32_t tb, uint32_t nt, int32_t r0, int32_t r1) {
+  if (nt <= 1) process_item_rows<1, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
+  else if (nt <= 2) process_item_rows<2, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
+  else process_item_rows<4, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
+}
+
+__global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
+      a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ws[0], 0x80000000u);
+    return;
+  }
+  const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
+  const uint32_t n_items = a.ws[1];
+  const uint64_t N = (uint64_t)n_items * (uint64_t)a.rows;
+  const uint64_t g0 = N * blockIdx.x / gridDim.x, g1 = N * (blockIdx.x + 1) / gridDim.x;
+  if (g0 >= g1) return;
+  stage_tables(a.image, smem);
+  __syncthreads();
+  const int32_t* perm = (const int32_t*)(a.ws + L.perm);
+  const uint4* items = (const uint4*)(a.ws + L.items);
+  uint64_t g = g0;
+  while (g < g1) {
+    const uint32_t q = (uint32_t)(g / (uint64_t)a.rows);
+    const int32_t r0 = (int32_t)(g - (uint64_t)q * a.rows);
+    const uint64_t left = g1 - g;
+    const int32_t r1 = (uint64_t)(a.rows - r0) < left ? a.rows : (int32_t)(r0 + left);
+    const uint4 it = items[q];
+    const sbm_matrix_desc d = a.experts[it.x];
+    if ((d.code_base % SBM_CODE_ALIGN) != 0 || d.rows != a.rows || d.cols != a.cols) {
+      if (threadIdx.x == 0) atomicOr(&a.ws[0], 0x40000000u);
+    } else if (a.cols < kSmallCols) {
+      dispatch_tc<true>(a, d, smem, perm, it.y, it.z, r0, r1);
+    } else {
+      dispatch_tc<false>(a, d, smem, perm, it.y, it.z, r0, r1);
+    }
+    g += (uint64_t)(r1 - r0);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ host entries
+struct DevInfo {
+  int cus = 0;
+  int max_lds = 0;
+  bool attr_set = false;
+};
+static std::mutex g_mu;
+static DevInfo g_dev[64];
+
+static int dev_info(DevInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SBM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SBM_EHIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevInfo& di = g_dev[dev];
+  if (!di.cus) {
+    int v = 0;
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return fail(SBM_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    di.cus = v;
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess)
+      return fail(SBM_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    di.max_lds = v;
+  }
+  if (!di.attr_set) {
+    e = hipFuncSetAttribute((const void*)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            di.max_lds);
+    if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    di.attr_set = true;
+  }
+  *out = &di;
+  return SBM_OK;
+}
+
+// LDS plan for a shape: tokens per item and rows per chunk.
+struct Plan {
+  int tcmax, rmax, xcols;
+  uint32_t lds_racc, lds_x, lds_total;
+};
+static bool make_plan(int cols, int max_lds, Plan* p) {
+  const bool small = cols < kSmallCols;
+  p->xcols = cols + (small ? kXPadSmall : kXPad);
+  for (int rmax : {1024, 512, 256, 128, 64}) {
+    if (cols >= 4096 && rmax > 512) continue;
+    for (int tc : {4, 2, 1}) {
+      const uint32_t racc = (uint32_t)(tc * (rmax + 2) * 4);
+      const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
+      const uint32_t lds_racc = kLdsFixed;
+      const uint32_t lds_x = (lds_racc + racc + 15u) & ~15u;
+      const uint32_t total = (lds_x + xbytes + 15u) & ~15u;
+      if ((int)total <= max_lds) {
+        p->tcmax = tc;
+        p->rmax = rmax;
+        p->lds_racc = lds_racc;
+        p->lds_x = lds_x;
+        p->lds_total = total;
+        return true;
+      }
+    }
+  }
+  return false;
+}
+
+}  // namespace sbm
+
+using namespace sbm;
+
+extern "C" {
+
+int sbm_decode_ref(const uint16_t* codes, const uint32_t* row_off, int32_t rows, int32_t cols,
+                   const uint32_t* words, uint8_t* out_sym, uint32_t* bad_rows, void* stream) {
+  if (rows < 0 || cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", rows, cols);
+  if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
+  if (rows == 0) return SBM_OK;
+  if (!codes || !row_off || !words || !out_sym) return fail(SBM_EINVAL, "null pointer");
+  const int threads = 256;
+  const int blocks = (rows + threads - 1) / threads;
+  hipLaunchKernelGGL(decode_ref_kernel, dim3(blocks), dim3(threads), 0, (hipStream_t)stream, codes,
+                     row_off, rows, cols, words, out_sym, bad_rows);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "decode_ref launch: %s", hipGetErrorString(e));
+  return SBM_OK;
+}
+
+size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
+  if (n_experts < 0 || n_tokens < 0) return 0;
+  return (size_t)ws_layout(n_experts, n_tokens).total_words * 4u;
+}
+
+int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
+                                const uint32_t* bstart, const uint16_t* scales,
+                                const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
+                                int32_t cols, const void* dict_image, const uint16_t* x,
+                                const int32_t* expert_ids, int32_t n_tokens, void* y,
+                                uint32_t flags, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (n_tokens < 0 || n_experts <= 0 || n_experts > (1 << 24))
+    return fail(SBM_EINVAL, "bad n_tokens=%d or n_experts=%d", n_tokens, n_experts);
+  if (rows <= 0 || rows > (1 << 24) || cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", rows, cols);
+  if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
+  if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
+    return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if (n_tokens == 0) return SBM_OK;
+  if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
+      !workspace)
+    return fail(SBM_EINVAL, "null pointer");
+  if (workspace_bytes < sbm_workspace_bytes(n_experts, n_tokens))
+    return fail(SBM_ENOSPACE, "workspace %zu < %zu bytes", workspace_bytes,
+                sbm_workspace_bytes(n_experts, n_tokens));
+  DevInfo* di = nullptr;
+  int st = dev_info(&di);
+  if (st) return st;
+  Plan plan;
+  if (!make_plan(cols, di->max_lds, &plan))
+    return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
+  FusedArgs a;
+  a.codes = codes;
+  a.row_off = row_off;
+  a.bstart = bstart;
+  a.scales = scales;
+  a.experts = experts;
+  a.image = (const DictImage*)dict_image;
+  a.x = x;
+  a.y = y;
+  a.ws = (uint32_t*)workspace;
+  a.rows = rows;
+  a.cols = cols;
+  a.n_experts = n_experts;
+  a.n_tokens = n_tokens;
+  a.flags = flags;
+  a.colsB = 6u * (uint32_t)cols;
+  div_magic(a.colsB, &a.magic_m, &a.magic_s);
+  a.rmax = plan.rmax;
+  a.tcmax = plan.tcmax;
+  a.xcols = plan.xcols;
+  a.lds_racc = plan.lds_racc;
+  a.lds_x = plan.lds_x;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
+                     plan.tcmax, (uint32_t*)workspace);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
+  const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / plan.tcmax + 1;
+  const int64_t n_upper = max_items * rows;
+  int64_t grid = (n_upper + 63) / 64;
+  if (grid > di->cus) grid = di->cus;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kThreads), plan.lds_total, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
+  return SBM_OK;
+}
+
+int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream) {
+  if (!workspace || !out_error) return fail(SBM_EINVAL, "null pointer");
+  hipError_t e = hipMemcpyAsync(out_error, workspace, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(SBM_EHIP, "reading the error word: %s", hipGetErrorString(e));
+  return SBM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path through the C ABI against the oracle."""
+import numpy as np
+import pytest
+
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lib_state(dev, odict):
+    from sub_bit_moe_amd import api
+    words = odict["words"]
+    lw, _ = api.build_dictionary(0.885)
+    assert np.array_equal(lw, words)
+    return {"api": api, "words_t": torch.from_numpy(words.view(np.int32)).to(dev),
+            "image_t": api.device_image(words, dev)}
+
+
+def _to_dev(a, dt, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+
+
+@pytest.mark.parametrize("rows,cols,p0,seed", [(768, 3072, 0.886, 1), (37, 30, 0.886, 2), (5, 2, 0.5, 3),
+                                               (129, 2080, 0.857, 4), (3, 6144, 0.0, 5)])
+def test_decode_ref_bit_exact(dev, lib_state, odict, rows, cols, p0, seed):
+    print(f"decode_ref {rows}x{cols} p0={p0}", flush=True)
+    api = lib_state["api"]
+    sym = P.host_experts(1, rows, cols, p0, seed)[0][0]
+    codes, row_off, _ = P.encode_all([(sym, np.ones(rows, np.float16))], odict["words"], odict)[0][:3]
+    out, bad = api.decode_ref(_to_dev(codes, np.int16, dev), _to_dev(row_off, np.int32, dev), rows, cols,
+                              lib_state["words_t"])
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert np.array_equal(out.cpu().numpy(), sym)
+
+
+def test_decode_ref_flags_truncated_rows(dev, lib_state, odict):
+    api = lib_state["api"]
+    sym = P.host_experts(1, 6, 60, 0.886, 8)[0][0]
+    codes, row_off, _ = api.encode_matrix(sym, odict["words"])
+    bad_off = row_off.copy()
+    bad_off[2] -= 1                     # row 1 loses a codeword, row 2 gains one
+    out, bad = api.decode_ref(_to_dev(codes, np.int16, dev), _to_dev(bad_off, np.int32, dev), 6, 60,
+                              lib_state["words_t"])
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 2
+
+
+def _run(lib_state, experts, rows, cols, x, ids, dev, odict, relu=False, out_f32=False, check_every=1):
+    api = lib_state["api"]
+    mats = P.encode_all(experts, odict["words"], odict, check_every)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    it = torch.from_numpy(np.asarray(ids, np.int32)).to(dev)
+    ws = api.alloc_workspace(stack.n_experts, x.shape[0], dev)
+    y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], xt, it, relu=relu, out_f32=out_f32,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), api.workspace_error(ws)
+
+
+@pytest.mark.parametrize("rows,cols,p0,T", [(768, 3072, 0.886, 1), (300, 512, 0.886, 3),
+                                            (64, 30, 0.886, 2), (200, 2, 0.7, 1), (33, 254, 0.857, 5),
+                                            (1000, 256, 0.886, 4), (17, 6144, 0.886, 2)])
+def test_fused_single_expert(dev, lib_state, odict, rows, cols, p0, T):
+    print(f"fused single {rows}x{cols} T={T}", flush=True)
+    ex = P.host_experts(1, rows, cols, p0, rows + cols)
+    x = np.random.default_rng(5).standard_normal((T, cols)).astype(np.float16)
+    ref = P.oracle_matvec_from_codes(odict, ex[0][0], ex[0][1], x)
+    for out_f32 in (False, True):
+        y, err = _run(lib_state, ex, rows, cols, x, np.zeros(T, np.int32), dev, odict, out_f32=out_f32)
+        assert err == 0
+        P.assert_close(y, ref, what=f"{rows}x{cols} T={T} f32={out_f32}")
+        if out_f32:
+            P.assert_close(y, ref, 2e-6, 2e-5, what="fp32 output")
+
+
+def test_fused_exact_special_inputs(dev, lib_state, odict):
+    rows, cols = 257, 2080
+    sym, sc = P.host_experts(1, rows, cols, 0.886, 77)[0]
+    js = [0, 1, 27, 28, 1039, 2079]
+    x = np.zeros((len(js) + 1, cols), np.float16)
+    for i, j in enumerate(js):
+        x[i, j] = 1.0
+    x[-1, :] = 1.0
+    y, _ = _run(lib_state, [(sym, sc)], rows, cols, x, np.zeros(len(x), np.int32), dev, odict, out_f32=True)
+    tern = (sym == 2).astype(np.float64) - (sym == 1)
+    s = sc.astype(np.float64)
+    for i, j in enumerate(js):
+        assert np.array_equal(y[i], s * tern[:, j])
+    assert np.array_equal(y[-1], s * tern.sum(1))
+    zero = [(np.zeros((rows, cols), np.uint8), sc)]
+    y0, _ = _run(lib_state, zero, rows, cols, x, np.zeros(len(x), np.int32), dev, odict, out_f32=True)
+    assert not np.any(y0)
+
+
+def test_fused_grouped_routing_and_edges(dev, lib_state, odict):
+    E, rows, cols = 12, 300, 512
+    ex = P.host_experts(E, rows, cols, 0.886, 99)
+    rng = np.random.default_rng(3)
+    for T in (1, 8, 32, 37):
+        x = rng.standard_normal((T, cols)).astype(np.float16)
+        ids = rng.integers(0, E, T).astype(np.int32)
+        ids[: T // 2] = 4                      # one heavy expert; several experts stay empty
+        y, err = _run(lib_state, ex, rows, cols, x, ids, dev, odict, relu=True, check_every=4)
+        assert err == 0
+        for t in range(T):
+            ref = np.maximum(P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0], 0)
+            P.assert_close(y[t], ref, what=f"T={T} token {t}")
+
+
+def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict):
+    api = lib_state["api"]
+    E, rows, cols = 3, 64, 256
+    ex = P.host_experts(E, rows, cols, 0.886, 5)
+    mats = P.encode_all(ex, odict["words"])
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    x = np.random.default_rng(1).standard_normal((4, cols)).astype(np.float16)
+    ids = np.array([0, -1, 7, 2], np.int32)
+    y = torch.full((4, rows), float("nan"), dtype=torch.float32, device=dev)
+    ws = api.alloc_workspace(E, 4, dev)
+    api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
+                                torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 2
+    yn = y.cpu().numpy()
+    assert np.isnan(yn[1]).all() and np.isnan(yn[2]).all()
+    for t in (0, 3):
+        P.assert_close(yn[t], P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0])
+
+
+def test_base128_layer_grouped(dev, lib_state, odict):
+    """128 experts, up 3072x768 and down 768x3072 at P(0)=0.857, 128 tokens
+    top-1 Zipf(1.1); the down projection runs on the GPU's own relu(up)."""
+    from sub_bit_moe_amd import synth
+    E, T = 128, 128
+    rng = np.random.default_rng(11)
+    ups = [(synth.ternary_symbols(rng, 3072, 768, 0.857), synth.row_scales(rng, 3072)) for _ in range(E)]
+    downs = [(synth.ternary_symbols(rng, 768, 3072, 0.857), synth.row_scales(rng, 768)) for _ in range(E)]
+    rng2 = np.random.default_rng(12)
+    x = synth.activations(rng2, T, 768)
+    ids = synth.zipf_routing(np.random.default_rng(13), T, E)
+    h, err = _run(lib_state, ups, 3072, 768, x, ids, dev, odict, relu=True, check_every=16)
+    assert err == 0
+    h16 = h.astype(np.float16)
+    y, err = _run(lib_state, downs, 768, 3072, h16, ids, dev, odict, check_every=16)
+    assert err == 0
+    sample = np.unique(np.concatenate([np.random.default_rng(14).choice(T, 24, replace=False),
+                                       np.flatnonzero(ids == np.bincount(ids).argmax())[:4]]))
+    for t in sample:
+        e = ids[t]
+        ref_h = np.maximum(P.oracle_matvec_from_symbols(*ups[e], x[t:t + 1])[0], 0)
+        P.assert_close(h[t], ref_h, what=f"up token {t}")
+        ref_y = P.oracle_matvec_from_symbols(*downs[e], h16[t:t + 1])[0]
+        P.assert_close(y[t], ref_y, what=f"down token {t}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_c2048_pair(dev, lib_state, odict, T):
+    """One c2048-shaped pair: up 6144x2080, down 2080x6144, P(0)=0.886, all
+    T tokens routed to it."""
+    from sub_bit_moe_amd import synth
+    rng = np.random.default_rng(21)
+    up = (synth.ternary_symbols(rng, 6144, 2080, 0.886), synth.row_scales(rng, 6144))
+    down = (synth.ternary_symbols(rng, 2080, 6144, 0.886), synth.row_scales(rng, 2080))
+    x = synth.activations(np.random.default_rng(22 + T), T, 2080)
+    ids = np.zeros(T, np.int32)
+    h, err = _run(lib_state, [up], 6144, 2080, x, ids, dev, odict, relu=True)
+    assert err == 0
+    h16 = h.astype(np.float16)
+    y, err = _run(lib_state, [down], 2080, 6144, h16, ids, dev, odict)
+    assert err == 0
+    ref_h = np.maximum(P.oracle_matvec_from_symbols(*up, x), 0)
+    ref_y = P.oracle_matvec_from_symbols(*down, h16)
+    for t in range(T):
+        P.assert_close(h[t], ref_h[t], what=f"up t={t}")
+        P.assert_close(y[t], ref_y[t], what=f"down t={t}")

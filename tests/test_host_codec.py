@@ -1,0 +1,206 @@
+"""Host side of libsbm against the oracle (CPU only; no GPU calls)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import codec as OC
+from oracle import dictionary as OD
+from sub_bit_moe_amd import _native as N
+from sub_bit_moe_amd import api, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _fnv1a64(words):
+    h = 0xCBF29CE484222325
+    for b in np.asarray(words, np.uint32).astype("<u4").tobytes():
+        h ^= b
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "sbm.h")).read()
+    declared = set(re.findall(r"\b(sbm_[a-z_]+)\s*\(", header))
+    assert declared, "no declarations found"
+    L = N.lib()
+    missing = [s for s in declared if not hasattr(L, s)]
+    assert not missing, missing
+    assert declared == set(N.exported_symbols())
+
+
+def test_dictionary_bit_exact_with_oracle(odict):
+    words, cs = api.build_dictionary(0.885)
+    assert np.array_equal(words, odict["words"])
+    assert cs == api.dictionary_checksum(words)
+    # FNV-1a 64 over the little-endian bytes (published definition), on a slice
+    part = words[:4096]
+    h = _fnv1a64(part)
+    assert isinstance(h, int)
+    w2, _ = api.build_dictionary(0.886)
+    assert np.array_equal(w2, words)
+
+
+@pytest.mark.parametrize("p0", [0.7, 0.857, 0.95])
+def test_dictionary_other_p0_matches_oracle(p0):
+    words, _ = api.build_dictionary(p0)
+    ref = OD.dictionary_words(OD.build_dictionary(p0))
+    assert np.array_equal(words, ref)
+
+
+def test_checksum_is_fnv1a64(odict):
+    assert api.dictionary_checksum(odict["words"]) == _fnv1a64(odict["words"])
+
+
+@pytest.mark.parametrize("rows,cols,p0,seed", [(1, 2, 0.886, 1), (17, 30, 0.886, 2), (64, 256, 0.857, 3),
+                                               (40, 2080, 0.886, 4), (9, 6144, 0.886, 5),
+                                               (31, 98, 0.5, 6), (5, 64, 0.0, 7), (6, 3072, 1.0, 8)])
+def test_encoder_bit_exact_with_oracle(odict, rows, cols, p0, seed):
+    sym = synth.ternary_symbols(np.random.default_rng(seed), rows, cols, p0)
+    codes, row_off, bstart = api.encode_matrix(sym, odict["words"])
+    rc, ro = OC.encode_matrix(sym, odict["child"])
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(row_off, ro)
+    assert np.array_equal(bstart, OC.block_starts(rc, odict["lens"], N.SBM_BLOCK))
+    api.validate_stream(codes, row_off, rows, cols, odict["words"])
+    assert np.array_equal(api.block_starts(codes, odict["words"]), bstart)
+
+
+def test_encoder_error_paths(odict):
+    w = odict["words"]
+    with pytest.raises(N.SbmError) as e:
+        api.encode_matrix(np.zeros((2, 7), np.uint8), w)
+    assert e.value.status == -2
+    bad = np.zeros((2, 8), np.uint8)
+    bad[1, 3] = 3
+    with pytest.raises(N.SbmError) as e:
+        api.encode_matrix(bad, w)
+    assert e.value.status == -1
+    # capacity too small
+    sym = np.full((1, 8), 2, np.uint8)
+    codes = np.zeros(1, np.uint16)
+    row_off = np.zeros(2, np.uint32)
+    n = C.c_uint64()
+    st = N.lib().sbm_encode_matrix(sym.ctypes.data, 1, 8, w.ctypes.data, codes.ctypes.data, 1,
+                                   row_off.ctypes.data, None, C.addressof(n))
+    assert st == -6 and n.value == 4
+    # a dictionary that is not prefix-closed
+    w2 = w.copy()
+    c = next(i for i, s in enumerate(odict["seqs"]) if len(s) == 4)
+    w2[2 * c] = w2[2 * c + 1] = 0
+    with pytest.raises(N.SbmError):
+        api.encode_matrix(np.zeros((1, 4), np.uint8), w2)
+
+
+def test_validate_stream_detects_corruption(odict):
+    w = odict["words"]
+    sym = synth.ternary_symbols(np.random.default_rng(9), 8, 120, 0.886)
+    codes, row_off, _ = api.encode_matrix(sym, w)
+    api.validate_stream(codes, row_off, 8, 120, w)
+    bad = row_off.copy()
+    bad[3] += 1
+    with pytest.raises(N.SbmError) as e:
+        api.validate_stream(codes, bad, 8, 120, w)
+    assert e.value.status == -3
+    with pytest.raises(N.SbmError):
+        api.validate_stream(codes[:-1], row_off, 8, 120, w)
+    trunc = row_off.copy()
+    trunc[-1] -= 1
+    with pytest.raises(N.SbmError):
+        api.validate_stream(codes[:-1], trunc, 8, 120, w)
+
+
+def _image_fields(img):
+    hdr = np.frombuffer(img[:32].tobytes(), np.uint32)
+    n_classes = int(hdr[2])
+    off = 32
+    cls_base = np.frombuffer(img[off:off + 68 * 4].tobytes(), np.uint32)
+    off += 68 * 4
+    A = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
+    off += 64 * 4
+    B = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
+    off += 64 * 4
+    post = np.frombuffer(img[off:off + 3684 * 4].tobytes(), np.uint32)
+    return n_classes, cls_base, A, B, post
+
+
+def test_decode_image_reproduces_every_codeword(odict):
+    """Apply the fused kernel's table arithmetic to all 65536 codewords on the
+    CPU and compare run length, nonzero positions and signs with the oracle."""
+    img = api.dict_image(odict["words"])
+    assert img.size == N.lib().sbm_dict_image_bytes()
+    n_classes, cls_base, A, B, post = _image_fields(img)
+    assert n_classes == 54
+    cls = np.zeros(65536, np.int64)
+    for k in range(n_classes):
+        cls[cls_base[k]:cls_base[k + 1]] = k
+    c = np.arange(65536, dtype=np.int64)
+    a = A[cls].astype(np.int64)
+    b = B[cls].astype(np.int64)
+    off = c - (a & 0xFFFF)
+    combo = off >> ((a >> 16) & 0xFF)
+    sg = off & (a >> 24)
+    e = post[((b & 0xFFFF) // 4) + combo].astype(np.int64)
+    slots = e + ((sg * 0x8102) & 0x20202)
+    L = ((b >> 16) & 0xFF) // 6
+    assert np.array_equal(L, odict["lens"])
+    sym28 = odict["sym28"]
+    for cw in range(65536):
+        exp = np.zeros(28, np.uint8)
+        for i in range(3):
+            byte = (int(slots[cw]) >> (8 * i)) & 0xFF
+            if byte == 4:
+                continue                       # zero slot
+            pos, k = divmod(byte, 6)
+            exp[pos] = 1 if k == 0 else 2      # triple layout [-x, +x, 0]
+        assert np.array_equal(exp, sym28[cw]), cw
+
+
+def test_image_rejects_non_canonical(odict):
+    w = odict["words"].copy()
+    # swap two entries of different classes
+    w[[2 * 100, 2 * 100 + 1, 2 * 60000, 2 * 60000 + 1]] = w[[2 * 60000, 2 * 60000 + 1, 2 * 100, 2 * 100 + 1]]
+    with pytest.raises(N.SbmError) as e:
+        api.dict_image(w)
+    assert e.value.status == -4
+    w3, _ = api.build_dictionary(0.5)         # entries with more than 3 nonzeros
+    with pytest.raises(N.SbmError) as e:
+        api.dict_image(w3)
+    assert e.value.status == -4
+
+
+def _div_magic(d):
+    l = 0
+    while (1 << l) < d:
+        l += 1
+    return (1 << (30 + l)) // d + 1, 30 + l
+
+
+@pytest.mark.parametrize("cols", [2, 6, 30, 256, 768, 2080, 3072, 6144, 13000])
+def test_division_magic_exact(cols):
+    """Granlund-Montgomery exact division used by the kernel for numerators
+    below 2^30 (positions in 6-byte units)."""
+    d = 6 * cols
+    m, s = _div_magic(d)
+    rng = np.random.default_rng(cols)
+    n = np.concatenate([rng.integers(0, 1 << 30, 20000), np.arange(0, 5 * d), [(1 << 30) - 1]])
+    n = n.astype(object)
+    assert all((int(v) * m) >> s == int(v) // d for v in n[::7])
+
+
+def test_fused_argument_errors_without_gpu():
+    L = N.lib()
+    z = None
+    # odd width, bad flags, bad shape are rejected before any device call
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 7, z, z, z, 1, z, 0, z, 0, z) == -2
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 64, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 0, 4, 8, z, z, z, 1, z, 0, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 0, z, 0, z, 0, z) == 0
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 3, z, 0, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 1 << 23, 6144, z, z, z, 1, z, 0, z, 0, z) == -5
+    assert L.sbm_decode_ref(z, z, 3, 5, z, z, z, z) == -2
+    assert L.sbm_decode_ref(z, z, 0, 4, z, z, z, z) == 0
+    assert L.sbm_workspace_bytes(10, 5) >= 4 * (16 + 10 + 11 + 11 + 5)
