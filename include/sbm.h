@@ -54,7 +54,7 @@ extern "C" {
 #define SBM_DICT_ENTRIES 65536
 #define SBM_DICT_WORDS   131072
 #define SBM_MAX_RUN      28
-#define SBM_BLOCK        512      /* codewords per block-offset entry */
+#define SBM_BLOCK        1024     /* codewords per block-offset entry */
 #define SBM_CODE_ALIGN   8        /* matrix code bases must be multiples of this */
 
 typedef enum {

@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(HERE, "libsbm.so")
 
 SBM_DICT_ENTRIES = 65536
 SBM_DICT_WORDS = 131072
-SBM_BLOCK = 512
+SBM_BLOCK = 1024
 SBM_CODE_ALIGN = 8
 SBM_F_RELU = 1
 SBM_F_OUT_F32 = 2

@@ -36,18 +36,25 @@
 namespace sbm {
 
 // ------------------------------------------------------------ constants
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;                // grouping kernel
 constexpr int kWaves = kThreads / 64;
-constexpr int kK = 8;                 // codewords per lane per block
+constexpr int kFThreads = 512;               // fused kernel: 8 waves, up to 256 VGPRs each
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kK = 16;                // codewords per lane per block
 static_assert(kK * 64 == SBM_BLOCK, "block = 64 lanes x kK codewords");
-constexpr int kXPad = 256;            // wrap columns: > (kK-1)*28 + 255/6, any slot byte stays inside
-constexpr int kXPadSmall = 48;        // narrow rows: > 255/6 columns past the row end
-constexpr int kSmallCols = 256;       // below this a lane may span several rows
-constexpr uint32_t kLdsCls = 0;                                   // u8[65536]
-constexpr uint32_t kLdsCtab = 65536;                              // uint2[64]
-constexpr uint32_t kLdsPost = kLdsCtab + kMaxClasses * 8;         // u32[kPostEntries+1]
-constexpr uint32_t kLdsFixed = kLdsPost + (kPostEntries + 1) * 4; // = 80784
+constexpr int kXPad = 48;             // columns past the row end: > 255/6, any slot byte stays inside
+constexpr int kSmallCols = 512;       // below this a lane (<= 448 symbols) may span several rows
+// LDS: the decode tables are static arrays (compile-time addresses fold into
+// instruction offsets); accumulators and activations are dynamic LDS.
+struct __align__(256) LdsTables {
+  uint32_t ctabA[kMaxClasses];        // 256 B
+  uint32_t ctabB[kMaxClasses];        // 256 B, 256 B after ctabA
+  uint32_t post[kPostEntries + 1];
+  uint8_t cls[65536];                 // 4 * class of every codeword
+};
+constexpr uint32_t kLdsFixed = (uint32_t)sizeof(LdsTables);
 static_assert(kLdsFixed % 16 == 0, "align");
+__shared__ LdsTables g_tab;
 
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items
@@ -236,108 +243,247 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
 }
 
 // ------------------------------------------------------------ fused kernel
-__device__ __forceinline__ void stage_tables(const DictImage* __restrict__ im, unsigned char* smem) {
+__device__ __forceinline__ void stage_tables(const DictImage* __restrict__ im) {
   const uint32_t nk = im->n_classes;
-  // class per codeword: thread t fills codewords [64t, 64t + 64)
+  // class per codeword, stored as 4*k (the byte offset of its class-table
+  // entries): each thread fills a run of 65536/kFThreads codewords
   {
-    const uint32_t c0 = threadIdx.x * 64u;
+    constexpr uint32_t per = 65536u / kFThreads;
+    const uint32_t c0 = threadIdx.x * per;
     uint32_t k = 0;
     while (k + 1 < nk && im->cls_base[k + 1] <= c0) ++k;
-    uint32_t* dst = (uint32_t*)(smem + kLdsCls + c0);
-    for (int w = 0; w < 16; ++w) {
+    uint32_t* dst = (uint32_t*)(g_tab.cls + c0);
+    for (uint32_t w = 0; w < per / 4; ++w) {
       uint32_t word = 0;
       for (int b = 0; b < 4; ++b) {
         const uint32_t c = c0 + 4 * w + b;
         while (k + 1 < nk && im->cls_base[k + 1] <= c) ++k;
-        word |= k << (8 * b);
+        word |= (4u * k) << (8 * b);
       }
       dst[w] = word;
     }
   }
-  uint2* ctab = (uint2*)(smem + kLdsCtab);
-  for (int k = threadIdx.x; k < kMaxClasses; k += kThreads)
-    ctab[k] = make_uint2(im->ctabA[k], im->ctabB[k]);
-  uint32_t* post = (uint32_t*)(smem + kLdsPost);
-  for (int i = threadIdx.x; i < (int)kPostEntries + 1; i += kThreads) post[i] = im->postab[i];
+  for (int k = threadIdx.x; k < kMaxClasses; k += kFThreads) {
+    g_tab.ctabA[k] = im->ctabA[k];
+    g_tab.ctabB[k] = im->ctabB[k];
+  }
+  for (int i = threadIdx.x; i < (int)kPostEntries + 1; i += kFThreads) g_tab.post[i] = im->postab[i];
 }
 
-// Decode one codeword: returns the slot word (3 byte offsets with signs folded
-// in) and the run length in bytes of the triple layout (6 per symbol).
-__device__ __forceinline__ void decode_cw(const unsigned char* smem, uint32_t c, uint32_t& slots,
-                                          uint32_t& lbytes) {
-  const uint32_t k = smem[kLdsCls + c];
-  const uint2 ab = *(const uint2*)(smem + kLdsCtab + 8 * k);
-  const uint32_t off = c - (ab.x & 0xFFFFu);
-  const uint32_t combo = off >> ((ab.x >> 16) & 0xFFu);
-  const uint32_t sg = off & (ab.x >> 24);
-  const uint32_t e = *(const uint32_t*)(smem + kLdsPost + (ab.y & 0xFFFFu) + 4 * combo);
-  slots = e + ((sg * 0x8102u) & 0x20202u);   // sign bit i -> +2 in byte i
-  lbytes = (ab.y >> 16) & 0xFFu;
+// acc += (float)x  with x the low / high fp16 half of v: one fp32 rounding.
+__device__ __forceinline__ float acc_lo(float acc, uint32_t v) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(v));
+  return acc;
+}
+__device__ __forceinline__ float acc_hi(float acc, uint32_t v) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(v));
+  return acc;
 }
 
-__device__ __forceinline__ float lds_h2f(const unsigned char* smem, uint32_t byte_addr) {
-  return (float)(*(const _Float16*)(smem + byte_addr));
+// The x values of TC tokens at one slot byte address a (TC=1: fp16 in the low
+// half; TC=2: one dword; TC=4: two dwords).
+template <int TC>
+struct XVal { uint32_t v[TC > 2 ? 2 : 1]; };
+
+template <int TC>
+__device__ __forceinline__ XVal<TC> lds_x(const unsigned char* smem, uint32_t a) {
+  XVal<TC> r;
+  if constexpr (TC == 1) r.v[0] = *(const uint16_t*)(smem + a);
+  else if constexpr (TC == 2) r.v[0] = *(const uint32_t*)(smem + a);
+  else {
+    const uint2 t = *(const uint2*)(smem + a);
+    r.v[0] = t.x;
+    r.v[1] = t.y;
+  }
+  return r;
 }
 
-template <int TC, bool SMALL>
-__device__ void process_block(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
-                              uint32_t b, int32_t ra, int32_t R) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t idx0 = b * SBM_BLOCK + lane * kK;
-  uint32_t w[kK / 2];
-  if (idx0 + kK <= d.n_codes) {
-    const uint4 v = *(const uint4*)(a.codes + d.code_base + idx0);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+template <int TC>
+__device__ __forceinline__ void acc_x(float* acc, const XVal<TC>& x) {
+  if constexpr (TC == 1) acc[0] = acc_lo(acc[0], x.v[0]);
+  else if constexpr (TC == 2) {
+    acc[0] = acc_lo(acc[0], x.v[0]);
+    acc[1] = acc_hi(acc[1], x.v[0]);
   } else {
-    for (int j = 0; j < kK / 2; ++j) {
-      const uint32_t i0 = idx0 + 2 * j, i1 = i0 + 1;
-      const uint32_t lo = i0 < d.n_codes ? a.codes[d.code_base + i0] : 0u;
-      const uint32_t hi = i1 < d.n_codes ? a.codes[d.code_base + i1] : 0u;
-      w[j] = lo | (hi << 16);
+    acc[0] = acc_lo(acc[0], x.v[0]);
+    acc[1] = acc_hi(acc[1], x.v[0]);
+    acc[2] = acc_lo(acc[2], x.v[1]);
+    acc[3] = acc_hi(acc[3], x.v[1]);
+  }
+}
+
+struct BlockCodes {
+  uint4 a, b;
+};
+
+// Everything a workgroup needs about one chunk: rows [ra, rb) of item q.
+struct Chunk {
+  uint32_t q, tb, nt;
+  int32_t ra, rb;
+  uint32_t b0, b1;        // block range (inclusive); b0 > b1 when empty
+  uint64_t code_base;
+  uint32_t n_codes;
+  uint64_t blk_base, scale_base;
+  bool ok;
+};
+
+__device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
+  Chunk ch;
+  ch.q = (uint32_t)(g / (uint64_t)a.rows);
+  ch.ra = (int32_t)(g - (uint64_t)ch.q * a.rows);
+  int64_t rb = ch.ra + a.rmax;
+  if (rb > a.rows) rb = a.rows;
+  if ((uint64_t)(rb - ch.ra) > g1 - g) rb = ch.ra + (int64_t)(g1 - g);
+  ch.rb = (int32_t)rb;
+  const uint4 it = items[ch.q];
+  ch.tb = it.y;
+  ch.nt = it.z;
+  const sbm_matrix_desc d = a.experts[it.x];
+  ch.ok = (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == a.rows && d.cols == a.cols;
+  ch.code_base = d.code_base;
+  ch.n_codes = d.n_codes;
+  ch.blk_base = d.blk_base;
+  ch.scale_base = d.scale_base;
+  ch.b0 = 1;
+  ch.b1 = 0;
+  if (ch.ok) {
+    const uint32_t c0 = a.row_off[d.off_base + ch.ra], c1 = a.row_off[d.off_base + ch.rb];
+    if (c1 > c0 && c1 <= d.n_codes) {
+      ch.b0 = c0 / SBM_BLOCK;
+      ch.b1 = (c1 - 1) / SBM_BLOCK;
     }
   }
-  // phase 1: decode, lane-local run-length prefix
-  uint32_t slots[kK], ls[kK];
+  return ch;
+}
+
+__device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t code_base, uint32_t n_codes,
+                                                 uint32_t b) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t idx0 = b * SBM_BLOCK + lane * kK;
+  BlockCodes r;
+  if (idx0 + kK <= n_codes) {
+    const uint4* p = (const uint4*)(a.codes + code_base + idx0);
+    r.a = p[0];
+    r.b = p[1];
+  } else {
+    uint32_t w[8];
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t i0 = idx0 + 2 * j, i1 = i0 + 1;
+      const uint32_t lo = i0 < n_codes ? a.codes[code_base + i0] : 0u;
+      const uint32_t hi = i1 < n_codes ? a.codes[code_base + i1] : 0u;
+      w[j] = lo | (hi << 16);
+    }
+    r.a = make_uint4(w[0], w[1], w[2], w[3]);
+    r.b = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  return r;
+}
+
+// Prefetch cursor of one wave over the blocks of its workgroup's slice, in
+// the same order the wave processes them.
+struct Cursor {
+  uint64_t g, g1;
+  Chunk ch;
+  uint32_t b;
+  bool done;
+};
+
+__device__ __forceinline__ void cursor_init(Cursor& cu, const FusedArgs& a, const uint4* items, uint64_t g0,
+                                            uint64_t g1) {
+  cu.g = g0;
+  cu.g1 = g1;
+  cu.done = g0 >= g1;
+  if (!cu.done) {
+    cu.ch = chunk_at(a, items, g0, g1);
+    cu.b = cu.ch.b0 + (threadIdx.x >> 6);
+  }
+}
+
+__device__ __forceinline__ BlockCodes cursor_next(Cursor& cu, const FusedArgs& a, const uint4* items) {
+  while (!cu.done) {
+    if (cu.ch.ok && cu.b <= cu.ch.b1) {
+      const BlockCodes r = load_block(a, cu.ch.code_base, cu.ch.n_codes, cu.b);
+      cu.b += kFWaves;
+      return r;
+    }
+    cu.g += (uint64_t)(cu.ch.rb - cu.ch.ra);
+    if (cu.g >= cu.g1) {
+      cu.done = true;
+      break;
+    }
+    cu.ch = chunk_at(a, items, cu.g, cu.g1);
+    cu.b = cu.ch.b0 + (threadIdx.x >> 6);
+  }
+  BlockCodes z;
+  z.a = make_uint4(0, 0, 0, 0);
+  z.b = z.a;
+  return z;
+}
+
+// One block of SBM_BLOCK codewords, kK per lane.
+template <int TC, bool SMALL>
+__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
+                              uint32_t b) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
+  uint32_t c[kK], kk[kK];
+#pragma unroll
+  for (int j = 0; j < kK; ++j) c[j] = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
+  // phase A: class of every codeword (LDS byte = 4 * class)
+#pragma unroll
+  for (int j = 0; j < kK; ++j) kk[j] = g_tab.cls[c[j]];
+  // phase B: class tables
+  uint32_t ca[kK], cb[kK];
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    ca[j] = *(const uint32_t*)((const unsigned char*)g_tab.ctabA + kk[j]);
+    cb[j] = *(const uint32_t*)((const unsigned char*)g_tab.ctabB + kk[j]);
+  }
+  // phase C: nonzero positions, signs, run lengths
+  uint32_t slots[kK], ls[kK], sp[kK];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    const uint32_t c = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    uint32_t lb;
-    decode_cw(smem, c, slots[j], lb);
+    const uint32_t off = c[j] - (ca[j] & 0xFFFFu);
+    const uint32_t combo = off >> ((ca[j] >> 16) & 0xFFu);
+    sp[j] = ((off & 7u) * 0x8102u) & 0x20202u;           // sign bit i -> +2 in byte i
+    slots[j] = *(const uint32_t*)((const unsigned char*)g_tab.post + cb[j] + 4u * combo);
     ls[j] = tot;
-    tot += lb;
+    tot += ca[j] >> 24;
   }
+#pragma unroll
+  for (int j = 0; j < kK; ++j) slots[j] += sp[j];
   const uint32_t excl = wave_incl_scan(tot) - tot;
-  const uint32_t pl = 6u * a.bstart[d.blk_base + b] + excl;   // lane start, bytes
+  const uint32_t pl = 6u * a.bstart[ch.blk_base + b] + excl;   // lane start, bytes
   float* racc = (float*)(smem + a.lds_racc);
-  const uint32_t xs = a.lds_x;
+  const int32_t R = ch.rb - ch.ra;
   if constexpr (!SMALL) {
     const uint32_t rl = div_magic_dev(pl, a.magic_m, a.magic_s);
     const uint32_t colB = pl - rl * a.colsB;
     const uint32_t thr = a.colsB - colB;
+    const uint32_t base0 = colB, base1 = colB - a.colsB;   // row rl / row rl+1 (wraps mod 2^32)
     float acc[TC], snap[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) { acc[t] = 0.f; snap[t] = 0.f; }
 #pragma unroll
     for (int j = 0; j < kK; ++j) {
-      const uint32_t base = colB + ls[j];
-      const uint32_t s = slots[j];
-      const uint32_t a0 = (base + (s & 0xFFu)) * TC + xs;
-      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + xs;
-      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + xs;
       const bool first_row = ls[j] < thr;
+      const uint32_t base = (first_row ? base0 : base1) + ls[j];
+      const uint32_t s = slots[j];
+      const uint32_t a0 = (base + (s & 0xFFu)) * TC + a.lds_x;
+      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x;
+      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x;
+      const XVal<TC> x0 = lds_x<TC>(smem, a0), x1 = lds_x<TC>(smem, a1), x2 = lds_x<TC>(smem, a2);
+      acc_x<TC>(acc, x0);
+      acc_x<TC>(acc, x1);
+      acc_x<TC>(acc, x2);
 #pragma unroll
-      for (int t = 0; t < TC; ++t) {
-        acc[t] += lds_h2f(smem, a0 + 2 * t);
-        acc[t] += lds_h2f(smem, a1 + 2 * t);
-        acc[t] += lds_h2f(smem, a2 + 2 * t);
-        snap[t] = first_row ? acc[t] : snap[t];
-      }
+      for (int t = 0; t < TC; ++t) snap[t] = first_row ? acc[t] : snap[t];
     }
     // Row sums from a wave prefix of lane sums: a lane whose span reaches the
     // next row start closes row rl with E = prefix - (part past the boundary).
     const bool closes = tot >= thr;
-    const int32_t i0 = (int32_t)rl - ra + 1;
+    const int32_t i0 = (int32_t)rl - ch.ra + 1;
     const int32_t ia = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
     const int32_t ib = (i0 + 1) < 0 ? 0 : ((i0 + 1) > R + 1 ? R + 1 : i0 + 1);
 #pragma unroll
@@ -352,42 +498,44 @@ __device__ void process_block(const FusedArgs& a, const sbm_matrix_desc& d, unsi
       if (lane == 63) atomicAdd(rt + (closes ? ib : ia), S);
     }
   } else {
-    // narrow rows: locate every codeword's row separately
+    // narrow rows: a lane may span several rows; locate every codeword's row
 #pragma unroll
     for (int j = 0; j < kK; ++j) {
       const uint32_t p = pl + ls[j];
       const uint32_t r = div_magic_dev(p, a.magic_m, a.magic_s);
       const uint32_t base = p - r * a.colsB;
       const uint32_t s = slots[j];
-      const uint32_t a0 = (base + (s & 0xFFu)) * TC + xs;
-      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + xs;
-      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + xs;
-      const int32_t i0 = (int32_t)r - ra + 1;
+      const uint32_t a0 = (base + (s & 0xFFu)) * TC + a.lds_x;
+      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x;
+      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x;
+      float v[TC];
+#pragma unroll
+      for (int t = 0; t < TC; ++t) v[t] = 0.f;
+      acc_x<TC>(v, lds_x<TC>(smem, a0));
+      acc_x<TC>(v, lds_x<TC>(smem, a1));
+      acc_x<TC>(v, lds_x<TC>(smem, a2));
+      const int32_t i0 = (int32_t)r - ch.ra + 1;
       const int32_t ii = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
 #pragma unroll
-      for (int t = 0; t < TC; ++t) {
-        const float v = lds_h2f(smem, a0 + 2 * t) + lds_h2f(smem, a1 + 2 * t) + lds_h2f(smem, a2 + 2 * t);
-        atomicAdd(racc + t * (a.rmax + 2) + ii, v);
-      }
+      for (int t = 0; t < TC; ++t) atomicAdd(racc + t * (a.rmax + 2) + ii, v[t]);
     }
   }
 }
 
 // Stage the activations of an item's tokens as triples [-x, +x, 0] per column,
 // tokens interleaved: element (col, k, t) at byte ((3*col + k) * TC + t) * 2.
-// Columns cols..xcols-1 repeat columns 0.. (the next row's start).
+// Columns past cols are zero.
 template <int TC>
 __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
                         uint32_t nt) {
   _Float16* xs = (_Float16*)(smem + a.lds_x);
   const int32_t total = a.xcols * TC;
-  for (int32_t i = threadIdx.x; i < total; i += kThreads) {
+  for (int32_t i = threadIdx.x; i < total; i += kFThreads) {
     const int32_t col = i / TC, t = i - col * TC;
-    const int32_t src = col < a.cols ? col : (a.cols >= kSmallCols ? col - a.cols : a.cols);
     _Float16 v = (_Float16)0.0f;
-    if ((uint32_t)t < nt && src < a.cols) {
+    if ((uint32_t)t < nt && col < a.cols) {
       const int32_t tok = perm[tb + t];
-      v = *(const _Float16*)(a.x + (int64_t)tok * a.cols + src);
+      v = *(const _Float16*)(a.x + (int64_t)tok * a.cols + col);
     }
     xs[(3 * col + 0) * TC + t] = -v;
     xs[(3 * col + 1) * TC + t] = v;
@@ -395,49 +543,72 @@ __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* 
   }
 }
 
-template <int TC, bool SMALL>
-__device__ void process_item_rows(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
-                                  const int32_t* perm, uint32_t tb, uint32_t nt, int32_t r0, int32_t r1) {
-  stage_x<TC>(a, smem, perm, tb, nt);
-  float* racc = (float*)(smem + a.lds_racc);
-  for (int32_t i = threadIdx.x; i < TC * (a.rmax + 2); i += kThreads) racc[i] = 0.f;
-  __syncthreads();
-  const int wave = threadIdx.x >> 6;
-  for (int32_t ra = r0; ra < r1; ra += a.rmax) {
-    const int32_t rb = (ra + a.rmax) < r1 ? (ra + a.rmax) : r1;
-    const int32_t R = rb - ra;
-    const uint32_t c0 = a.row_off[d.off_base + ra], c1 = a.row_off[d.off_base + rb];
-    if (c1 > c0) {
-      const uint32_t b0 = c0 / SBM_BLOCK, b1 = (c1 - 1) / SBM_BLOCK;
-      for (uint32_t b = b0 + wave; b <= b1; b += kWaves) process_block<TC, SMALL>(a, d, smem, b, ra, R);
-    }
-    __syncthreads();
-    // epilogue: scale, activation, convert, scatter to token order
-    for (int32_t i = threadIdx.x; i < R * (int32_t)nt; i += kThreads) {
-      const int32_t t = i / R, r = i - t * R;
-      float v = racc[t * (a.rmax + 2) + r + 1];
-      const float s = (float)(*(const _Float16*)(a.scales + d.scale_base + ra + r));
-      v *= s;
-      if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
-      const int64_t o = (int64_t)perm[tb + t] * a.rows + ra + r;
-      if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
-      else ((_Float16*)a.y)[o] = (_Float16)v;
-    }
-    __syncthreads();
-    for (int32_t i = threadIdx.x; i < TC * (a.rmax + 2); i += kThreads) racc[i] = 0.f;
-    __syncthreads();
-  }
+__device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 2 ? 2 : 4); }
+
+template <bool SMALL>
+__device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
+                                                 const BlockCodes& raw, uint32_t b) {
+  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, b);
+  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, b);
+  else process_block<4, SMALL>(a, ch, smem, raw, b);
 }
 
 template <bool SMALL>
-__device__ void dispatch_tc(const FusedArgs& a, const sbm_matrix_desc& d, unsigned char* smem,
-                            const int32_t* perm, uint32_t tb, uint32_t nt, int32_t r0, int32_t r1) {
-  if (nt <= 1) process_item_rows<1, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
-  else if (nt <= 2) process_item_rows<2, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
-  else process_item_rows<4, SMALL>(a, d, smem, perm, tb, nt, r0, r1);
+__device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
+                          uint64_t g0, uint64_t g1) {
+  const int wave = threadIdx.x >> 6;
+  float* racc = (float*)(smem + a.lds_racc);
+  // prefetch ring: three blocks ahead of the block being processed
+  Cursor cu;
+  cursor_init(cu, a, items, g0, g1);
+  BlockCodes r0 = cursor_next(cu, a, items);
+  BlockCodes r1 = cursor_next(cu, a, items);
+  BlockCodes r2 = cursor_next(cu, a, items);
+  uint32_t cur_q = 0xFFFFFFFFu;
+  for (uint64_t g = g0; g < g1;) {
+    const Chunk ch = chunk_at(a, items, g, g1);
+    const int tc = tc_of(ch.nt);
+    if (ch.q != cur_q) {
+      if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
+      else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
+      else stage_x<4>(a, smem, perm, ch.tb, ch.nt);
+      cur_q = ch.q;
+      __syncthreads();
+    }
+    if (ch.ok) {
+      for (uint32_t b = ch.b0 + wave; b <= ch.b1; b += kFWaves) {
+        const BlockCodes cur = r0;
+        r0 = r1;
+        r1 = r2;
+        r2 = cursor_next(cu, a, items);
+        process_dispatch<SMALL>(tc, a, ch, smem, cur, b);
+      }
+    }
+    __syncthreads();
+    // epilogue: scale, activation, convert, scatter to token order
+    const int32_t R = ch.rb - ch.ra;
+    if (ch.ok) {
+      for (int32_t i = threadIdx.x; i < R * (int32_t)ch.nt; i += kFThreads) {
+        const int32_t t = i / R, r = i - t * R;
+        float v = racc[t * (a.rmax + 2) + r + 1];
+        const float s = (float)(*(const _Float16*)(a.scales + ch.scale_base + ch.ra + r));
+        v *= s;
+        if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+        const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + r;
+        if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+        else ((_Float16*)a.y)[o] = (_Float16)v;
+      }
+    } else if (threadIdx.x == 0) {
+      atomicOr(&a.ws[0], 0x40000000u);
+    }
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
+    __syncthreads();
+    g += (uint64_t)R;
+  }
 }
 
-__global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
       a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
@@ -449,28 +620,14 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const uint64_t N = (uint64_t)n_items * (uint64_t)a.rows;
   const uint64_t g0 = N * blockIdx.x / gridDim.x, g1 = N * (blockIdx.x + 1) / gridDim.x;
   if (g0 >= g1) return;
-  stage_tables(a.image, smem);
+  stage_tables(a.image);
+  float* racc = (float*)(smem + a.lds_racc);
+  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
   __syncthreads();
   const int32_t* perm = (const int32_t*)(a.ws + L.perm);
   const uint4* items = (const uint4*)(a.ws + L.items);
-  uint64_t g = g0;
-  while (g < g1) {
-    const uint32_t q = (uint32_t)(g / (uint64_t)a.rows);
-    const int32_t r0 = (int32_t)(g - (uint64_t)q * a.rows);
-    const uint64_t left = g1 - g;
-    const int32_t r1 = (uint64_t)(a.rows - r0) < left ? a.rows : (int32_t)(r0 + left);
-    const uint4 it = items[q];
-    const sbm_matrix_desc d = a.experts[it.x];
-    if ((d.code_base % SBM_CODE_ALIGN) != 0 || d.rows != a.rows || d.cols != a.cols) {
-      if (threadIdx.x == 0) atomicOr(&a.ws[0], 0x40000000u);
-    } else if (a.cols < kSmallCols) {
-      dispatch_tc<true>(a, d, smem, perm, it.y, it.z, r0, r1);
-    } else {
-      dispatch_tc<false>(a, d, smem, perm, it.y, it.z, r0, r1);
-    }
-    g += (uint64_t)(r1 - r0);
-    __syncthreads();
-  }
+  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1);
+  else run_slice<false>(a, smem, perm, items, g0, g1);
 }
 
 // ------------------------------------------------------------ host entries
@@ -500,7 +657,7 @@ static int dev_info(DevInfo** out) {
   }
   if (!di.attr_set) {
     e = hipFuncSetAttribute((const void*)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            di.max_lds);
+                            di.max_lds - (int)kLdsFixed);
     if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     di.attr_set = true;
   }
@@ -514,17 +671,17 @@ struct Plan {
   uint32_t lds_racc, lds_x, lds_total;
 };
 static bool make_plan(int cols, int max_lds, Plan* p) {
-  const bool small = cols < kSmallCols;
-  p->xcols = cols + (small ? kXPadSmall : kXPad);
-  for (int rmax : {1024, 512, 256, 128, 64}) {
-    if (cols >= 4096 && rmax > 512) continue;
-    for (int tc : {4, 2, 1}) {
+  p->xcols = cols + kXPad;
+  // prefer more tokens per item, then longer row chunks (fewer barriers)
+  for (int tc : {4, 2, 1}) {
+    for (int rmax : {1024, 512, 256, 128, 64}) {
+      if (rmax < 256 && tc > 1) continue;
       const uint32_t racc = (uint32_t)(tc * (rmax + 2) * 4);
       const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
-      const uint32_t lds_racc = kLdsFixed;
+      const uint32_t lds_racc = 0;
       const uint32_t lds_x = (lds_racc + racc + 15u) & ~15u;
       const uint32_t total = (lds_x + xbytes + 15u) & ~15u;
-      if ((int)total <= max_lds) {
+      if ((int)(total + kLdsFixed) <= max_lds) {
         p->tcmax = tc;
         p->rmax = rmax;
         p->lds_racc = lds_racc;
@@ -622,7 +779,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   int64_t grid = (n_upper + 63) / 64;
   if (grid > di->cus) grid = di->cus;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kThreads), plan.lds_total, s, a);
+  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), plan.lds_total, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
   return SBM_OK;

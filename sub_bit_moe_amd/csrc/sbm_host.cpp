@@ -166,7 +166,9 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
     while (more) {
       uint32_t e = 0;
       for (int i = 0; i < 3; ++i) {
-        const uint32_t b = i < n ? (uint32_t)(6 * pos[i]) : 4u;  // 4 = the zero slot
+        // 4 = the zero element; for i >= n bit i of the in-class offset is bit
+        // (i - n) of the combo, which the sign spread adds back as 2*bit.
+        const uint32_t b = i < n ? (uint32_t)(6 * pos[i]) : 4u - 2u * ((m >> (i - n)) & 1u);
         e |= b << (8 * i);
       }
       im->postab[seg[n] + m] = e;
@@ -200,8 +202,8 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
       cur_n = n;
       base = c;
       im->cls_base[k] = c;
-      im->ctabA[k] = (c & 0xFFFFu) | ((uint32_t)n << 16) | (((1u << n) - 1u) << 24);
-      im->ctabB[k] = ((seg[n] * 4u) & 0xFFFFu) | ((uint32_t)(6 * L) << 16);
+      im->ctabA[k] = (c & 0xFFFFu) | ((uint32_t)n << 16) | ((uint32_t)(6 * L) << 24);
+      im->ctabB[k] = seg[n] * 4u;
       ++k;
     }
     uint32_t colex = 0;

@@ -11,7 +11,7 @@
 namespace sbm {
 
 constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
-constexpr uint32_t kImageVersion = 1;
+constexpr uint32_t kImageVersion = 2;
 constexpr int kMaxClasses = 64;
 
 // Position table segments: colex-ordered n-subsets of {0..27} for n = 0..3.
@@ -26,11 +26,16 @@ constexpr uint32_t kPostEntries = 3683;
 // Compact decode image of a canonical dictionary (device copy read by the
 // fused kernel).  Codeword c of class k (cls_base[k] <= c < cls_base[k+1]):
 //   off   = c - base(k)
-//   combo = off >> n(k)             (colex rank of the nonzero positions)
-//   signs = off & (2^n(k) - 1)      (bit i set: nonzero i is positive)
-//   slots = postab[seg(n) + combo]  (byte i = 6 * position i, or 4 if i >= n)
-// ctabA[k] = base | n << 16 | (2^n - 1) << 24
-// ctabB[k] = 4*seg(n) | (6*L) << 16
+//   combo = off >> n(k)                 (colex rank of the nonzero positions)
+//   sg    = off & 7                     (bit i < n set: nonzero i is positive)
+//   slots = postab[seg(n) + combo] + spread(sg)
+// where spread puts 2*bit i of sg into byte i.  Byte i of a slot word is the
+// byte offset 6*p_i + 2*positive of nonzero i in the [-x, +x, 0] triple
+// layout, or 4 (the zero) when i >= n.  For i >= n, bit i of off belongs to
+// combo, so those postab bytes are stored as 4 - 2*bit_i(off), which the
+// spread brings back to 4.
+// ctabA[k] = base | n << 16 | (6*L) << 24
+// ctabB[k] = 4*seg(n)   (byte offset of the class's postab segment)
 struct DictImage {
   uint32_t magic;
   uint32_t version;

@@ -51,7 +51,7 @@ def encode_all(experts, words, odict=None, check_every=1):
         if odict is not None and i % check_every == 0:
             rc, ro = OC.encode_matrix(sym, odict["child"])
             assert np.array_equal(codes, rc) and np.array_equal(row_off, ro)
-            assert np.array_equal(bstart, OC.block_starts(rc, odict["lens"], 512))
+            assert np.array_equal(bstart, OC.block_starts(rc, odict["lens"], 1024))
         mats.append((codes, row_off, bstart, sc))
     return mats
 

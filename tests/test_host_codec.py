@@ -142,10 +142,10 @@ def test_decode_image_reproduces_every_codeword(odict):
     b = B[cls].astype(np.int64)
     off = c - (a & 0xFFFF)
     combo = off >> ((a >> 16) & 0xFF)
-    sg = off & (a >> 24)
-    e = post[((b & 0xFFFF) // 4) + combo].astype(np.int64)
+    sg = off & 7
+    e = post[(b // 4) + combo].astype(np.int64)
     slots = e + ((sg * 0x8102) & 0x20202)
-    L = ((b >> 16) & 0xFF) // 6
+    L = ((a >> 24) & 0xFF) // 6
     assert np.array_equal(L, odict["lens"])
     sym28 = odict["sym28"]
     for cw in range(65536):
