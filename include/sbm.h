@@ -164,6 +164,47 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
                                 void* y, uint32_t flags, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* ------------------------------------------- synthetic stack generation */
+/* The QMoE page's c2048 stack (1.6T parameters, under 160 GB at ~0.8 bit per
+ * parameter, ~88.6% zeros; Executive Summary and "Natural sparsity") cannot be
+ * held as ternary symbols, so benchmark stacks are generated on the GPU row by
+ * row and encoded on the fly with the same greedy trie walk as the host
+ * encoder.  Symbols come from SplitMix64 (Steele, Lea, Flood 2014) used as a
+ * counter-based generator:
+ *   out(s, i)  = mix64(s + i * 0x9E3779B97F4A7C15)
+ *   key        = out(seed, m + 1),  m = (layer * n_experts + expert) * 2 + mat
+ *   symbol r,j = 16-bit lane j%4 of out(key, r*ceil(cols/4) + j/4 + 1):
+ *                v < zero_threshold16 -> 0, odd v -> 2 (+), even v -> 1 (-)
+ *   scale r    = scale_table[out(key, 2^40 + r + 1) >> 52]  (4096 fp16 entries)
+ * mat 0 = up projection, 1 = down projection.  All buffers are device memory
+ * owned by the caller. */
+
+/* Trie child table of a dictionary: (SBM_DICT_ENTRIES+1)*9 int32; entry
+ * node*9 + 3a+b is the codeword of node's sequence extended by pair (a,b), or
+ * -1; node SBM_DICT_ENTRIES is the empty sequence.  Host in, host out. */
+size_t sbm_trie_words(void);
+int sbm_build_trie(const uint32_t* words, int32_t* out_child);
+
+/* Pass 1: codeword count of every row of n_experts matrices -> row_counts[E*rows]. */
+int sbm_gen_count(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, int32_t rows, int32_t cols,
+                  uint32_t zero_threshold16, const int32_t* trie, uint32_t* row_counts, void* stream);
+
+/* Row offsets (E*(rows+1), matrix-local), matrix descriptors (E) and totals
+ * (uint64[2]: codewords including per-matrix alignment padding, blocks). */
+int sbm_gen_layout(const uint32_t* row_counts, int32_t n_experts, int32_t rows, int32_t cols, uint32_t* row_off,
+                   sbm_matrix_desc* desc, uint64_t* totals, void* stream);
+
+/* Pass 2: codewords, block starts and row scales into arrays sized from totals. */
+int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, int32_t rows, int32_t cols,
+                  uint32_t zero_threshold16, const int32_t* trie, const uint32_t* row_off,
+                  const sbm_matrix_desc* desc, uint16_t* codes, uint32_t* bstart, const uint16_t* scale_table,
+                  uint16_t* scales, void* stream);
+
+/* Benchmark glue between stacked layers (not part of the method): per token,
+ * x_out = y / sqrt(mean(y^2)) in fp32, stored fp16.  y, x_out: device fp16
+ * [n_tokens x d]; they may not alias. */
+int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint16_t* x_out, void* stream);
+
 /* Workspace error word of the last fused call (device read; synchronises the stream). */
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream);
 

@@ -47,6 +47,14 @@ _SIGS = {
     "sbm_moe_fused_decode_matvec": (C.c_int, [P, P, P, P, P, C.c_int32, C.c_int32, C.c_int32, P,
                                               P, P, C.c_int32, P, C.c_uint32, P, C.c_size_t, P]),
     "sbm_workspace_error": (C.c_int, [P, P, P]),
+    "sbm_rms_glue": (C.c_int, [P, C.c_int32, C.c_int32, P, P]),
+    "sbm_trie_words": (C.c_size_t, []),
+    "sbm_build_trie": (C.c_int, [P, P]),
+    "sbm_gen_count": (C.c_int, [C.c_uint64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                C.c_uint32, P, P, P]),
+    "sbm_gen_layout": (C.c_int, [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]),
+    "sbm_gen_write": (C.c_int, [C.c_uint64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                C.c_uint32, P, P, P, P, P, P, P, P]),
 }
 
 _lib = None

@@ -192,3 +192,47 @@ def workspace_error(workspace, stream=None) -> int:
     v = C.c_uint32()
     check(lib().sbm_workspace_error(_ptr(workspace), C.addressof(v), _stream(stream)))
     return int(v.value)
+
+# ------------------------------------------------------------------ synthetic stacks
+
+def build_trie(words: np.ndarray) -> np.ndarray:
+    """Host trie child table (int32[(65536+1)*9]) of a dictionary."""
+    out = np.zeros(int(lib().sbm_trie_words()), np.int32)
+    check(lib().sbm_build_trie(np.ascontiguousarray(words, np.uint32).ctypes.data, out.ctypes.data))
+    return out
+
+
+def generate_stack(seed: int, layer: int, n_experts: int, mat: int, rows: int, cols: int, p0: float,
+                   trie_t, scale_table_t, stream=None) -> ExpertStack:
+    """Generate and encode n_experts counter-based matrices on the GPU
+    (count pass, row offsets, descriptors, write pass) as an ExpertStack."""
+    import torch
+    from . import synth
+    dev = trie_t.device
+    z = synth.zero_threshold16(p0)
+    s = _stream(stream)
+    counts = torch.empty(n_experts * rows, dtype=torch.int32, device=dev)
+    check(lib().sbm_gen_count(seed, layer, n_experts, mat, rows, cols, z, _ptr(trie_t), _ptr(counts), s))
+    row_off = torch.empty(n_experts * (rows + 1), dtype=torch.int32, device=dev)
+    desc = torch.empty(n_experts * C.sizeof(N.MatrixDesc), dtype=torch.uint8, device=dev)
+    totals = torch.zeros(2, dtype=torch.int64, device=dev)
+    check(lib().sbm_gen_layout(_ptr(counts), n_experts, rows, cols, _ptr(row_off), _ptr(desc), _ptr(totals), s))
+    tot = totals.cpu().tolist()
+    codes = torch.empty(max(int(tot[0]), 8), dtype=torch.int16, device=dev)
+    bstart = torch.empty(max(int(tot[1]), 1), dtype=torch.int32, device=dev)
+    scales = torch.empty(n_experts * rows, dtype=torch.float16, device=dev)
+    check(lib().sbm_gen_write(seed, layer, n_experts, mat, rows, cols, z, _ptr(trie_t), _ptr(row_off),
+                              _ptr(desc), _ptr(codes), _ptr(bstart), _ptr(scale_table_t), _ptr(scales), s))
+    del counts
+    host_desc = list((N.MatrixDesc * n_experts).from_buffer_copy(desc.cpu().numpy().tobytes()))
+    used = 2 * sum(int(d.n_codes) for d in host_desc)
+    return ExpertStack(rows, cols, n_experts, codes, row_off, bstart, scales, desc, host_desc, used)
+
+
+def rms_glue(y, out=None, stream=None):
+    """Stack glue (not the method): x_next = y / rms(y) per token, fp16."""
+    import torch
+    if out is None:
+        out = torch.empty_like(y)
+    check(lib().sbm_rms_glue(_ptr(y), int(y.shape[0]), int(y.shape[1]), _ptr(out), _stream(stream)))
+    return out

@@ -50,6 +50,7 @@ struct __align__(256) LdsTables {
   uint32_t ctabA[kMaxClasses];        // 256 B
   uint32_t ctabB[kMaxClasses];        // 256 B, 256 B after ctabA
   uint32_t post[kPostEntries + 1];
+  uint32_t bases[kMaxClasses + 4];    // first codeword of each class (staging only)
   uint8_t cls[65536];                 // 4 * class of every codeword
 };
 constexpr uint32_t kLdsFixed = (uint32_t)sizeof(LdsTables);
@@ -162,6 +163,12 @@ __global__ void decode_ref_kernel(const uint16_t* __restrict__ codes,
 // indices by expert, and the item list (expert, first token, token count) with
 // at most tcmax tokens per item.  Experts without tokens get no item ([QMoE]:
 // calls for experts that receive no tokens are skipped).
+// Relative cost of one output row of an item with nt tokens (processed with
+// 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
+__host__ __device__ inline uint32_t item_weight(uint32_t nt) {
+  return nt <= 1 ? 4u : (nt <= 2 ? 6u : 10u);
+}
+
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
@@ -237,37 +244,60 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
     uint32_t q = chunk[e];
     for (uint32_t k = 0; k < n; k += (uint32_t)tcmax, ++q) {
       const uint32_t nt = (n - k) < (uint32_t)tcmax ? (n - k) : (uint32_t)tcmax;
-      items[q] = make_uint4((uint32_t)e, s0 + k, nt, 0u);
+      items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt));
     }
   }
+  __syncthreads();
+  // exclusive prefix of the per-row weights over items (.w), total in hdr[2]
+  const uint32_t n_items = hdr[1];
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < n_items; base += kThreads) {
+    const uint32_t q = base + threadIdx.x;
+    const uint32_t wq = q < n_items ? items[q].w : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(wq, sh_tot, &tot);
+    if (q < n_items) items[q].w = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) hdr[2] = carry;
 }
 
 // ------------------------------------------------------------ fused kernel
 __device__ __forceinline__ void stage_tables(const DictImage* __restrict__ im) {
+  uint32_t* bases = g_tab.bases;
   const uint32_t nk = im->n_classes;
-  // class per codeword, stored as 4*k (the byte offset of its class-table
-  // entries): each thread fills a run of 65536/kFThreads codewords
-  {
-    constexpr uint32_t per = 65536u / kFThreads;
-    const uint32_t c0 = threadIdx.x * per;
-    uint32_t k = 0;
-    while (k + 1 < nk && im->cls_base[k + 1] <= c0) ++k;
-    uint32_t* dst = (uint32_t*)(g_tab.cls + c0);
-    for (uint32_t w = 0; w < per / 4; ++w) {
-      uint32_t word = 0;
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t c = c0 + 4 * w + b;
-        while (k + 1 < nk && im->cls_base[k + 1] <= c) ++k;
-        word |= (4u * k) << (8 * b);
-      }
-      dst[w] = word;
-    }
-  }
+  for (int k = threadIdx.x; k < kMaxClasses + 4; k += kFThreads) bases[k] = im->cls_base[k];
   for (int k = threadIdx.x; k < kMaxClasses; k += kFThreads) {
     g_tab.ctabA[k] = im->ctabA[k];
     g_tab.ctabB[k] = im->ctabB[k];
   }
   for (int i = threadIdx.x; i < (int)kPostEntries + 1; i += kFThreads) g_tab.post[i] = im->postab[i];
+  __syncthreads();
+  // class per codeword, stored as 4*k (the byte offset of its class-table
+  // entries): each thread fills a run of 65536/kFThreads codewords
+  constexpr uint32_t per = 65536u / kFThreads;
+  const uint32_t c0 = threadIdx.x * per;
+  uint32_t lo = 0, hi = nk - 1;          // last class whose base <= c0
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if (bases[mid] <= c0) lo = mid;
+    else hi = mid - 1;
+  }
+  uint32_t k = lo;
+  uint32_t next = k + 1 < nk ? bases[k + 1] : 0xFFFFFFFFu;
+  uint32_t* dst = (uint32_t*)(g_tab.cls + c0);
+  for (uint32_t w = 0; w < per / 4; ++w) {
+    uint32_t word = 0;
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t c = c0 + 4 * w + b;
+      while (c >= next) {
+        ++k;
+        next = k + 1 < nk ? bases[k + 1] : 0xFFFFFFFFu;
+      }
+      word |= (4u * k) << (8 * b);
+    }
+    dst[w] = word;
+  }
 }
 
 // acc += (float)x  with x the low / high fp16 half of v: one fp32 rounding.
@@ -608,6 +638,26 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
   }
 }
 
+// Global row index (item * rows + row) where weighted position u falls: item q
+// covers weighted positions [wpre_q * rows, wpre_{q+1} * rows), each of its
+// rows weighing wpre_{q+1} - wpre_q.  Monotone in u, so consecutive
+// workgroups tile the row space exactly.
+__device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint32_t wtot, int32_t rows, uint64_t u) {
+  if (n_items == 0 || u >= (uint64_t)wtot * rows) return (uint64_t)n_items * rows;
+  uint32_t lo = 0, hi = n_items - 1;      // last item with wpre * rows <= u
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if ((uint64_t)items[mid].w * rows <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  const uint64_t w0 = items[lo].w;
+  const uint64_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
+  const uint64_t wq = w1 > w0 ? w1 - w0 : 1;
+  uint64_t r = (u - w0 * rows + wq - 1) / wq;
+  if (r > (uint64_t)rows) r = rows;
+  return (uint64_t)lo * rows + r;
+}
+
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
@@ -617,8 +667,10 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   }
   const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
   const uint32_t n_items = a.ws[1];
-  const uint64_t N = (uint64_t)n_items * (uint64_t)a.rows;
-  const uint64_t g0 = N * blockIdx.x / gridDim.x, g1 = N * (blockIdx.x + 1) / gridDim.x;
+  const uint64_t Wtot = (uint64_t)a.ws[2] * (uint64_t)a.rows;
+  const uint4* items_g = (const uint4*)(a.ws + L.items);
+  const uint64_t g0 = weighted_boundary(items_g, n_items, a.ws[2], a.rows, Wtot * blockIdx.x / gridDim.x);
+  const uint64_t g1 = weighted_boundary(items_g, n_items, a.ws[2], a.rows, Wtot * (blockIdx.x + 1) / gridDim.x);
   if (g0 >= g1) return;
   stage_tables(a.image);
   float* racc = (float*)(smem + a.lds_racc);
@@ -633,7 +685,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
 // ------------------------------------------------------------ host entries
 struct DevInfo {
   int cus = 0;
-  int max_lds = 0;
+  int max_lds = 0;        // LDS per workgroup
+  int static_lds = 0;     // static LDS of the fused kernel
   bool attr_set = false;
 };
 static std::mutex g_mu;
@@ -656,8 +709,12 @@ static int dev_info(DevInfo** out) {
     di.max_lds = v;
   }
   if (!di.attr_set) {
+    hipFuncAttributes fa;
+    if ((e = hipFuncGetAttributes(&fa, (const void*)fused_kernel)) != hipSuccess)
+      return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
+    di.static_lds = (int)fa.sharedSizeBytes;
     e = hipFuncSetAttribute((const void*)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            di.max_lds - (int)kLdsFixed);
+                            di.max_lds - di.static_lds);
     if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     di.attr_set = true;
   }
@@ -670,7 +727,7 @@ struct Plan {
   int tcmax, rmax, xcols;
   uint32_t lds_racc, lds_x, lds_total;
 };
-static bool make_plan(int cols, int max_lds, Plan* p) {
+static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
   p->xcols = cols + kXPad;
   // prefer more tokens per item, then longer row chunks (fewer barriers)
   for (int tc : {4, 2, 1}) {
@@ -681,7 +738,7 @@ static bool make_plan(int cols, int max_lds, Plan* p) {
       const uint32_t lds_racc = 0;
       const uint32_t lds_x = (lds_racc + racc + 15u) & ~15u;
       const uint32_t total = (lds_x + xbytes + 15u) & ~15u;
-      if ((int)(total + kLdsFixed) <= max_lds) {
+      if ((int)total + static_lds <= max_lds) {
         p->tcmax = tc;
         p->rmax = rmax;
         p->lds_racc = lds_racc;
@@ -745,7 +802,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   int st = dev_info(&di);
   if (st) return st;
   Plan plan;
-  if (!make_plan(cols, di->max_lds, &plan))
+  if (!make_plan(cols, di->max_lds, di->static_lds, &plan))
     return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
   FusedArgs a;
   a.codes = codes;

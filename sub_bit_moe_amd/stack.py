@@ -1,0 +1,127 @@
+"""HBM-resident c2048-shaped MoE stack: generation on the GPU and one pass.
+
+Shapes follow the QMoE page's c2048 model (section "Experimental setup" and
+Figure 5's matrix shapes 2080x6144 / 6144x2080): every layer has E experts,
+each an up projection W_up (f x d, d -> f, ReLU) and a down projection
+W_down (d x f).  Weights are ternary with P(0) = 0.886 ("Natural sparsity",
+Table 4) and per-row fp16 scales; they are generated and encoded on the GPU
+from a counter-based generator, so nothing is ever materialised densely.
+
+A pass sends T tokens through all layers: per layer each token's top-1 expert
+(Zipf popularity, the cache-amplification page's routing statistics) applies
+up + ReLU + down through the fused decode + matvec; between layers the token
+is RMS-normalised (benchmark glue standing in for the absent transformer
+block).  Every step runs in libsbm's HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import api, synth
+
+
+@dataclass
+class StackConfig:
+    n_layers: int = 30
+    n_experts: int = 2048
+    d_model: int = 2080
+    d_ff: int = 6144
+    p0: float = 0.886
+    dict_p0: float = 0.885
+    seed: int = 41
+    n_tokens: int = 64
+    zipf_s: float = 1.1
+
+
+@dataclass
+class Stack:
+    cfg: StackConfig
+    image: object
+    up: list = field(default_factory=list)
+    down: list = field(default_factory=list)
+    routes: object = None        # torch int32 [L, T]
+    routes_host: object = None   # numpy int32 [L, T]
+    x0: object = None            # torch fp16 [T, d]
+
+    def stored_bytes(self) -> int:
+        """Every byte of the artefact on the device: codes (with alignment
+        padding), row offsets, block starts, scales, descriptors."""
+        tot = 0
+        for s in self.up + self.down:
+            tot += s.codes.numel() * 2 + s.row_off.numel() * 4 + s.bstart.numel() * 4
+            tot += s.scales.numel() * 2 + s.desc.numel()
+        return tot
+
+    def n_params(self) -> int:
+        c = self.cfg
+        return c.n_layers * c.n_experts * 2 * c.d_model * c.d_ff
+
+    def touched(self, layer: int):
+        """Experts that receive tokens in this layer."""
+        return np.unique(self.routes_host[layer])
+
+    def pass_bytes(self):
+        """(compressed bytes read by one pass, bf16-equivalent bytes) over the
+        touched (expert, matrix) pairs of all layers."""
+        comp = 0
+        bf16 = 0
+        c = self.cfg
+        for l in range(c.n_layers):
+            for e in self.touched(l):
+                comp += self.up[l].matrix_bytes(int(e)) + self.down[l].matrix_bytes(int(e))
+                bf16 += 2 * 2 * c.d_model * c.d_ff
+        return comp, bf16
+
+
+def build(cfg: StackConfig, device="cuda", log=None) -> Stack:
+    import torch
+    words, _ = api.build_dictionary(cfg.dict_p0)
+    st = Stack(cfg, api.device_image(words, device))
+    trie = torch.from_numpy(api.build_trie(words)).to(device)
+    table = torch.from_numpy(synth.scale_table().view(np.int16)).to(device)
+    for l in range(cfg.n_layers):
+        st.up.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 0, cfg.d_ff, cfg.d_model, cfg.p0, trie, table))
+        st.down.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 1, cfg.d_model, cfg.d_ff, cfg.p0, trie, table))
+        if log:
+            log(f"layer {l + 1}/{cfg.n_layers} generated")
+    routes = np.stack([synth.zipf_routing(np.random.default_rng(cfg.seed * 1000 + l), cfg.n_tokens,
+                                          cfg.n_experts, cfg.zipf_s) for l in range(cfg.n_layers)])
+    st.routes_host = routes.astype(np.int32)
+    st.routes = torch.from_numpy(st.routes_host).to(device)
+    st.x0 = torch.from_numpy(synth.activations(np.random.default_rng(cfg.seed + 1), cfg.n_tokens,
+                                               cfg.d_model)).to(device)
+    torch.cuda.synchronize()
+    return st
+
+
+class Runner:
+    """Preallocated buffers for repeated passes."""
+
+    def __init__(self, st: Stack):
+        import torch
+        c = st.cfg
+        dev = st.x0.device
+        self.st = st
+        self.ws_up = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
+        self.ws_down = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
+        self.h = torch.empty(c.n_tokens, c.d_ff, dtype=torch.float16, device=dev)
+        self.y = torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev)
+        self.x = [torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev) for _ in range(2)]
+
+    def run(self, keep=None):
+        """One pass over all layers.  keep: optional dict filled with the
+        per-layer (input, h, y) device tensors for checking."""
+        st = self.st
+        x = st.x0
+        for l in range(st.cfg.n_layers):
+            ids = st.routes[l]
+            api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h)
+            api.moe_fused_decode_matvec(st.down[l], st.image, self.h, ids, workspace=self.ws_down, y=self.y)
+            if keep is not None:
+                keep[l] = (x.clone(), self.h.clone(), self.y.clone())
+            nxt = self.x[l % 2]
+            api.rms_glue(self.y, out=nxt)
+            x = nxt
+        return x

@@ -1,0 +1,113 @@
+"""GPU-generated stacks: codes bit-exact against the oracle's encoding of the
+host-regenerated matrices, and fused outputs of a stack pass against the
+oracle on the GPU's actual per-layer inputs (sampled experts and rows)."""
+import numpy as np
+import pytest
+
+from oracle import codec as OC
+from oracle import matvec as OM
+from sub_bit_moe_amd import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def gen_state(dev, odict):
+    from sub_bit_moe_amd import api
+    trie = torch.from_numpy(api.build_trie(odict["words"])).to(dev)
+    table = torch.from_numpy(synth.scale_table().view(np.int16)).to(dev)
+    return api, trie, table
+
+
+def _host_matrix(st_gpu, e):
+    d = st_gpu.host_desc[e]
+    codes = st_gpu.codes[d.code_base:d.code_base + d.n_codes].cpu().numpy().view(np.uint16)
+    row_off = st_gpu.row_off[d.off_base:d.off_base + st_gpu.rows + 1].cpu().numpy().view(np.uint32)
+    nblk = (d.n_codes + 1023) // 1024
+    bstart = st_gpu.bstart[d.blk_base:d.blk_base + nblk].cpu().numpy().view(np.uint32)
+    scales = st_gpu.scales[d.scale_base:d.scale_base + st_gpu.rows].cpu().numpy()
+    return codes, row_off, bstart, scales
+
+
+@pytest.mark.parametrize("E,rows,cols,mat,layer,p0", [(5, 300, 512, 0, 3, 0.886), (4, 130, 98, 1, 0, 0.857),
+                                                     (2, 6144, 2080, 0, 7, 0.886), (2, 2080, 6144, 1, 29, 0.886)])
+def test_generated_codes_bit_exact(dev, odict, gen_state, E, rows, cols, mat, layer, p0):
+    print(f"gen E={E} {rows}x{cols} mat={mat} layer={layer}", flush=True)
+    api, trie, table = gen_state
+    seed = 41
+    stg = api.generate_stack(seed, layer, E, mat, rows, cols, p0, trie, table)
+    torch.cuda.synchronize()
+    for e in range(E):
+        key = synth.matrix_key(seed, layer, e, mat, E)
+        sym = synth.counter_symbols(key, rows, cols, p0)
+        codes, row_off, bstart, scales = _host_matrix(stg, e)
+        rc, ro = OC.encode_matrix(sym, odict["child"])
+        assert np.array_equal(codes, rc), f"expert {e}: codes differ"
+        assert np.array_equal(row_off, ro), f"expert {e}: row offsets differ"
+        assert np.array_equal(bstart, OC.block_starts(rc, odict["lens"], 1024)), f"expert {e}: block starts"
+        exp_sc = synth.scale_table()[synth.counter_scale_index(key, rows)]
+        assert np.array_equal(scales.view(np.uint16), exp_sc.view(np.uint16)), f"expert {e}: scales"
+        assert stg.host_desc[e].code_base % 8 == 0
+
+
+def test_small_stack_pass_against_oracle(dev, odict):
+    """A 3-layer stack of 64 experts with c2048 widths and 64 Zipf tokens: every
+    layer's up and down outputs for sampled tokens against the oracle applied
+    to the GPU's own inputs to that layer; the glue against its fp64 form."""
+    from sub_bit_moe_amd import stack as S
+    cfg = S.StackConfig(n_layers=3, n_experts=64, seed=43)
+    st = S.build(cfg, dev)
+    run = S.Runner(st)
+    keep = {}
+    run.run(keep)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for l in range(cfg.n_layers):
+        xin, h, y = (t.float().cpu().numpy() for t in keep[l])
+        ids = st.routes_host[l]
+        if l > 0:
+            prev_y = keep[l - 1][2].float().cpu().numpy()
+            P.assert_close(xin, OM.rms_glue(prev_y).astype(np.float64), 2e-3, 2e-3, what=f"glue {l}")
+        for t in rng.choice(cfg.n_tokens, 6, replace=False):
+            e = int(ids[t])
+            for mat, inp, out, relu in ((0, xin[t], h[t], True), (1, h[t], y[t], False)):
+                rows, cols = (cfg.d_ff, cfg.d_model) if mat == 0 else (cfg.d_model, cfg.d_ff)
+                key = synth.matrix_key(cfg.seed, l, e, mat, cfg.n_experts)
+                rsel = np.sort(rng.choice(rows, 48, replace=False))
+                sym = np.concatenate([synth.counter_symbols(key, 1, cols, cfg.p0, row0=int(r)) for r in rsel])
+                sc = synth.scale_table()[synth.counter_scale_index(key, rows)][rsel]
+                ref = P.oracle_matvec_from_symbols(sym, sc, inp.astype(np.float16)[None, :])[0]
+                if relu:
+                    ref = np.maximum(ref, 0)
+                P.assert_close(out[rsel], ref, what=f"layer {l} token {t} mat {mat}")
+
+
+def test_graph_replay_matches_eager(dev):
+    """The bench captures a pass in a HIP graph: several replays, with eager
+    work between them, must reproduce the eager pass.  Row sums are combined
+    with LDS float atomics whose order varies, so equality is up to fp16
+    rounding of the final outputs."""
+    from sub_bit_moe_amd import stack as S
+    cfg = S.StackConfig(n_layers=2, n_experts=32, seed=44, n_tokens=24)
+    st = S.build(cfg, dev)
+    run = S.Runner(st)
+    ref = run.run().clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = run.run()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        P.assert_close(out.float().cpu().numpy(), ref.float().cpu().numpy(), 2e-3, 2e-3, what="replay")
+        run.run()              # eager work in between
+        torch.cuda.synchronize()
