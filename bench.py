@@ -33,7 +33,23 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(st, n_mats: int = 8, budget_s: float = 25.0):
+def measured_traffic():
+    """Calibrated HBM bytes per fused launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "sub_bit_moe_amd", "csrc", "sbm_gpu.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "fused_kernel_traffic_*.md"))):
+        for line in open(f):
+            if line.startswith("traffic_bytes_per_launch"):
+                kv = dict(t.split("=") for t in line.split()[1:])
+                if kv.get("source_sha256_16") == sha:
+                    return int(kv["fetch"]) + int(kv["write"]), os.path.basename(f)
+    return None, None
+
+
+def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
     """The oracle (pure Python/numpy, fp64) decoding and multiplying a bounded
     sample of the same workload: the first n_mats touched matrices of layer 0,
     regenerated on the host from the same counter-based generator and encoded
@@ -56,6 +72,7 @@ def cpu_baseline(st, n_mats: int = 8, budget_s: float = 25.0):
     t_total = 0.0
     n_done = 0
     rng_h = np.random.default_rng(7)
+    sample = []
     for i in range(n_mats):
         e = experts[i // 2 % len(experts)]
         mat = i % 2
@@ -66,19 +83,22 @@ def cpu_baseline(st, n_mats: int = 8, budget_s: float = 25.0):
         codes, row_off = OC.encode_matrix(sym, child)
         toks = np.flatnonzero(routes == e)
         xin = x0[toks] if mat == 0 else rng_h.standard_normal((len(toks), cols)).astype(np.float16)
-        t0 = time.perf_counter()
-        OM.matvec(codes, row_off, scales, sym28, lens, cols, xin)
-        t_total += time.perf_counter() - t0
-        nblk = (codes.size + 1023) // 1024
-        done_bytes += 2 * codes.size + 4 * nblk + 2 * rows
-        n_done += 1
-        if t_total > budget_s:
-            break
+        sample.append((codes, row_off, scales, cols, xin, rows))
+    reps = 0
+    while t_total < budget_s:
+        for codes, row_off, scales, cols, xin, rows in sample:
+            t0 = time.perf_counter()
+            OM.matvec(codes, row_off, scales, sym28, lens, cols, xin)
+            t_total += time.perf_counter() - t0
+            nblk = (codes.size + 1023) // 1024
+            done_bytes += 2 * codes.size + 4 * nblk + 2 * rows
+            n_done += 1
+        reps += 1
     return {"value": done_bytes / t_total / 1e9, "unit": "GB/s compressed", "cores": os.cpu_count(),
             "kind": "oracle",
-            "sample": f"{n_done} touched c2048 matrices of layer 0 (regenerated and oracle-encoded on the "
-                      f"host, untimed); timed: reference decode + fp64 matvec of the routed tokens, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{len(sample)} touched c2048 matrices of layer 0 (2 experts x up/down, regenerated "
+                      f"and oracle-encoded on the host, untimed), decoded by the reference decoder and "
+                      f"multiplied in fp64 for their routed tokens, {reps} repetitions, {t_total:.1f} s timed"}
 
 
 def main():
@@ -158,8 +178,10 @@ def main():
         x = S.api.rms_glue(run.y, out=run.x[l % 2])
     torch.cuda.synchronize()
     achieved = sum(byts) / (sum(durs) * 1e-3) / 1e9
+    traffic, traffic_src = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "traffic_source": traffic_src,
                 "kernel": "sbm::fused_kernel (grouping kernel included in each timed call)",
                 "avg_launch_us": round(1e3 * sum(durs) / len(durs), 2),
                 "bytes_per_launch": int(sum(byts) / len(byts))}
