@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <mutex>
 
 #include "sbm_internal.h"
@@ -47,20 +48,30 @@ constexpr int kSmallCols = 512;       // below this a lane (<= 448 symbols) may 
 // LDS: the decode tables are static arrays (compile-time addresses fold into
 // instruction offsets); accumulators and activations are dynamic LDS.
 struct __align__(256) LdsTables {
+  uint8_t pad[240];                   // puts ctabA on a 256-byte boundary
+  uint32_t bases[kMaxClasses + 4];    // first codeword of each class
   uint32_t ctabA[kMaxClasses];        // 256 B
   uint32_t ctabB[kMaxClasses];        // 256 B, 256 B after ctabA
   uint32_t post[kPostEntries + 1];
-  uint32_t bases[kMaxClasses + 4];    // first codeword of each class (staging only)
   uint8_t cls[65536];                 // 4 * class of every codeword
 };
+// bases..cls are one contiguous copy of the image's cls_base..cls
+static_assert(offsetof(LdsTables, ctabA) % 256 == 0, "ctabA alignment");
+static_assert(offsetof(LdsTables, ctabB) == offsetof(LdsTables, ctabA) + 256, "ctabB follows ctabA");
+static_assert(offsetof(DictImage, cls) - offsetof(DictImage, cls_base) ==
+              offsetof(LdsTables, cls) - offsetof(LdsTables, bases), "image and LDS layouts agree");
+static_assert(offsetof(DictImage, cls_base) % 16 == 0 && offsetof(LdsTables, bases) % 16 == 0, "16B copies");
+constexpr uint32_t kImageCopyU4 =
+    (uint32_t)((offsetof(DictImage, cls) - offsetof(DictImage, cls_base) + 65536) / 16);
 constexpr uint32_t kLdsFixed = (uint32_t)sizeof(LdsTables);
 static_assert(kLdsFixed % 16 == 0, "align");
 __shared__ LdsTables g_tab;
 
 // workspace layout (uint32 words)
-constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items
+constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
+constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
 struct WsLayout {
-  uint64_t cnt, start, chunk, perm, items, total_words;
+  uint64_t cnt, start, chunk, perm, items, bounds, total_words;
 };
 __host__ __device__ inline WsLayout ws_layout(int64_t E, int64_t T) {
   WsLayout L;
@@ -69,7 +80,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t E, int64_t T) {
   L.chunk = L.start + E + 1;
   L.perm = L.chunk + E + 1;
   L.items = (L.perm + T + 3) & ~3ull;              // uint4 aligned
-  L.total_words = L.items + 4 * (E + T);
+  L.bounds = L.items + 4 * (E + T);                // uint64[kMaxGrid + 1], 8-byte aligned
+  L.total_words = L.bounds + 2 * (kMaxGrid + 1);
   return L;
 }
 
@@ -163,6 +175,26 @@ __global__ void decode_ref_kernel(const uint16_t* __restrict__ codes,
 // indices by expert, and the item list (expert, first token, token count) with
 // at most tcmax tokens per item.  Experts without tokens get no item ([QMoE]:
 // calls for experts that receive no tokens are skipped).
+// Global row index (item * rows + row) where weighted position u falls: item q
+// covers weighted positions [wpre_q * rows, wpre_{q+1} * rows), each of its
+// rows weighing wpre_{q+1} - wpre_q.  Monotone in u, so consecutive
+// workgroups tile the row space exactly.
+__device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint32_t wtot, int32_t rows, uint64_t u) {
+  if (n_items == 0 || u >= (uint64_t)wtot * rows) return (uint64_t)n_items * rows;
+  uint32_t lo = 0, hi = n_items - 1;      // last item with wpre * rows <= u
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if ((uint64_t)items[mid].w * rows <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  const uint64_t w0 = items[lo].w;
+  const uint64_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
+  const uint64_t wq = w1 > w0 ? w1 - w0 : 1;
+  uint64_t r = (u - w0 * rows + wq - 1) / wq;
+  if (r > (uint64_t)rows) r = rows;
+  return (uint64_t)lo * rows + r;
+}
+
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
 __host__ __device__ inline uint32_t item_weight(uint32_t nt) {
@@ -191,7 +223,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
 }
 
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
-                                                         int32_t E, int32_t tcmax,
+                                                         int32_t E, int32_t tcmax, int32_t rows, int32_t grid,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
   const WsLayout L = ws_layout(E, T);
@@ -260,43 +292,39 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
     carry += tot;
   }
   if (threadIdx.x == 0) hdr[2] = carry;
+  __syncthreads();
+  // contiguous weighted slices of the (item, row) space, one per fused workgroup
+  uint64_t* bounds = (uint64_t*)(ws + L.bounds);
+  const uint64_t wrows = (uint64_t)carry * (uint64_t)rows;
+  for (int g = threadIdx.x; g <= grid; g += kThreads)
+    bounds[g] = weighted_boundary(items, n_items, carry, rows, wrows * (uint64_t)g / (uint64_t)grid);
 }
 
 // ------------------------------------------------------------ fused kernel
-__device__ __forceinline__ void stage_tables(const DictImage* __restrict__ im) {
-  uint32_t* bases = g_tab.bases;
-  const uint32_t nk = im->n_classes;
-  for (int k = threadIdx.x; k < kMaxClasses + 4; k += kFThreads) bases[k] = im->cls_base[k];
-  for (int k = threadIdx.x; k < kMaxClasses; k += kFThreads) {
-    g_tab.ctabA[k] = im->ctabA[k];
-    g_tab.ctabB[k] = im->ctabB[k];
+// Copy of the decode image into LDS: loads issued at kernel entry, stores
+// after the first blocks have been requested.
+constexpr int kImgPer = (kImageCopyU4 + kFThreads - 1) / kFThreads;
+struct ImgRegs {
+  uint4 v[kImgPer];
+};
+
+__device__ __forceinline__ ImgRegs stage_tables_load(const DictImage* __restrict__ im) {
+  const uint4* src = (const uint4*)im->cls_base;
+  ImgRegs r;
+#pragma unroll
+  for (int j = 0; j < kImgPer; ++j) {
+    const uint32_t i = threadIdx.x + j * kFThreads;
+    r.v[j] = i < kImageCopyU4 ? src[i] : make_uint4(0, 0, 0, 0);
   }
-  for (int i = threadIdx.x; i < (int)kPostEntries + 1; i += kFThreads) g_tab.post[i] = im->postab[i];
-  __syncthreads();
-  // class per codeword, stored as 4*k (the byte offset of its class-table
-  // entries): each thread fills a run of 65536/kFThreads codewords
-  constexpr uint32_t per = 65536u / kFThreads;
-  const uint32_t c0 = threadIdx.x * per;
-  uint32_t lo = 0, hi = nk - 1;          // last class whose base <= c0
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1) / 2;
-    if (bases[mid] <= c0) lo = mid;
-    else hi = mid - 1;
-  }
-  uint32_t k = lo;
-  uint32_t next = k + 1 < nk ? bases[k + 1] : 0xFFFFFFFFu;
-  uint32_t* dst = (uint32_t*)(g_tab.cls + c0);
-  for (uint32_t w = 0; w < per / 4; ++w) {
-    uint32_t word = 0;
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t c = c0 + 4 * w + b;
-      while (c >= next) {
-        ++k;
-        next = k + 1 < nk ? bases[k + 1] : 0xFFFFFFFFu;
-      }
-      word |= (4u * k) << (8 * b);
-    }
-    dst[w] = word;
+  return r;
+}
+
+__device__ __forceinline__ void stage_tables(const ImgRegs& r) {
+  uint4* dst = (uint4*)g_tab.bases;
+#pragma unroll
+  for (int j = 0; j < kImgPer; ++j) {
+    const uint32_t i = threadIdx.x + j * kFThreads;
+    if (i < kImageCopyU4) dst[i] = r.v[j];
   }
 }
 
@@ -554,22 +582,60 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
 
 // Stage the activations of an item's tokens as triples [-x, +x, 0] per column,
 // tokens interleaved: element (col, k, t) at byte ((3*col + k) * TC + t) * 2.
-// Columns past cols are zero.
+// Columns past cols are zero.  Each thread takes 8 columns of all TC tokens
+// (one 16-byte load per token) and writes 48*TC contiguous bytes.
 template <int TC>
 __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
                         uint32_t nt) {
-  _Float16* xs = (_Float16*)(smem + a.lds_x);
-  const int32_t total = a.xcols * TC;
-  for (int32_t i = threadIdx.x; i < total; i += kFThreads) {
-    const int32_t col = i / TC, t = i - col * TC;
-    _Float16 v = (_Float16)0.0f;
-    if ((uint32_t)t < nt && col < a.cols) {
-      const int32_t tok = perm[tb + t];
-      v = *(const _Float16*)(a.x + (int64_t)tok * a.cols + col);
+  int32_t tok[TC];
+#pragma unroll
+  for (int t = 0; t < TC; ++t) tok[t] = (uint32_t)t < nt ? perm[tb + t] : -1;
+  const int32_t n8 = a.xcols / 8;
+  const bool vec = (a.cols % 8) == 0 && ((uintptr_t)a.x & 15u) == 0;
+  for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
+    const int32_t c0 = 8 * i;
+    uint32_t p[TC][4];                       // [token][column pair] fp16x2
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+      if (tok[t] >= 0 && c0 + 8 <= a.cols && vec) {
+        const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + c0);
+        p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          uint32_t lo = 0, hi = 0;
+          if (tok[t] >= 0 && c0 + 2 * m < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m];
+          if (tok[t] >= 0 && c0 + 2 * m + 1 < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m + 1];
+          p[t][m] = lo | (hi << 16);
+        }
+      }
     }
-    xs[(3 * col + 0) * TC + t] = -v;
-    xs[(3 * col + 1) * TC + t] = v;
-    xs[(3 * col + 2) * TC + t] = (_Float16)0.0f;
+    uint32_t o[12 * TC];
+    if constexpr (TC == 1) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {           // columns 2m, 2m+1
+        const uint32_t x = p[0][m];
+        const uint32_t xl = x & 0xFFFFu, xh = x >> 16;
+        o[3 * m + 0] = (xl ^ 0x8000u) | (xl << 16);          // [-x0, +x0]
+        o[3 * m + 1] = (xh ^ 0x8000u) << 16;                 // [0, -x1]
+        o[3 * m + 2] = xh;                                   // [+x1, 0]
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int tp = 0; tp < TC / 2; ++tp) {                // token pair (2tp, 2tp+1)
+          const uint32_t a0 = p[2 * tp][c / 2], a1 = p[2 * tp + 1][c / 2];
+          const uint32_t pair = (c & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+          o[(3 * c + 0) * (TC / 2) + tp] = pair ^ 0x80008000u;
+          o[(3 * c + 1) * (TC / 2) + tp] = pair;
+          o[(3 * c + 2) * (TC / 2) + tp] = 0u;
+        }
+      }
+    }
+    uint4* d = (uint4*)(smem + a.lds_x + (uint32_t)(6 * c0 * TC));
+#pragma unroll
+    for (int q = 0; q < 3 * TC; ++q) d[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   }
 }
 
@@ -588,12 +654,17 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
                           uint64_t g0, uint64_t g1) {
   const int wave = threadIdx.x >> 6;
   float* racc = (float*)(smem + a.lds_racc);
+  const ImgRegs img = stage_tables_load(a.image);
   // prefetch ring: three blocks ahead of the block being processed
   Cursor cu;
   cursor_init(cu, a, items, g0, g1);
   BlockCodes r0 = cursor_next(cu, a, items);
   BlockCodes r1 = cursor_next(cu, a, items);
   BlockCodes r2 = cursor_next(cu, a, items);
+  // the decode tables are stored while the first blocks are in flight
+  stage_tables(img);
+  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
+  __syncthreads();
   uint32_t cur_q = 0xFFFFFFFFu;
   for (uint64_t g = g0; g < g1;) {
     const Chunk ch = chunk_at(a, items, g, g1);
@@ -638,26 +709,6 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
   }
 }
 
-// Global row index (item * rows + row) where weighted position u falls: item q
-// covers weighted positions [wpre_q * rows, wpre_{q+1} * rows), each of its
-// rows weighing wpre_{q+1} - wpre_q.  Monotone in u, so consecutive
-// workgroups tile the row space exactly.
-__device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint32_t wtot, int32_t rows, uint64_t u) {
-  if (n_items == 0 || u >= (uint64_t)wtot * rows) return (uint64_t)n_items * rows;
-  uint32_t lo = 0, hi = n_items - 1;      // last item with wpre * rows <= u
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1) / 2;
-    if ((uint64_t)items[mid].w * rows <= u) lo = mid;
-    else hi = mid - 1;
-  }
-  const uint64_t w0 = items[lo].w;
-  const uint64_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
-  const uint64_t wq = w1 > w0 ? w1 - w0 : 1;
-  uint64_t r = (u - w0 * rows + wq - 1) / wq;
-  if (r > (uint64_t)rows) r = rows;
-  return (uint64_t)lo * rows + r;
-}
-
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
@@ -666,16 +717,9 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     return;
   }
   const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
-  const uint32_t n_items = a.ws[1];
-  const uint64_t Wtot = (uint64_t)a.ws[2] * (uint64_t)a.rows;
-  const uint4* items_g = (const uint4*)(a.ws + L.items);
-  const uint64_t g0 = weighted_boundary(items_g, n_items, a.ws[2], a.rows, Wtot * blockIdx.x / gridDim.x);
-  const uint64_t g1 = weighted_boundary(items_g, n_items, a.ws[2], a.rows, Wtot * (blockIdx.x + 1) / gridDim.x);
+  const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
+  const uint64_t g0 = bounds[blockIdx.x], g1 = bounds[blockIdx.x + 1];
   if (g0 >= g1) return;
-  stage_tables(a.image);
-  float* racc = (float*)(smem + a.lds_racc);
-  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
-  __syncthreads();
   const int32_t* perm = (const int32_t*)(a.ws + L.perm);
   const uint4* items = (const uint4*)(a.ws + L.items);
   if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1);
@@ -728,7 +772,7 @@ struct Plan {
   uint32_t lds_racc, lds_x, lds_total;
 };
 static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
-  p->xcols = cols + kXPad;
+  p->xcols = (cols + kXPad + 7) / 8 * 8;
   // prefer more tokens per item, then longer row chunks (fewer barriers)
   for (int tc : {4, 2, 1}) {
     for (int rmax : {1024, 512, 256, 128, 64}) {
@@ -827,15 +871,16 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   a.lds_racc = plan.lds_racc;
   a.lds_x = plan.lds_x;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                     plan.tcmax, (uint32_t*)workspace);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / plan.tcmax + 1;
   const int64_t n_upper = max_items * rows;
   int64_t grid = (n_upper + 63) / 64;
   if (grid > di->cus) grid = di->cus;
+  if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
+                     plan.tcmax, rows, (int32_t)grid, (uint32_t*)workspace);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), plan.lds_total, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));

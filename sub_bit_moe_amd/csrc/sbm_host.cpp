@@ -213,6 +213,8 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
   }
   im->n_classes = k;
   im->cls_base[k] = SBM_DICT_ENTRIES;
+  for (uint32_t j = 0; j < k; ++j)
+    for (uint32_t c = im->cls_base[j]; c < im->cls_base[j + 1]; ++c) im->cls[c] = (uint8_t)(4u * j);
   return SBM_OK;
 }
 

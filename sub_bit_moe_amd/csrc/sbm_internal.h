@@ -11,7 +11,7 @@
 namespace sbm {
 
 constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
-constexpr uint32_t kImageVersion = 2;
+constexpr uint32_t kImageVersion = 3;
 constexpr int kMaxClasses = 64;
 
 // Position table segments: colex-ordered n-subsets of {0..27} for n = 0..3.
@@ -36,6 +36,7 @@ constexpr uint32_t kPostEntries = 3683;
 // spread brings back to 4.
 // ctabA[k] = base | n << 16 | (6*L) << 24
 // ctabB[k] = 4*seg(n)   (byte offset of the class's postab segment)
+// cls[c]   = 4*k        (byte offset of codeword c's class-table entries)
 struct DictImage {
   uint32_t magic;
   uint32_t version;
@@ -47,6 +48,7 @@ struct DictImage {
   uint32_t ctabA[kMaxClasses];
   uint32_t ctabB[kMaxClasses];
   uint32_t postab[kPostEntries + 1];
+  uint8_t cls[SBM_DICT_ENTRIES];    // 4 * class of every codeword
 };
 
 int fail(int status, const char* fmt, ...);
