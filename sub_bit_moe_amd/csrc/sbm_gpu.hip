@@ -198,7 +198,7 @@ __device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
 __host__ __device__ inline uint32_t item_weight(uint32_t nt) {
-  return nt <= 1 ? 4u : (nt <= 2 ? 6u : 10u);
+  return nt <= 1 ? 4u : (nt <= 2 ? 5u : 6u);
 }
 
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* total) {
@@ -382,6 +382,7 @@ struct Chunk {
   uint64_t code_base;
   uint32_t n_codes;
   uint64_t blk_base, scale_base;
+  uint32_t seq0;          // first block sequence number of the chunk in its round
   bool ok;
 };
 
@@ -435,47 +436,6 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
     r.b = make_uint4(w[4], w[5], w[6], w[7]);
   }
   return r;
-}
-
-// Prefetch cursor of one wave over the blocks of its workgroup's slice, in
-// the same order the wave processes them.
-struct Cursor {
-  uint64_t g, g1;
-  Chunk ch;
-  uint32_t b;
-  bool done;
-};
-
-__device__ __forceinline__ void cursor_init(Cursor& cu, const FusedArgs& a, const uint4* items, uint64_t g0,
-                                            uint64_t g1) {
-  cu.g = g0;
-  cu.g1 = g1;
-  cu.done = g0 >= g1;
-  if (!cu.done) {
-    cu.ch = chunk_at(a, items, g0, g1);
-    cu.b = cu.ch.b0 + (threadIdx.x >> 6);
-  }
-}
-
-__device__ __forceinline__ BlockCodes cursor_next(Cursor& cu, const FusedArgs& a, const uint4* items) {
-  while (!cu.done) {
-    if (cu.ch.ok && cu.b <= cu.ch.b1) {
-      const BlockCodes r = load_block(a, cu.ch.code_base, cu.ch.n_codes, cu.b);
-      cu.b += kFWaves;
-      return r;
-    }
-    cu.g += (uint64_t)(cu.ch.rb - cu.ch.ra);
-    if (cu.g >= cu.g1) {
-      cu.done = true;
-      break;
-    }
-    cu.ch = chunk_at(a, items, cu.g, cu.g1);
-    cu.b = cu.ch.b0 + (threadIdx.x >> 6);
-  }
-  BlockCodes z;
-  z.a = make_uint4(0, 0, 0, 0);
-  z.b = z.a;
-  return z;
 }
 
 // One block of SBM_BLOCK codewords, kK per lane.
@@ -649,63 +609,154 @@ __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, con
   else process_block<4, SMALL>(a, ch, smem, raw, b);
 }
 
+// Chunks of the current round of a workgroup's slice (LDS) and the block
+// sequence counter the waves draw from.
+constexpr int kMaxChunks = 32;
+__shared__ Chunk s_chunks[kMaxChunks];
+__shared__ uint32_t s_nchunks, s_nseq, s_next_seq;
+__shared__ uint64_t s_gnext;
+
+// Fill the chunk table from row index g (at most kMaxChunks chunks).
+__device__ void build_chunks(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
+  if (threadIdx.x == 0) {
+    uint32_t n = 0, seq = 0;
+    while (g < g1 && n < (uint32_t)kMaxChunks) {
+      Chunk ch = chunk_at(a, items, g, g1);
+      ch.seq0 = seq;
+      if (ch.ok && ch.b1 >= ch.b0) seq += ch.b1 - ch.b0 + 1;
+      s_chunks[n++] = ch;
+      g += (uint64_t)(ch.rb - ch.ra);
+    }
+    s_nchunks = n;
+    s_nseq = seq;
+    s_next_seq = 0;
+    s_gnext = g;
+  }
+  __syncthreads();
+}
+
+// Chunk c of the table, every field made wave-uniform (scalar registers).
+__device__ __forceinline__ Chunk load_chunk(uint32_t c) {
+  const Chunk& m = s_chunks[c];
+  auto u32 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); };
+  auto u64 = [&](uint64_t v) { return (uint64_t)u32((uint32_t)v) | ((uint64_t)u32((uint32_t)(v >> 32)) << 32); };
+  Chunk ch;
+  ch.q = u32(m.q);
+  ch.tb = u32(m.tb);
+  ch.nt = u32(m.nt);
+  ch.ra = (int32_t)u32((uint32_t)m.ra);
+  ch.rb = (int32_t)u32((uint32_t)m.rb);
+  ch.b0 = u32(m.b0);
+  ch.b1 = u32(m.b1);
+  ch.code_base = u64(m.code_base);
+  ch.n_codes = u32(m.n_codes);
+  ch.blk_base = u64(m.blk_base);
+  ch.scale_base = u64(m.scale_base);
+  ch.seq0 = u32(m.seq0);
+  ch.ok = u32((uint32_t)m.ok) != 0;
+  return ch;
+}
+
+// Chunk holding block sequence number q (q < s_nseq).
+__device__ __forceinline__ uint32_t chunk_of_seq(uint32_t q, uint32_t nch) {
+  uint32_t c = 0;
+  while (c + 1 < nch && s_chunks[c + 1].seq0 <= q) ++c;
+  return c;
+}
+
+// Draw the next block for this wave and start loading it.
+struct Slot {
+  BlockCodes v;
+  uint32_t seq;         // 0xFFFFFFFF when empty
+};
+
+__device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t nch) {
+  uint32_t q = 0;
+  if ((threadIdx.x & 63) == 0) q = atomicAdd(&s_next_seq, 1u);
+  q = __builtin_amdgcn_readfirstlane(q);
+  Slot sl;
+  sl.seq = 0xFFFFFFFFu;
+  sl.v.a = make_uint4(0, 0, 0, 0);
+  sl.v.b = sl.v.a;
+  if (q < nseq) {
+    const uint32_t c = chunk_of_seq(q, nch);
+    const uint64_t cb = (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)s_chunks[c].code_base) |
+                        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_chunks[c].code_base >> 32)) << 32);
+    const uint32_t nc = __builtin_amdgcn_readfirstlane(s_chunks[c].n_codes);
+    const uint32_t b = __builtin_amdgcn_readfirstlane(s_chunks[c].b0 + (q - s_chunks[c].seq0));
+    sl.v = load_block(a, cb, nc, b);
+    sl.seq = q;
+  }
+  return sl;
+}
+
 template <bool SMALL>
 __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1) {
-  const int wave = threadIdx.x >> 6;
   float* racc = (float*)(smem + a.lds_racc);
   const ImgRegs img = stage_tables_load(a.image);
-  // prefetch ring: three blocks ahead of the block being processed
-  Cursor cu;
-  cursor_init(cu, a, items, g0, g1);
-  BlockCodes r0 = cursor_next(cu, a, items);
-  BlockCodes r1 = cursor_next(cu, a, items);
-  BlockCodes r2 = cursor_next(cu, a, items);
-  // the decode tables are stored while the first blocks are in flight
-  stage_tables(img);
-  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
-  __syncthreads();
+  build_chunks(a, items, g0, g1);
+  bool tables_staged = false;
   uint32_t cur_q = 0xFFFFFFFFu;
-  for (uint64_t g = g0; g < g1;) {
-    const Chunk ch = chunk_at(a, items, g, g1);
-    const int tc = tc_of(ch.nt);
-    if (ch.q != cur_q) {
-      if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
-      else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
-      else stage_x<4>(a, smem, perm, ch.tb, ch.nt);
-      cur_q = ch.q;
-      __syncthreads();
+  while (true) {
+    const uint32_t nch = __builtin_amdgcn_readfirstlane(s_nchunks), nseq = __builtin_amdgcn_readfirstlane(s_nseq);
+    if (nch == 0) break;
+    // prefetch ring: three blocks ahead of the block being processed
+    Slot r0 = grab(a, nseq, nch), r1 = grab(a, nseq, nch), r2 = grab(a, nseq, nch);
+    if (!tables_staged) {
+      // the decode tables are stored while the first blocks are in flight
+      stage_tables(img);
+      for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
+      tables_staged = true;
     }
-    if (ch.ok) {
-      for (uint32_t b = ch.b0 + wave; b <= ch.b1; b += kFWaves) {
-        const BlockCodes cur = r0;
+    __syncthreads();
+    for (uint32_t c = 0; c < nch; ++c) {
+      const Chunk ch = load_chunk(c);
+      const int tc = tc_of(ch.nt);
+      if (ch.q != cur_q) {
+        if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
+        else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
+        else stage_x<4>(a, smem, perm, ch.tb, ch.nt);
+        cur_q = ch.q;
+        __syncthreads();
+      }
+      const uint32_t seq_end = c + 1 < nch ? __builtin_amdgcn_readfirstlane(s_chunks[c + 1].seq0) : nseq;
+      while (r0.seq < seq_end) {
+        const Slot cur = r0;
         r0 = r1;
         r1 = r2;
-        r2 = cursor_next(cu, a, items);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur, b);
+        r2 = grab(a, nseq, nch);
+        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, ch.b0 + (cur.seq - ch.seq0));
       }
-    }
-    __syncthreads();
-    // epilogue: scale, activation, convert, scatter to token order
-    const int32_t R = ch.rb - ch.ra;
-    if (ch.ok) {
-      for (int32_t i = threadIdx.x; i < R * (int32_t)ch.nt; i += kFThreads) {
-        const int32_t t = i / R, r = i - t * R;
-        float v = racc[t * (a.rmax + 2) + r + 1];
-        const float s = (float)(*(const _Float16*)(a.scales + ch.scale_base + ch.ra + r));
-        v *= s;
-        if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
-        const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + r;
-        if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
-        else ((_Float16*)a.y)[o] = (_Float16)v;
+      __syncthreads();
+      // epilogue: scale, activation, convert, scatter to token order
+      const int32_t R = ch.rb - ch.ra;
+      if (ch.ok) {
+        for (int32_t i = threadIdx.x; i < R * (int32_t)ch.nt; i += kFThreads) {
+          const int32_t t = i / R, r = i - t * R;
+          float v = racc[t * (a.rmax + 2) + r + 1];
+          const float s = (float)(*(const _Float16*)(a.scales + ch.scale_base + ch.ra + r));
+          v *= s;
+          if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+          const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + r;
+          if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+          else ((_Float16*)a.y)[o] = (_Float16)v;
+        }
+      } else if (threadIdx.x == 0) {
+        atomicOr(&a.ws[0], 0x40000000u);
       }
-    } else if (threadIdx.x == 0) {
-      atomicOr(&a.ws[0], 0x40000000u);
+      __syncthreads();
+      // blocks write accumulator slots [0, R + 1] of tokens t < tc
+      for (int32_t i = threadIdx.x; i < tc * (R + 2); i += kFThreads) {
+        const int32_t t = i / (R + 2);
+        racc[t * (a.rmax + 2) + (i - t * (R + 2))] = 0.f;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
-    __syncthreads();
-    g += (uint64_t)R;
+    const uint64_t gn = s_gnext;
+    __syncthreads();      // every wave has read the table before it is rebuilt
+    if (gn >= g1) break;
+    build_chunks(a, items, gn, g1);
   }
 }
 
@@ -773,24 +824,19 @@ struct Plan {
 };
 static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
   p->xcols = (cols + kXPad + 7) / 8 * 8;
-  // prefer more tokens per item, then longer row chunks (fewer barriers)
+  // prefer more tokens per item, then the longest row chunks that fit
   for (int tc : {4, 2, 1}) {
-    for (int rmax : {1024, 512, 256, 128, 64}) {
-      if (rmax < 256 && tc > 1) continue;
-      const uint32_t racc = (uint32_t)(tc * (rmax + 2) * 4);
-      const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
-      const uint32_t lds_racc = 0;
-      const uint32_t lds_x = (lds_racc + racc + 15u) & ~15u;
-      const uint32_t total = (lds_x + xbytes + 15u) & ~15u;
-      if ((int)total + static_lds <= max_lds) {
-        p->tcmax = tc;
-        p->rmax = rmax;
-        p->lds_racc = lds_racc;
-        p->lds_x = lds_x;
-        p->lds_total = total;
-        return true;
-      }
-    }
+    const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
+    const int64_t room = (int64_t)max_lds - static_lds - xbytes - 32;
+    int64_t rmax = room / (4 * tc) - 2;
+    if (rmax > 4096) rmax = 4096;
+    if (rmax < (tc > 1 ? 256 : 64)) continue;
+    p->tcmax = tc;
+    p->rmax = (int)rmax;
+    p->lds_racc = 0;
+    p->lds_x = ((uint32_t)(tc * (rmax + 2) * 4) + 15u) & ~15u;
+    p->lds_total = (p->lds_x + xbytes + 15u) & ~15u;
+    return true;
   }
   return false;
 }
