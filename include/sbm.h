@@ -205,7 +205,11 @@ int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
  * [n_tokens x d]; they may not alias. */
 int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint16_t* x_out, void* stream);
 
-/* Workspace error word of the last fused call (device read; synchronises the stream). */
+/* Workspace error word of the last fused call (device read; synchronises the
+ * stream).  Bits 0-29: number of tokens whose expert id was out of range;
+ * bit 30: a touched expert's descriptor disagrees with the call's shape or
+ * alignment (its tokens get no output); bit 31: the decode image failed its
+ * header check (nothing was computed). */
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream);
 
 #ifdef __cplusplus

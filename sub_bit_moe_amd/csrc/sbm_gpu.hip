@@ -70,6 +70,8 @@ __shared__ LdsTables g_tab;
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
 constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
+constexpr int kGroupInLds = 128;  // up to this many tokens are grouped inside the fused kernel
+constexpr uint32_t kErrBadDesc = 0x40000000u, kErrBadImage = 0x80000000u;
 struct WsLayout {
   uint64_t cnt, start, chunk, perm, items, bounds, total_words;
 };
@@ -93,9 +95,12 @@ struct FusedArgs {
   const sbm_matrix_desc* experts;
   const DictImage* image;
   const uint16_t* x;
+  const int32_t* ids;
   void* y;
   uint32_t* ws;
   int32_t rows, cols, n_experts, n_tokens;
+  int32_t group_in_lds; // 1: tokens grouped by every workgroup in LDS; 0: by group_kernel in ws
+  int32_t grid;
   uint32_t flags;
   uint32_t colsB;       // 6 * cols
   uint32_t magic_s;
@@ -195,6 +200,11 @@ __device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint
   return (uint64_t)lo * rows + r;
 }
 
+// A matrix descriptor the fused kernel can use for a call of this shape.
+__device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, int32_t cols) {
+  return (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols;
+}
+
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
 __host__ __device__ inline uint32_t item_weight(uint32_t nt) {
@@ -223,7 +233,8 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
 }
 
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
-                                                         int32_t E, int32_t tcmax, int32_t rows, int32_t grid,
+                                                         int32_t E, int32_t tcmax, int32_t rows, int32_t cols,
+                                                         int32_t grid, const sbm_matrix_desc* __restrict__ experts,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
   const WsLayout L = ws_layout(E, T);
@@ -278,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
       const uint32_t nt = (n - k) < (uint32_t)tcmax ? (n - k) : (uint32_t)tcmax;
       items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt));
     }
+    if (n && !desc_ok(experts[e], rows, cols)) atomicOr(&hdr[0], kErrBadDesc);
   }
   __syncthreads();
   // exclusive prefix of the per-row weights over items (.w), total in hdr[2]
@@ -398,7 +410,7 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   ch.tb = it.y;
   ch.nt = it.z;
   const sbm_matrix_desc d = a.experts[it.x];
-  ch.ok = (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == a.rows && d.cols == a.cols;
+  ch.ok = desc_ok(d, a.rows, a.cols);
   ch.code_base = d.code_base;
   ch.n_codes = d.n_codes;
   ch.blk_base = d.blk_base;
@@ -611,7 +623,7 @@ __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, con
 
 // Chunks of the current round of a workgroup's slice (LDS) and the block
 // sequence counter the waves draw from.
-constexpr int kMaxChunks = 32;
+constexpr int kMaxChunks = 16;
 __shared__ Chunk s_chunks[kMaxChunks];
 __shared__ uint32_t s_nchunks, s_nseq, s_next_seq;
 __shared__ uint64_t s_gnext;
@@ -742,8 +754,6 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
           if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
           else ((_Float16*)a.y)[o] = (_Float16)v;
         }
-      } else if (threadIdx.x == 0) {
-        atomicOr(&a.ws[0], 0x40000000u);
       }
       __syncthreads();
       // blocks write accumulator slots [0, R + 1] of tokens t < tc
@@ -760,19 +770,105 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
   }
 }
 
+// Token grouping inside the fused kernel for n_tokens <= kGroupInLds: every
+// workgroup derives the same items as group_kernel from the ids alone.  Sort
+// key (expert << 8 | token) is unique; a token's rank among the keys is its
+// place in perm, rank minus the count of smaller experts its place in its
+// expert's run.  Items start at run places divisible by tcmax.
+__shared__ uint4 s_items[kGroupInLds];
+__shared__ int32_t s_perm[kGroupInLds];
+__shared__ uint32_t s_ghdr[4];   // n_items, total weight, invalid ids, bad descriptors
+
+__device__ void group_lds(const FusedArgs& a, uint32_t* keys /* LDS, 2 * n_tokens words */) {
+  const int32_t T = a.n_tokens;
+  uint32_t* ntv = keys + T;
+  const int t = threadIdx.x;
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  uint32_t key = kNone;
+  if (t < T) {
+    const int32_t e = a.ids[t];
+    key = (e >= 0 && e < a.n_experts) ? ((uint32_t)e << 8) | (uint32_t)t : kNone;
+    keys[t] = key;
+  }
+  __syncthreads();
+  uint32_t rank = 0, lt = 0, eq = 0;
+  if (key != kNone) {
+    const uint32_t ek = key >> 8;
+    for (int32_t j = 0; j < T; ++j) {
+      const uint32_t kj = keys[j];
+      rank += kj < key;
+      lt += (kj >> 8) < ek;
+      eq += (kj >> 8) == ek;
+    }
+  }
+  const uint32_t off = rank - lt;
+  const uint32_t tcm = (uint32_t)a.tcmax;
+  const bool start = key != kNone && off % tcm == 0;
+  const uint32_t nt = start ? (eq - off < tcm ? eq - off : tcm) : 0u;
+  if (t < T) ntv[t] = nt;
+  if (key != kNone) s_perm[rank] = t;
+  __syncthreads();
+  if (start || t == 0) {
+    uint32_t q = 0, wpre = 0, n_items = 0, wtot = 0, bad = 0;
+    for (int32_t j = 0; j < T; ++j) {
+      const uint32_t kj = keys[j], nj = ntv[j];
+      const uint32_t wj = nj ? item_weight(nj) : 0u;
+      const bool before = nj && kj < key;
+      q += before;
+      wpre += before ? wj : 0u;
+      n_items += nj != 0;
+      wtot += wj;
+      bad += kj == kNone;
+    }
+    if (start) s_items[q] = make_uint4(key >> 8, rank, nt, wpre);
+    if (t == 0) {
+      s_ghdr[0] = n_items;
+      s_ghdr[1] = wtot;
+      s_ghdr[2] = bad;
+      s_ghdr[3] = 0;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    // descriptors of the touched experts; workgroup 0 alone writes the error word
+    const uint32_t n_items = s_ghdr[0];
+    for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
+      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols)) atomicOr(&s_ghdr[3], 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) a.ws[0] = s_ghdr[2] | (s_ghdr[3] ? kErrBadDesc : 0u);
+  }
+}
+
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
       a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ws[0], 0x80000000u);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      if (a.group_in_lds) a.ws[0] = kErrBadImage;
+      else atomicOr(&a.ws[0], kErrBadImage);
+    }
     return;
   }
-  const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
-  const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
-  const uint64_t g0 = bounds[blockIdx.x], g1 = bounds[blockIdx.x + 1];
+  const int32_t* perm;
+  const uint4* items;
+  uint64_t g0, g1;
+  if (a.group_in_lds) {
+    group_lds(a, (uint32_t*)smem);
+    const uint32_t n_items = s_ghdr[0], wtot = s_ghdr[1];
+    const uint64_t wrows = (uint64_t)wtot * (uint64_t)a.rows;
+    g0 = weighted_boundary(s_items, n_items, wtot, a.rows, wrows * blockIdx.x / (uint64_t)a.grid);
+    g1 = weighted_boundary(s_items, n_items, wtot, a.rows, wrows * (blockIdx.x + 1) / (uint64_t)a.grid);
+    perm = s_perm;
+    items = s_items;
+  } else {
+    const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
+    const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
+    g0 = bounds[blockIdx.x];
+    g1 = bounds[blockIdx.x + 1];
+    perm = (const int32_t*)(a.ws + L.perm);
+    items = (const uint4*)(a.ws + L.items);
+  }
   if (g0 >= g1) return;
-  const int32_t* perm = (const int32_t*)(a.ws + L.perm);
-  const uint4* items = (const uint4*)(a.ws + L.items);
   if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1);
   else run_slice<false>(a, smem, perm, items, g0, g1);
 }
@@ -902,6 +998,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   a.experts = experts;
   a.image = (const DictImage*)dict_image;
   a.x = x;
+  a.ids = expert_ids;
   a.y = y;
   a.ws = (uint32_t*)workspace;
   a.rows = rows;
@@ -923,11 +1020,18 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (grid > di->cus) grid = di->cus;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                     plan.tcmax, rows, (int32_t)grid, (uint32_t*)workspace);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), plan.lds_total, s, a);
+  a.grid = (int32_t)grid;
+  a.group_in_lds = n_tokens <= kGroupInLds && n_experts < (1 << 24);
+  hipError_t e;
+  if (!a.group_in_lds) {
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
+                       plan.tcmax, rows, cols, (int32_t)grid, experts, (uint32_t*)workspace);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
+  }
+  // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
+  const uint32_t lds = std::max<uint32_t>(plan.lds_total, 8u * kGroupInLds);
+  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
   return SBM_OK;

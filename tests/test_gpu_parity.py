@@ -108,7 +108,7 @@ def test_fused_grouped_routing_and_edges(dev, lib_state, odict):
     E, rows, cols = 12, 300, 512
     ex = P.host_experts(E, rows, cols, 0.886, 99)
     rng = np.random.default_rng(3)
-    for T in (1, 8, 32, 37):
+    for T in (1, 8, 32, 37, 129):
         x = rng.standard_normal((T, cols)).astype(np.float16)
         ids = rng.integers(0, E, T).astype(np.int32)
         ids[: T // 2] = 4                      # one heavy expert; several experts stay empty
@@ -119,23 +119,56 @@ def test_fused_grouped_routing_and_edges(dev, lib_state, odict):
             P.assert_close(y[t], ref, what=f"T={T} token {t}")
 
 
-def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict):
+@pytest.mark.parametrize("T", [4, 140])
+def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict, T):
+    """Up to 128 tokens are grouped inside the fused kernel, more by the
+    grouping kernel: both count out-of-range ids and leave their rows alone."""
     api = lib_state["api"]
     E, rows, cols = 3, 64, 256
     ex = P.host_experts(E, rows, cols, 0.886, 5)
     mats = P.encode_all(ex, odict["words"])
     stack = api.ExpertStack.from_host(mats, rows, cols, dev)
-    x = np.random.default_rng(1).standard_normal((4, cols)).astype(np.float16)
-    ids = np.array([0, -1, 7, 2], np.int32)
-    y = torch.full((4, rows), float("nan"), dtype=torch.float32, device=dev)
-    ws = api.alloc_workspace(E, 4, dev)
+    x = np.random.default_rng(1).standard_normal((T, cols)).astype(np.float16)
+    ids = np.random.default_rng(2).integers(0, E, T).astype(np.int32)
+    ids[:4] = [0, -1, 7, 2]
+    bad = (ids < 0) | (ids >= E)
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+    ws = api.alloc_workspace(E, T, dev)
     api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
                                 torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, y=y)
     torch.cuda.synchronize()
-    assert api.workspace_error(ws) == 2
+    assert api.workspace_error(ws) == int(bad.sum())
     yn = y.cpu().numpy()
-    assert np.isnan(yn[1]).all() and np.isnan(yn[2]).all()
-    for t in (0, 3):
+    assert np.isnan(yn[bad]).all()
+    for t in np.flatnonzero(~bad)[:12]:
+        P.assert_close(yn[t], P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0])
+
+
+@pytest.mark.parametrize("T", [5, 150])
+def test_fused_bad_descriptor_is_flagged(dev, lib_state, odict, T):
+    """An expert whose descriptor disagrees with the call's shape produces no
+    rows and sets the descriptor bit of the error word; the others are exact."""
+    import ctypes
+    from sub_bit_moe_amd import _native as N
+    api = lib_state["api"]
+    E, rows, cols = 3, 64, 256
+    ex = P.host_experts(E, rows, cols, 0.886, 6)
+    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev)
+    descs = list(stack.host_desc)
+    descs[1].rows = rows + 1
+    arr = (N.MatrixDesc * E)(*descs)
+    stack.desc.copy_(torch.from_numpy(np.frombuffer(bytes(arr), np.uint8).copy()))
+    x = np.random.default_rng(3).standard_normal((T, cols)).astype(np.float16)
+    ids = (np.arange(T) % E).astype(np.int32)
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+    ws = api.alloc_workspace(E, T, dev)
+    api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
+                                torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 0x40000000
+    yn = y.cpu().numpy()
+    assert np.isnan(yn[ids == 1]).all()
+    for t in np.flatnonzero(ids != 1)[:8]:
         P.assert_close(yn[t], P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0])
 
 
