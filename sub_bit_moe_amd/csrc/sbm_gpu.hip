@@ -70,6 +70,9 @@ __shared__ LdsTables g_tab;
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
 constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
+constexpr int kItemChangeBlocks = 12;
+constexpr int kMaxRmax = 4096;    // rows per chunk
+constexpr int kEpiRegs = (kMaxRmax + 2 + kFThreads - 1) / kFThreads;   // epilogue slots per thread
 constexpr int kGroupInLds = 128;  // up to this many tokens are grouped inside the fused kernel
 constexpr uint32_t kErrBadDesc = 0x40000000u, kErrBadImage = 0x80000000u;
 struct WsLayout {
@@ -101,6 +104,7 @@ struct FusedArgs {
   int32_t rows, cols, n_experts, n_tokens;
   int32_t group_in_lds; // 1: tokens grouped by every workgroup in LDS; 0: by group_kernel in ws
   int32_t grid;
+  uint32_t item_cost;   // slice weight of an item change (row weights are 4..6)
   uint32_t flags;
   uint32_t colsB;       // 6 * cols
   uint32_t magic_s;
@@ -180,24 +184,39 @@ __global__ void decode_ref_kernel(const uint16_t* __restrict__ codes,
 // indices by expert, and the item list (expert, first token, token count) with
 // at most tcmax tokens per item.  Experts without tokens get no item ([QMoE]:
 // calls for experts that receive no tokens are skipped).
-// Global row index (item * rows + row) where weighted position u falls: item q
-// covers weighted positions [wpre_q * rows, wpre_{q+1} * rows), each of its
-// rows weighing wpre_{q+1} - wpre_q.  Monotone in u, so consecutive
-// workgroups tile the row space exactly.
-__device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint32_t wtot, int32_t rows, uint64_t u) {
-  if (n_items == 0 || u >= (uint64_t)wtot * rows) return (uint64_t)n_items * rows;
-  uint32_t lo = 0, hi = n_items - 1;      // last item with wpre * rows <= u
+// Workgroup slices split the (item, row) space by estimated cost.  Item q,
+// whose rows each weigh w_q, covers weighted positions [P_q, P_q + F + w_q *
+// rows) with P_q = wpre_q * rows + q * F (wpre_q: exclusive prefix of w); the
+// leading F charges the activation restaging and drain of an item change to
+// the slice that contains it.  Positions map monotonically to global row
+// indices (item * rows + row), so consecutive workgroups tile the row space.
+__device__ __forceinline__ uint64_t udiv_small(uint64_t n, uint32_t d) {
+  return (n >> 32) == 0 ? (uint64_t)((uint32_t)n / d) : n / d;
+}
+
+__device__ __forceinline__ uint64_t boundary_in_item(uint64_t u, uint64_t pq, uint32_t q, uint32_t wq, uint32_t F,
+                                                     uint64_t rows) {
+  uint64_t r = 0;
+  if (u > pq + F) {
+    r = udiv_small(u - pq - F + wq - 1, wq);
+    if (r > rows) r = rows;
+  }
+  return (uint64_t)q * rows + r;
+}
+
+__device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint32_t wtot, int32_t rows, uint32_t F,
+                                      uint64_t u) {
+  const uint64_t R = (uint64_t)rows;
+  if (n_items == 0 || u >= (uint64_t)wtot * R + (uint64_t)n_items * F) return (uint64_t)n_items * R;
+  uint32_t lo = 0, hi = n_items - 1;      // last item with P_q <= u
   while (lo < hi) {
     const uint32_t mid = (lo + hi + 1) / 2;
-    if ((uint64_t)items[mid].w * rows <= u) lo = mid;
+    if ((uint64_t)items[mid].w * R + (uint64_t)mid * F <= u) lo = mid;
     else hi = mid - 1;
   }
-  const uint64_t w0 = items[lo].w;
-  const uint64_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
-  const uint64_t wq = w1 > w0 ? w1 - w0 : 1;
-  uint64_t r = (u - w0 * rows + wq - 1) / wq;
-  if (r > (uint64_t)rows) r = rows;
-  return (uint64_t)lo * rows + r;
+  const uint32_t w0 = items[lo].w;
+  const uint32_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
+  return boundary_in_item(u, (uint64_t)w0 * R + (uint64_t)lo * F, lo, w1 > w0 ? w1 - w0 : 1u, F, R);
 }
 
 // A matrix descriptor the fused kernel can use for a call of this shape.
@@ -234,7 +253,8 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
 
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
                                                          int32_t E, int32_t tcmax, int32_t rows, int32_t cols,
-                                                         int32_t grid, const sbm_matrix_desc* __restrict__ experts,
+                                                         int32_t grid, uint32_t item_cost,
+                                                         const sbm_matrix_desc* __restrict__ experts,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
   const WsLayout L = ws_layout(E, T);
@@ -307,9 +327,9 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   __syncthreads();
   // contiguous weighted slices of the (item, row) space, one per fused workgroup
   uint64_t* bounds = (uint64_t*)(ws + L.bounds);
-  const uint64_t wrows = (uint64_t)carry * (uint64_t)rows;
+  const uint64_t wall = (uint64_t)carry * (uint64_t)rows + (uint64_t)n_items * item_cost;
   for (int g = threadIdx.x; g <= grid; g += kThreads)
-    bounds[g] = weighted_boundary(items, n_items, carry, rows, wrows * (uint64_t)g / (uint64_t)grid);
+    bounds[g] = weighted_boundary(items, n_items, carry, rows, item_cost, wall * (uint64_t)g / (uint64_t)grid);
 }
 
 // ------------------------------------------------------------ fused kernel
@@ -382,8 +402,11 @@ __device__ __forceinline__ void acc_x(float* acc, const XVal<TC>& x) {
   }
 }
 
+// The codewords of one block as this lane sees them, and the block's start
+// position (bstart, in symbols from the matrix start).
 struct BlockCodes {
   uint4 a, b;
+  uint32_t bst;
 };
 
 // Everything a workgroup needs about one chunk: rows [ra, rb) of item q.
@@ -398,14 +421,13 @@ struct Chunk {
   bool ok;
 };
 
-__device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
+// Rows [ra, rb) of item q.
+__device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items, uint32_t q, int32_t ra,
+                                          int32_t rb) {
   Chunk ch;
-  ch.q = (uint32_t)(g / (uint64_t)a.rows);
-  ch.ra = (int32_t)(g - (uint64_t)ch.q * a.rows);
-  int64_t rb = ch.ra + a.rmax;
-  if (rb > a.rows) rb = a.rows;
-  if ((uint64_t)(rb - ch.ra) > g1 - g) rb = ch.ra + (int64_t)(g1 - g);
-  ch.rb = (int32_t)rb;
+  ch.q = q;
+  ch.ra = ra;
+  ch.rb = rb;
   const uint4 it = items[ch.q];
   ch.tb = it.y;
   ch.nt = it.z;
@@ -452,8 +474,7 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
 
 // One block of SBM_BLOCK codewords, kK per lane.
 template <int TC, bool SMALL>
-__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
-                              uint32_t b) {
+__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw) {
   const int lane = threadIdx.x & 63;
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
   uint32_t c[kK], kk[kK];
@@ -484,7 +505,7 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
 #pragma unroll
   for (int j = 0; j < kK; ++j) slots[j] += sp[j];
   const uint32_t excl = wave_incl_scan(tot) - tot;
-  const uint32_t pl = 6u * a.bstart[ch.blk_base + b] + excl;   // lane start, bytes
+  const uint32_t pl = 6u * raw.bst + excl;   // lane start, bytes
   float* racc = (float*)(smem + a.lds_racc);
   const int32_t R = ch.rb - ch.ra;
   if constexpr (!SMALL) {
@@ -554,8 +575,43 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
 
 // Stage the activations of an item's tokens as triples [-x, +x, 0] per column,
 // tokens interleaved: element (col, k, t) at byte ((3*col + k) * TC + t) * 2.
-// Columns past cols are zero.  Each thread takes 8 columns of all TC tokens
-// (one 16-byte load per token) and writes 48*TC contiguous bytes.
+// Columns past cols are zero.  Each thread takes groups of 8 columns of all TC
+// tokens (one 16-byte load per token) and writes 48*TC contiguous bytes.
+template <int TC>
+__device__ __forceinline__ void store_x_group(const FusedArgs& a, unsigned char* smem, int32_t c0,
+                                              const uint32_t (&p)[TC][4]) {
+  uint32_t o[12 * TC];
+  if constexpr (TC == 1) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {           // columns 2m, 2m+1
+      const uint32_t x = p[0][m];
+      const uint32_t xl = x & 0xFFFFu, xh = x >> 16;
+      o[3 * m + 0] = (xl ^ 0x8000u) | (xl << 16);          // [-x0, +x0]
+      o[3 * m + 1] = (xh ^ 0x8000u) << 16;                 // [0, -x1]
+      o[3 * m + 2] = xh;                                   // [+x1, 0]
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int tp = 0; tp < TC / 2; ++tp) {                // token pair (2tp, 2tp+1)
+        const uint32_t a0 = p[2 * tp][c / 2], a1 = p[2 * tp + 1][c / 2];
+        const uint32_t pair = (c & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+        o[(3 * c + 0) * (TC / 2) + tp] = pair ^ 0x80008000u;
+        o[(3 * c + 1) * (TC / 2) + tp] = pair;
+        o[(3 * c + 2) * (TC / 2) + tp] = 0u;
+      }
+    }
+  }
+  uint4* d = (uint4*)(smem + a.lds_x + (uint32_t)(6 * c0 * TC));
+#pragma unroll
+  for (int q = 0; q < 3 * TC; ++q) d[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+}
+
+__device__ __forceinline__ bool x_vec(const FusedArgs& a) {
+  return (a.cols % 8) == 0 && ((uintptr_t)a.x & 15u) == 0;
+}
+
 template <int TC>
 __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
                         uint32_t nt) {
@@ -563,7 +619,7 @@ __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* 
 #pragma unroll
   for (int t = 0; t < TC; ++t) tok[t] = (uint32_t)t < nt ? perm[tb + t] : -1;
   const int32_t n8 = a.xcols / 8;
-  const bool vec = (a.cols % 8) == 0 && ((uintptr_t)a.x & 15u) == 0;
+  const bool vec = x_vec(a);
   for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
     const int32_t c0 = 8 * i;
     uint32_t p[TC][4];                       // [token][column pair] fp16x2
@@ -582,32 +638,52 @@ __device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* 
         }
       }
     }
-    uint32_t o[12 * TC];
-    if constexpr (TC == 1) {
+    store_x_group<TC>(a, smem, c0, p);
+  }
+}
+
+// Activations of the next item, requested before the drain barrier of the
+// current chunk and stored after it: up to 4 groups of 8 columns x tokens
+// per thread (4/TC groups of TC tokens), vector loads only.
+struct XPre {
+  uint4 v[4];
+};
+
+__device__ __forceinline__ bool x_prefetchable(const FusedArgs& a, int tc) {
+  return x_vec(a) && a.xcols / 8 <= kFThreads * (4 / tc);
+}
+
+template <int TC>
+__device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* perm, uint32_t tb, uint32_t nt,
+                                          XPre& r) {
+  const int32_t n8 = a.xcols / 8;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {           // columns 2m, 2m+1
-        const uint32_t x = p[0][m];
-        const uint32_t xl = x & 0xFFFFu, xh = x >> 16;
-        o[3 * m + 0] = (xl ^ 0x8000u) | (xl << 16);          // [-x0, +x0]
-        o[3 * m + 1] = (xh ^ 0x8000u) << 16;                 // [0, -x1]
-        o[3 * m + 2] = xh;                                   // [+x1, 0]
-      }
-    } else {
+  for (int j = 0; j < 4 / TC; ++j) {
+    const int32_t c0 = 8 * ((int32_t)threadIdx.x + j * kFThreads);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int tp = 0; tp < TC / 2; ++tp) {                // token pair (2tp, 2tp+1)
-          const uint32_t a0 = p[2 * tp][c / 2], a1 = p[2 * tp + 1][c / 2];
-          const uint32_t pair = (c & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-          o[(3 * c + 0) * (TC / 2) + tp] = pair ^ 0x80008000u;
-          o[(3 * c + 1) * (TC / 2) + tp] = pair;
-          o[(3 * c + 2) * (TC / 2) + tp] = 0u;
-        }
-      }
+    for (int t = 0; t < TC; ++t) {
+      const int32_t tok = (uint32_t)t < nt ? perm[tb + t] : -1;
+      r.v[j * TC + t] = (tok >= 0 && c0 + 8 <= a.cols && c0 < 8 * n8)
+                            ? *(const uint4*)(a.x + (int64_t)tok * a.cols + c0) : make_uint4(0, 0, 0, 0);
     }
-    uint4* d = (uint4*)(smem + a.lds_x + (uint32_t)(6 * c0 * TC));
+  }
+}
+
+template <int TC>
+__device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* smem, const XPre& r) {
+  const int32_t n8 = a.xcols / 8;
 #pragma unroll
-    for (int q = 0; q < 3 * TC; ++q) d[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  for (int j = 0; j < 4 / TC; ++j) {
+    const int32_t i = (int32_t)threadIdx.x + j * kFThreads;
+    if (i < n8) {
+      uint32_t p[TC][4];
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {
+        const uint4 v = r.v[j * TC + t];
+        p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
+      }
+      store_x_group<TC>(a, smem, 8 * i, p);
+    }
   }
 }
 
@@ -615,10 +691,10 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
-                                                 const BlockCodes& raw, uint32_t b) {
-  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, b);
-  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, b);
-  else process_block<4, SMALL>(a, ch, smem, raw, b);
+                                                 const BlockCodes& raw) {
+  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw);
+  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw);
+  else process_block<4, SMALL>(a, ch, smem, raw);
 }
 
 // Chunks of the current round of a workgroup's slice (LDS) and the block
@@ -628,21 +704,60 @@ __shared__ Chunk s_chunks[kMaxChunks];
 __shared__ uint32_t s_nchunks, s_nseq, s_next_seq;
 __shared__ uint64_t s_gnext;
 
-// Fill the chunk table from row index g (at most kMaxChunks chunks).
-__device__ void build_chunks(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
-  if (threadIdx.x == 0) {
-    uint32_t n = 0, seq = 0;
-    while (g < g1 && n < (uint32_t)kMaxChunks) {
-      Chunk ch = chunk_at(a, items, g, g1);
-      ch.seq0 = seq;
-      if (ch.ok && ch.b1 >= ch.b0) seq += ch.b1 - ch.b0 + 1;
-      s_chunks[n++] = ch;
-      g += (uint64_t)(ch.rb - ch.ra);
+// Fill the chunk table from global row index g (at most kMaxChunks chunks):
+// lane i of wave 0 walks the row arithmetic to chunk i's start, then loads
+// its descriptor and row offsets; a wave scan of block counts numbers the
+// blocks of the round.
+__device__ __forceinline__ void build_chunks(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
+  static_assert(kMaxChunks <= 64, "one lane per chunk");
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint32_t q = (uint32_t)udiv_small(g, (uint32_t)a.rows);
+    int32_t ra = (int32_t)(g - (uint64_t)q * a.rows);
+    uint64_t gg = g;
+    // end row of the chunk starting at row ra of an item, global index gg
+    auto chunk_end = [&](int32_t r0, uint64_t at) {
+      int64_t e = (int64_t)r0 + a.rmax;
+      if (e > a.rows) e = a.rows;
+      if ((uint64_t)(e - r0) > g1 - at) e = r0 + (int64_t)(g1 - at);
+      return (int32_t)e;
+    };
+    for (int k = 0; k < lane && gg < g1; ++k) {
+      const int32_t e = chunk_end(ra, gg);
+      gg += (uint64_t)(e - ra);
+      if (e == a.rows) {
+        ++q;
+        ra = 0;
+      } else {
+        ra = e;
+      }
     }
-    s_nchunks = n;
-    s_nseq = seq;
-    s_next_seq = 0;
-    s_gnext = g;
+    const bool exists = lane < kMaxChunks && gg < g1;
+    const int32_t rb = exists ? chunk_end(ra, gg) : ra;
+    Chunk ch;
+    uint32_t nblk = 0;
+    if (exists) {
+      ch = chunk_at(a, items, q, ra, rb);
+      if (ch.ok && ch.b1 >= ch.b0) nblk = ch.b1 - ch.b0 + 1;
+    }
+    const uint32_t incl = wave_incl_scan(nblk);
+    const uint32_t nch = (uint32_t)__popcll(__ballot(exists));
+    if (exists) {
+      ch.seq0 = incl - nblk;
+      s_chunks[lane] = ch;
+      if ((uint32_t)lane == nch - 1) {
+        s_nseq = incl;
+        s_gnext = gg + (uint64_t)(rb - ra);
+      }
+    }
+    if (lane == 0) {
+      s_nchunks = nch;
+      s_next_seq = 0;
+      if (nch == 0) {
+        s_nseq = 0;
+        s_gnext = g1;
+      }
+    }
   }
   __syncthreads();
 }
@@ -690,38 +805,40 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
   sl.seq = 0xFFFFFFFFu;
   sl.v.a = make_uint4(0, 0, 0, 0);
   sl.v.b = sl.v.a;
+  sl.v.bst = 0;
   if (q < nseq) {
+    auto u64 = [](uint64_t v) {
+      return (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)v) |
+             ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32);
+    };
     const uint32_t c = chunk_of_seq(q, nch);
-    const uint64_t cb = (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)s_chunks[c].code_base) |
-                        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_chunks[c].code_base >> 32)) << 32);
+    const uint64_t cb = u64(s_chunks[c].code_base), bb = u64(s_chunks[c].blk_base);
     const uint32_t nc = __builtin_amdgcn_readfirstlane(s_chunks[c].n_codes);
     const uint32_t b = __builtin_amdgcn_readfirstlane(s_chunks[c].b0 + (q - s_chunks[c].seq0));
+    // the block start is requested with the codes, so that waiting for this
+    // block never waits for blocks requested after it
     sl.v = load_block(a, cb, nc, b);
+    sl.v.bst = a.bstart[bb + b];
     sl.seq = q;
   }
   return sl;
 }
 
 template <bool SMALL>
-__device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
-                          uint64_t g0, uint64_t g1) {
+__device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
+                          uint64_t g0, uint64_t g1, const ImgRegs& img) {
   float* racc = (float*)(smem + a.lds_racc);
-  const ImgRegs img = stage_tables_load(a.image);
+  // the image arrived while the slice was computed; storing it before any
+  // block is requested keeps these stores from waiting for block loads
+  stage_tables(img);
+  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
   build_chunks(a, items, g0, g1);
-  bool tables_staged = false;
   uint32_t cur_q = 0xFFFFFFFFu;
   while (true) {
     const uint32_t nch = __builtin_amdgcn_readfirstlane(s_nchunks), nseq = __builtin_amdgcn_readfirstlane(s_nseq);
     if (nch == 0) break;
     // prefetch ring: three blocks ahead of the block being processed
     Slot r0 = grab(a, nseq, nch), r1 = grab(a, nseq, nch), r2 = grab(a, nseq, nch);
-    if (!tables_staged) {
-      // the decode tables are stored while the first blocks are in flight
-      stage_tables(img);
-      for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
-      tables_staged = true;
-    }
-    __syncthreads();
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
       const int tc = tc_of(ch.nt);
@@ -738,28 +855,66 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
         r0 = r1;
         r1 = r2;
         r2 = grab(a, nseq, nch);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, ch.b0 + (cur.seq - ch.seq0));
+        process_dispatch<SMALL>(tc, a, ch, smem, cur.v);
       }
-      __syncthreads();
-      // epilogue: scale, activation, convert, scatter to token order
+      // This wave has no more blocks of the chunk.  While the others finish,
+      // request the row scales of this thread's epilogue rows and, when the
+      // next chunk starts another item, that item's activations.
       const int32_t R = ch.rb - ch.ra;
-      if (ch.ok) {
-        for (int32_t i = threadIdx.x; i < R * (int32_t)ch.nt; i += kFThreads) {
-          const int32_t t = i / R, r = i - t * R;
-          float v = racc[t * (a.rmax + 2) + r + 1];
-          const float s = (float)(*(const _Float16*)(a.scales + ch.scale_base + ch.ra + r));
-          v *= s;
-          if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
-          const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + r;
-          if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
-          else ((_Float16*)a.y)[o] = (_Float16)v;
+      uint32_t sc[kEpiRegs];
+#pragma unroll
+      for (int k = 0; k < kEpiRegs; ++k) {
+        const int32_t i = (int32_t)threadIdx.x + k * kFThreads;   // accumulator slot, row i - 1
+        sc[k] = (ch.ok && i >= 1 && i <= R) ? a.scales[ch.scale_base + ch.ra + i - 1] : 0u;
+      }
+      bool next_new = false, next_pre = false;
+      Chunk nx;
+      XPre xp;
+      if (c + 1 < nch) {
+        nx = load_chunk(c + 1);
+        next_new = nx.q != ch.q;
+        const int ntc = tc_of(nx.nt);
+        if (next_new && x_prefetchable(a, ntc)) {
+          next_pre = true;
+          if (ntc == 1) xpre_load<1>(a, perm, nx.tb, nx.nt, xp);
+          else if (ntc == 2) xpre_load<2>(a, perm, nx.tb, nx.nt, xp);
+          else xpre_load<4>(a, perm, nx.tb, nx.nt, xp);
         }
       }
       __syncthreads();
-      // blocks write accumulator slots [0, R + 1] of tokens t < tc
-      for (int32_t i = threadIdx.x; i < tc * (R + 2); i += kFThreads) {
-        const int32_t t = i / (R + 2);
-        racc[t * (a.rmax + 2) + (i - t * (R + 2))] = 0.f;
+      // epilogue: scale, activation, convert, scatter to token order; the
+      // accumulator slots [0, R + 1] of tokens t < tc are cleared for the next chunk
+#pragma unroll
+      for (int k = 0; k < kEpiRegs; ++k) {
+        const int32_t i = (int32_t)threadIdx.x + k * kFThreads;
+        if (i < R + 2) {
+          const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
+          for (int t = 0; t < tc; ++t) {
+            float* p = racc + t * (a.rmax + 2) + i;
+            float v = *p;
+            *p = 0.f;
+            if (ch.ok && i >= 1 && i <= R && (uint32_t)t < ch.nt) {
+              v *= s;
+              if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+              const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + i - 1;
+              if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+              else ((_Float16*)a.y)[o] = (_Float16)v;
+            }
+          }
+        }
+      }
+      if (next_new) {
+        const int ntc = tc_of(nx.nt);
+        if (next_pre) {
+          if (ntc == 1) xpre_store<1>(a, smem, xp);
+          else if (ntc == 2) xpre_store<2>(a, smem, xp);
+          else xpre_store<4>(a, smem, xp);
+        } else {
+          if (ntc == 1) stage_x<1>(a, smem, perm, nx.tb, nx.nt);
+          else if (ntc == 2) stage_x<2>(a, smem, perm, nx.tb, nx.nt);
+          else stage_x<4>(a, smem, perm, nx.tb, nx.nt);
+        }
+        cur_q = nx.q;
       }
       __syncthreads();
     }
@@ -771,61 +926,120 @@ __device__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t
 }
 
 // Token grouping inside the fused kernel for n_tokens <= kGroupInLds: every
-// workgroup derives the same items as group_kernel from the ids alone.  Sort
-// key (expert << 8 | token) is unique; a token's rank among the keys is its
-// place in perm, rank minus the count of smaller experts its place in its
-// expert's run.  Items start at run places divisible by tcmax.
+// workgroup derives the same items as group_kernel from the ids alone.  The
+// sort key (expert << 8 | token) is unique; a token's rank among the keys is
+// its place in perm, and rank minus the count of smaller experts its place in
+// its expert's run.  Items start at run places divisible by tcmax; a wave
+// scan over sorted places numbers them and sums their weights.
 __shared__ uint4 s_items[kGroupInLds];
 __shared__ int32_t s_perm[kGroupInLds];
-__shared__ uint32_t s_ghdr[4];   // n_items, total weight, invalid ids, bad descriptors
+__shared__ uint32_t s_ghdr[4];   // n_items, total weight, valid tokens, bad descriptors
+__shared__ uint64_t s_slice[2];  // this workgroup's [g0, g1)
+constexpr uint32_t kGroupScratch = 6 * kGroupInLds * 4;   // bytes of dynamic LDS used while grouping
+static_assert(kFThreads % kGroupInLds == 0 && kGroupInLds == 128, "4 threads per token, 2 places per lane");
 
-__device__ void group_lds(const FusedArgs& a, uint32_t* keys /* LDS, 2 * n_tokens words */) {
-  const int32_t T = a.n_tokens;
-  uint32_t* ntv = keys + T;
-  const int t = threadIdx.x;
+__device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int32_t my_id) {
+  constexpr int N = kGroupInLds;
+  constexpr int kParts = kFThreads / N;
   constexpr uint32_t kNone = 0xFFFFFFFFu;
-  uint32_t key = kNone;
-  if (t < T) {
-    const int32_t e = a.ids[t];
-    key = (e >= 0 && e < a.n_experts) ? ((uint32_t)e << 8) | (uint32_t)t : kNone;
-    keys[t] = key;
+  uint32_t* keys = sc;           // by token
+  uint32_t* rk = sc + N;         // rank, smaller experts, same expert: by token
+  uint32_t* lt = sc + 2 * N;
+  uint32_t* eq = sc + 3 * N;
+  uint32_t* nts = sc + 4 * N;    // item size at an item's first sorted place, else 0
+  uint32_t* ks = sc + 5 * N;     // key by sorted place
+  const int32_t T = a.n_tokens;
+  const int tid = threadIdx.x;
+  if (tid < N) {
+    uint32_t key = kNone;
+    if (tid < T && my_id >= 0 && my_id < a.n_experts) key = ((uint32_t)my_id << 8) | (uint32_t)tid;
+    keys[tid] = key;
+    rk[tid] = 0;
+    lt[tid] = 0;
+    eq[tid] = 0;
+    nts[tid] = 0;
+    if (tid < 4) s_ghdr[tid] = 0;
   }
   __syncthreads();
-  uint32_t rank = 0, lt = 0, eq = 0;
-  if (key != kNone) {
-    const uint32_t ek = key >> 8;
-    for (int32_t j = 0; j < T; ++j) {
-      const uint32_t kj = keys[j];
-      rank += kj < key;
-      lt += (kj >> 8) < ek;
-      eq += (kj >> 8) == ek;
+  {
+    const int t = tid % N, part = tid / N;
+    const int span = ((T + 4 * kParts - 1) / (4 * kParts)) * 4;   // keys per part, multiple of 4
+    const uint32_t key = t < T ? keys[t] : kNone;
+    if (key != kNone) {
+      const uint32_t ek = key >> 8;
+      uint32_t r = 0, l = 0, m = 0;
+      const int j0 = part * span, j1 = j0 + span < N ? j0 + span : N;
+      for (int j = j0; j < j1; j += 4) {
+        const uint4 k4 = *(const uint4*)(keys + j);
+        const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          r += kk[u] < key;
+          l += (kk[u] >> 8) < ek;
+          m += (kk[u] >> 8) == ek;
+        }
+      }
+      if (r) atomicAdd(&rk[t], r);
+      if (l) atomicAdd(&lt[t], l);
+      atomicAdd(&eq[t], m);
     }
   }
-  const uint32_t off = rank - lt;
-  const uint32_t tcm = (uint32_t)a.tcmax;
-  const bool start = key != kNone && off % tcm == 0;
-  const uint32_t nt = start ? (eq - off < tcm ? eq - off : tcm) : 0u;
-  if (t < T) ntv[t] = nt;
-  if (key != kNone) s_perm[rank] = t;
   __syncthreads();
-  if (start || t == 0) {
-    uint32_t q = 0, wpre = 0, n_items = 0, wtot = 0, bad = 0;
-    for (int32_t j = 0; j < T; ++j) {
-      const uint32_t kj = keys[j], nj = ntv[j];
-      const uint32_t wj = nj ? item_weight(nj) : 0u;
-      const bool before = nj && kj < key;
-      q += before;
-      wpre += before ? wj : 0u;
-      n_items += nj != 0;
-      wtot += wj;
-      bad += kj == kNone;
+  if (tid < N) {
+    const uint32_t key = keys[tid];
+    const bool valid = key != kNone;
+    if (valid) {
+      const uint32_t rank = rk[tid], off = rank - lt[tid], cnt = eq[tid];
+      const uint32_t tcm = (uint32_t)a.tcmax;
+      s_perm[rank] = tid;
+      ks[rank] = key;
+      if (off % tcm == 0) nts[rank] = cnt - off < tcm ? cnt - off : tcm;
     }
-    if (start) s_items[q] = make_uint4(key >> 8, rank, nt, wpre);
-    if (t == 0) {
-      s_ghdr[0] = n_items;
-      s_ghdr[1] = wtot;
-      s_ghdr[2] = bad;
-      s_ghdr[3] = 0;
+    const uint64_t b = __ballot(valid);
+    if ((tid & 63) == 0 && b) atomicAdd(&s_ghdr[2], (uint32_t)__popcll(b));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t n0 = nts[2 * tid], n1 = nts[2 * tid + 1];
+    const uint32_t w0 = n0 ? item_weight(n0) : 0u, w1 = n1 ? item_weight(n1) : 0u;
+    const uint32_t c = (n0 != 0) + (n1 != 0);
+    const uint32_t ci = wave_incl_scan(c), wi = wave_incl_scan(w0 + w1);
+    uint32_t q = ci - c, wp = wi - w0 - w1;
+    if (n0) {
+      s_items[q] = make_uint4(ks[2 * tid] >> 8, 2 * tid, n0, wp);
+      ++q;
+      wp += w0;
+    }
+    if (n1) s_items[q] = make_uint4(ks[2 * tid + 1] >> 8, 2 * tid + 1, n1, wp);
+    if (tid == 63) {
+      s_ghdr[0] = ci;
+      s_ghdr[1] = wi;
+    }
+    // this workgroup's slice: weighted positions u0, u1 of the (item, row)
+    // space; item q covers [wpre_q * rows, (wpre_q + w_q) * rows), each of
+    // its rows weighing w_q (the same split as group_kernel's)
+    const uint32_t n_items = __builtin_amdgcn_readlane(ci, 63), wtot = __builtin_amdgcn_readlane(wi, 63);
+    const uint32_t F = a.item_cost;
+    const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
+    const uint64_t u[2] = {udiv_small(wall * blockIdx.x, (uint32_t)a.grid),
+                           udiv_small(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
+    uint32_t qi = ci - c, wq = wi - w0 - w1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t nh = h ? n1 : n0, wh = h ? w1 : w0;
+      if (nh) {
+        const uint64_t pq = (uint64_t)wq * rows + (uint64_t)qi * F;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (u[k] >= pq && u[k] < pq + F + (uint64_t)wh * rows) s_slice[k] = boundary_in_item(u[k], pq, qi, wh, F, rows);
+        ++qi;
+        wq += wh;
+      }
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (u[k] >= wall) s_slice[k] = (uint64_t)n_items * rows;
     }
   }
   __syncthreads();
@@ -835,12 +1049,17 @@ __device__ void group_lds(const FusedArgs& a, uint32_t* keys /* LDS, 2 * n_token
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
       if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols)) atomicOr(&s_ghdr[3], 1u);
     __syncthreads();
-    if (threadIdx.x == 0) a.ws[0] = s_ghdr[2] | (s_ghdr[3] ? kErrBadDesc : 0u);
+    if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
   }
 }
 
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // requests in order of need: token ids, then the decode image (stored to LDS
+  // once the slice is known), so waiting for the ids never waits for the image
+  int32_t my_id = -1;
+  if (a.group_in_lds && (int32_t)threadIdx.x < a.n_tokens) my_id = a.ids[threadIdx.x];
+  const ImgRegs img = stage_tables_load(a.image);
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
       a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -853,11 +1072,9 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const uint4* items;
   uint64_t g0, g1;
   if (a.group_in_lds) {
-    group_lds(a, (uint32_t*)smem);
-    const uint32_t n_items = s_ghdr[0], wtot = s_ghdr[1];
-    const uint64_t wrows = (uint64_t)wtot * (uint64_t)a.rows;
-    g0 = weighted_boundary(s_items, n_items, wtot, a.rows, wrows * blockIdx.x / (uint64_t)a.grid);
-    g1 = weighted_boundary(s_items, n_items, wtot, a.rows, wrows * (blockIdx.x + 1) / (uint64_t)a.grid);
+    group_lds(a, (uint32_t*)smem, my_id);
+    g0 = s_slice[0];
+    g1 = s_slice[1];
     perm = s_perm;
     items = s_items;
   } else {
@@ -869,8 +1086,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1);
-  else run_slice<false>(a, smem, perm, items, g0, g1);
+  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, img);
+  else run_slice<false>(a, smem, perm, items, g0, g1, img);
 }
 
 // ------------------------------------------------------------ host entries
@@ -925,7 +1142,7 @@ static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
     const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
     const int64_t room = (int64_t)max_lds - static_lds - xbytes - 32;
     int64_t rmax = room / (4 * tc) - 2;
-    if (rmax > 4096) rmax = 4096;
+    if (rmax > kMaxRmax) rmax = kMaxRmax;
     if (rmax < (tc > 1 ? 256 : 64)) continue;
     p->tcmax = tc;
     p->rmax = (int)rmax;
@@ -1021,16 +1238,20 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
   a.grid = (int32_t)grid;
+  // an item change costs about as much as kItemChangeBlocks blocks of one-token
+  // rows (activation restaging, drain, epilogue); a one-token row of cols
+  // columns is about cols / 22 codewords and weighs 4
+  a.item_cost = (uint32_t)std::min<int64_t>(4ll * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
   a.group_in_lds = n_tokens <= kGroupInLds && n_experts < (1 << 24);
   hipError_t e;
   if (!a.group_in_lds) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                       plan.tcmax, rows, cols, (int32_t)grid, experts, (uint32_t*)workspace);
+                       plan.tcmax, rows, cols, (int32_t)grid, a.item_cost, experts, (uint32_t*)workspace);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }
   // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
-  const uint32_t lds = std::max<uint32_t>(plan.lds_total, 8u * kGroupInLds);
+  const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
   hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
