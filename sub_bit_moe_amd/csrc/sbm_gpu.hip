@@ -47,17 +47,13 @@ constexpr int kXPad = 48;             // columns past the row end: > 255/6, any 
 constexpr int kSmallCols = 512;       // below this a lane (<= 448 symbols) may span several rows
 // LDS: the decode tables are static arrays (compile-time addresses fold into
 // instruction offsets); accumulators and activations are dynamic LDS.
-struct __align__(256) LdsTables {
-  uint8_t pad[240];                   // puts ctabA on a 256-byte boundary
+struct __align__(16) LdsTables {
   uint32_t bases[kMaxClasses + 4];    // first codeword of each class
-  uint32_t ctabA[kMaxClasses];        // 256 B
-  uint32_t ctabB[kMaxClasses];        // 256 B, 256 B after ctabA
+  uint32_t ctab[kMaxClasses];         // class words (the kernel keeps them in a VGPR)
   uint32_t post[kPostEntries + 1];
   uint8_t cls[65536];                 // 4 * class of every codeword
 };
 // bases..cls are one contiguous copy of the image's cls_base..cls
-static_assert(offsetof(LdsTables, ctabA) % 256 == 0, "ctabA alignment");
-static_assert(offsetof(LdsTables, ctabB) == offsetof(LdsTables, ctabA) + 256, "ctabB follows ctabA");
 static_assert(offsetof(DictImage, cls) - offsetof(DictImage, cls_base) ==
               offsetof(LdsTables, cls) - offsetof(LdsTables, bases), "image and LDS layouts agree");
 static_assert(offsetof(DictImage, cls_base) % 16 == 0 && offsetof(LdsTables, bases) % 16 == 0, "16B copies");
@@ -474,7 +470,8 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
 
 // One block of SBM_BLOCK codewords, kK per lane.
 template <int TC, bool SMALL>
-__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw) {
+__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
+                              uint32_t ctab_v) {
   const int lane = threadIdx.x & 63;
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
   uint32_t c[kK], kk[kK];
@@ -483,22 +480,20 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
   // phase A: class of every codeword (LDS byte = 4 * class)
 #pragma unroll
   for (int j = 0; j < kK; ++j) kk[j] = g_tab.cls[c[j]];
-  // phase B: class tables
-  uint32_t ca[kK], cb[kK];
+  // phase B: class words, lane k of ctab_v holding class k's (a permute,
+  // which has no LDS bank conflicts)
+  uint32_t ca[kK];
 #pragma unroll
-  for (int j = 0; j < kK; ++j) {
-    ca[j] = *(const uint32_t*)((const unsigned char*)g_tab.ctabA + kk[j]);
-    cb[j] = *(const uint32_t*)((const unsigned char*)g_tab.ctabB + kk[j]);
-  }
+  for (int j = 0; j < kK; ++j) ca[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)kk[j], (int)ctab_v);
   // phase C: nonzero positions, signs, run lengths
   uint32_t slots[kK], ls[kK], sp[kK];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    const uint32_t off = c[j] - (ca[j] & 0xFFFFu);
-    const uint32_t combo = off >> ((ca[j] >> 16) & 0xFFu);
+    const uint32_t off = c[j] + (uint32_t)(((int32_t)(ca[j] << 15)) >> 15);
+    const uint32_t pidx = off >> ((ca[j] >> 17) & 3u);
     sp[j] = ((off & 7u) * 0x8102u) & 0x20202u;           // sign bit i -> +2 in byte i
-    slots[j] = *(const uint32_t*)((const unsigned char*)g_tab.post + cb[j] + 4u * combo);
+    slots[j] = g_tab.post[pidx];
     ls[j] = tot;
     tot += ca[j] >> 24;
   }
@@ -516,20 +511,37 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
     float acc[TC], snap[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) { acc[t] = 0.f; snap[t] = 0.f; }
+    // Activation gathers in batches of kXB codewords: every address of a batch
+    // is formed and its loads issued before the first sum, so up to 15 LDS
+    // reads are in flight instead of three.
+    constexpr int kXB = TC == 4 ? 4 : 8;
+    uint32_t frm = 0;                         // bit j: codeword j starts in row rl
 #pragma unroll
-    for (int j = 0; j < kK; ++j) {
-      const bool first_row = ls[j] < thr;
-      const uint32_t base = (first_row ? base0 : base1) + ls[j];
-      const uint32_t s = slots[j];
-      const uint32_t a0 = (base + (s & 0xFFu)) * TC + a.lds_x;
-      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x;
-      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x;
-      const XVal<TC> x0 = lds_x<TC>(smem, a0), x1 = lds_x<TC>(smem, a1), x2 = lds_x<TC>(smem, a2);
-      acc_x<TC>(acc, x0);
-      acc_x<TC>(acc, x1);
-      acc_x<TC>(acc, x2);
+    for (int j = 0; j < kK; ++j) frm |= (ls[j] < thr ? 1u : 0u) << j;
 #pragma unroll
-      for (int t = 0; t < TC; ++t) snap[t] = first_row ? acc[t] : snap[t];
+    for (int j0 = 0; j0 < kK; j0 += kXB) {
+      XVal<TC> xv[kXB][3];
+#pragma unroll
+      for (int jj = 0; jj < kXB; ++jj) {
+        const int j = j0 + jj;
+        const uint32_t base = (((frm >> j) & 1u) ? base0 : base1) + ls[j];
+        const uint32_t s = slots[j];
+        xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
+        xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
+        xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < kXB; ++jj) {
+        const int j = j0 + jj;
+        acc_x<TC>(acc, xv[jj][0]);
+        acc_x<TC>(acc, xv[jj][1]);
+        acc_x<TC>(acc, xv[jj][2]);
+        const bool first_row = (frm >> j) & 1u;
+#pragma unroll
+        for (int t = 0; t < TC; ++t) snap[t] = first_row ? acc[t] : snap[t];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Row sums from a wave prefix of lane sums: a lane whose span reaches the
     // next row start closes row rl with E = prefix - (part past the boundary).
@@ -691,10 +703,10 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
-                                                 const BlockCodes& raw) {
-  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw);
-  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw);
-  else process_block<4, SMALL>(a, ch, smem, raw);
+                                                 const BlockCodes& raw, uint32_t ctab_v) {
+  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, ctab_v);
+  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, ctab_v);
+  else process_block<4, SMALL>(a, ch, smem, raw, ctab_v);
 }
 
 // Chunks of the current round of a workgroup's slice (LDS) and the block
@@ -826,7 +838,7 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 
 template <bool SMALL>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
-                          uint64_t g0, uint64_t g1, const ImgRegs& img) {
+                          uint64_t g0, uint64_t g1, const ImgRegs& img, uint32_t ctab_v) {
   float* racc = (float*)(smem + a.lds_racc);
   // the image arrived while the slice was computed; storing it before any
   // block is requested keeps these stores from waiting for block loads
@@ -837,8 +849,8 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
   while (true) {
     const uint32_t nch = __builtin_amdgcn_readfirstlane(s_nchunks), nseq = __builtin_amdgcn_readfirstlane(s_nseq);
     if (nch == 0) break;
-    // prefetch ring: three blocks ahead of the block being processed
-    Slot r0 = grab(a, nseq, nch), r1 = grab(a, nseq, nch), r2 = grab(a, nseq, nch);
+    // prefetch: the next block is requested before the current one is decoded
+    Slot r0 = grab(a, nseq, nch), r1 = grab(a, nseq, nch);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
       const int tc = tc_of(ch.nt);
@@ -853,9 +865,8 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       while (r0.seq < seq_end) {
         const Slot cur = r0;
         r0 = r1;
-        r1 = r2;
-        r2 = grab(a, nseq, nch);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur.v);
+        r1 = grab(a, nseq, nch);
+        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, ctab_v);
       }
       // This wave has no more blocks of the chunk.  While the others finish,
       // request the row scales of this thread's epilogue rows and, when the
@@ -1060,6 +1071,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   int32_t my_id = -1;
   if (a.group_in_lds && (int32_t)threadIdx.x < a.n_tokens) my_id = a.ids[threadIdx.x];
   const ImgRegs img = stage_tables_load(a.image);
+  const uint32_t ctab_v = a.image->ctab[threadIdx.x & 63];   // lane k: class k's word
   if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
       a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -1086,8 +1098,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, img);
-  else run_slice<false>(a, smem, perm, items, g0, g1, img);
+  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, img, ctab_v);
+  else run_slice<false>(a, smem, perm, items, g0, g1, img, ctab_v);
 }
 
 // ------------------------------------------------------------ host entries

@@ -165,10 +165,11 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
     bool more = true;
     while (more) {
       uint32_t e = 0;
+      const uint32_t pidx = seg[n] + m;
       for (int i = 0; i < 3; ++i) {
-        // 4 = the zero element; for i >= n bit i of the in-class offset is bit
-        // (i - n) of the combo, which the sign spread adds back as 2*bit.
-        const uint32_t b = i < n ? (uint32_t)(6 * pos[i]) : 4u - 2u * ((m >> (i - n)) & 1u);
+        // 4 = the zero element; for i >= n bit i of the shifted offset is bit
+        // (i - n) of pidx, which the sign spread adds back as 2*bit.
+        const uint32_t b = i < n ? (uint32_t)(6 * pos[i]) : 4u - 2u * ((pidx >> (i - n)) & 1u);
         e |= b << (8 * i);
       }
       im->postab[seg[n] + m] = e;
@@ -202,8 +203,8 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
       cur_n = n;
       base = c;
       im->cls_base[k] = c;
-      im->ctabA[k] = (c & 0xFFFFu) | ((uint32_t)n << 16) | ((uint32_t)(6 * L) << 24);
-      im->ctabB[k] = seg[n] * 4u;
+      const int32_t K = (int32_t)(seg[n] << n) - (int32_t)c;
+      im->ctab[k] = ((uint32_t)K & 0x1FFFFu) | ((uint32_t)n << 17) | ((uint32_t)(6 * L) << 24);
       ++k;
     }
     uint32_t colex = 0;

@@ -11,7 +11,7 @@
 namespace sbm {
 
 constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
-constexpr uint32_t kImageVersion = 3;
+constexpr uint32_t kImageVersion = 4;
 constexpr int kMaxClasses = 64;
 
 // Position table segments: colex-ordered n-subsets of {0..27} for n = 0..3.
@@ -24,19 +24,21 @@ constexpr uint32_t kPostSeg3 = 407;
 constexpr uint32_t kPostEntries = 3683;
 
 // Compact decode image of a canonical dictionary (device copy read by the
-// fused kernel).  Codeword c of class k (cls_base[k] <= c < cls_base[k+1]):
-//   off   = c - base(k)
-//   combo = off >> n(k)                 (colex rank of the nonzero positions)
+// fused kernel).  Codeword c of class k (cls_base[k] <= c < cls_base[k+1],
+// n(k) nonzeros, length L(k)):
+//   off   = c + K(k),  K(k) = seg(n) * 2^n - cls_base[k]
+//   pidx  = off >> n                    (seg(n) + colex rank of the positions)
 //   sg    = off & 7                     (bit i < n set: nonzero i is positive)
-//   slots = postab[seg(n) + combo] + spread(sg)
-// where spread puts 2*bit i of sg into byte i.  Byte i of a slot word is the
-// byte offset 6*p_i + 2*positive of nonzero i in the [-x, +x, 0] triple
-// layout, or 4 (the zero) when i >= n.  For i >= n, bit i of off belongs to
-// combo, so those postab bytes are stored as 4 - 2*bit_i(off), which the
-// spread brings back to 4.
-// ctabA[k] = base | n << 16 | (6*L) << 24
-// ctabB[k] = 4*seg(n)   (byte offset of the class's postab segment)
-// cls[c]   = 4*k        (byte offset of codeword c's class-table entries)
+//   slots = postab[pidx] + spread(sg)
+// Adding a multiple of 2^n keeps the sign bits of the in-class offset and
+// moves the colex rank into the class's position-table segment.  spread puts
+// 2*bit i of sg into byte i.  Byte i of a slot word is the byte offset
+// 6*p_i + 2*positive of nonzero i in the [-x, +x, 0] triple layout, or 4 (the
+// zero) when i >= n.  For i >= n, bit i of off is bit i - n of pidx, so those
+// postab bytes are stored as 4 - 2*bit_{i-n}(pidx), which the spread brings
+// back to 4.
+// ctab[k] = (K(k) & 0x1FFFF) | n << 17 | (6*L) << 24   (K: 17-bit two's complement)
+// cls[c]  = 4*k                                          (byte offset of ctab[k])
 struct DictImage {
   uint32_t magic;
   uint32_t version;
@@ -45,8 +47,7 @@ struct DictImage {
   uint64_t checksum;
   uint64_t reserved1;
   uint32_t cls_base[kMaxClasses + 4];
-  uint32_t ctabA[kMaxClasses];
-  uint32_t ctabB[kMaxClasses];
+  uint32_t ctab[kMaxClasses];
   uint32_t postab[kPostEntries + 1];
   uint8_t cls[SBM_DICT_ENTRIES];    // 4 * class of every codeword
 };

@@ -119,12 +119,12 @@ def _image_fields(img):
     off = 32
     cls_base = np.frombuffer(img[off:off + 68 * 4].tobytes(), np.uint32)
     off += 68 * 4
-    A = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
-    off += 64 * 4
-    B = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
+    ctab = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
     off += 64 * 4
     post = np.frombuffer(img[off:off + 3684 * 4].tobytes(), np.uint32)
-    return n_classes, cls_base, A, B, post
+    off += 3684 * 4
+    cls = np.frombuffer(img[off:off + 65536].tobytes(), np.uint8)
+    return n_classes, cls_base, ctab, post, cls
 
 
 def test_decode_image_reproduces_every_codeword(odict):
@@ -132,18 +132,20 @@ def test_decode_image_reproduces_every_codeword(odict):
     CPU and compare run length, nonzero positions and signs with the oracle."""
     img = api.dict_image(odict["words"])
     assert img.size == N.lib().sbm_dict_image_bytes()
-    n_classes, cls_base, A, B, post = _image_fields(img)
+    n_classes, cls_base, ctab, post, cls = _image_fields(img)
     assert n_classes == 54
-    cls = np.zeros(65536, np.int64)
-    for k in range(n_classes):
-        cls[cls_base[k]:cls_base[k + 1]] = k
+    k = np.zeros(65536, np.int64)
+    for j in range(n_classes):
+        k[cls_base[j]:cls_base[j + 1]] = j
+    assert np.array_equal(cls.astype(np.int64), 4 * k)
     c = np.arange(65536, dtype=np.int64)
-    a = A[cls].astype(np.int64)
-    b = B[cls].astype(np.int64)
-    off = c - (a & 0xFFFF)
-    combo = off >> ((a >> 16) & 0xFF)
+    a = ctab[k].astype(np.int64)
+    K = (a & 0x1FFFF) - ((a & 0x10000) << 1)          # 17-bit two's complement
+    off = c + K
+    assert off.min() >= 0
+    pidx = off >> ((a >> 17) & 3)
     sg = off & 7
-    e = post[(b // 4) + combo].astype(np.int64)
+    e = post[pidx].astype(np.int64)
     slots = e + ((sg * 0x8102) & 0x20202)
     L = ((a >> 24) & 0xFF) // 6
     assert np.array_equal(L, odict["lens"])
@@ -154,8 +156,8 @@ def test_decode_image_reproduces_every_codeword(odict):
             byte = (int(slots[cw]) >> (8 * i)) & 0xFF
             if byte == 4:
                 continue                       # zero slot
-            pos, k = divmod(byte, 6)
-            exp[pos] = 1 if k == 0 else 2      # triple layout [-x, +x, 0]
+            pos, kk = divmod(byte, 6)
+            exp[pos] = 1 if kk == 0 else 2     # triple layout [-x, +x, 0]
         assert np.array_equal(exp, sym28[cw]), cw
 
 
