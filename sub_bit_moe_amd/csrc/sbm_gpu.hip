@@ -508,6 +508,7 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
     const uint32_t colB = pl - rl * a.colsB;
     const uint32_t thr = a.colsB - colB;
     const uint32_t base0 = colB, base1 = colB - a.colsB;   // row rl / row rl+1 (wraps mod 2^32)
+    const uint32_t base0x = base0 + a.lds_x, base1x = base1 + a.lds_x;
     float acc[TC], snap[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) { acc[t] = 0.f; snap[t] = 0.f; }
@@ -524,11 +525,19 @@ __device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char
 #pragma unroll
       for (int jj = 0; jj < kXB; ++jj) {
         const int j = j0 + jj;
-        const uint32_t base = (((frm >> j) & 1u) ? base0 : base1) + ls[j];
         const uint32_t s = slots[j];
-        xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
-        xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
-        xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
+        if constexpr (TC == 1) {
+          // one add per slot: the byte operand is taken straight from s
+          const uint32_t bx = (((frm >> j) & 1u) ? base0x : base1x) + ls[j];
+          xv[jj][0] = lds_x<TC>(smem, bx + (s & 0xFFu));
+          xv[jj][1] = lds_x<TC>(smem, bx + ((s >> 8) & 0xFFu));
+          xv[jj][2] = lds_x<TC>(smem, bx + ((s >> 16) & 0xFFu));
+        } else {
+          const uint32_t base = (((frm >> j) & 1u) ? base0 : base1) + ls[j];
+          xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
+          xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
+          xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
