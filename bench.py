@@ -6,7 +6,9 @@ and a down projection (2080 x 6144) of ternary weights with P(0) = 0.886 and
 per-row fp16 scales, generated and encoded on the GPU from seed 41 (~147 GB of
 compressed artefact, ~1.57 T parameters).  One step = one pass of 64 fp16
 N(0,1) tokens through all 30 layers (top-1 Zipf(1.1) routing per layer:
-up + ReLU, down, RMS glue), captured once in a HIP graph and replayed.
+up + ReLU, down; the RMS glue between layers runs inside the next up
+projection, and once after the last layer), captured once in a HIP graph
+and replayed.
 
 Metric: compressed bytes (codewords + block starts + row scales of every
 touched (expert, matrix)) read per second.  Also reported: bf16-equivalent
@@ -165,17 +167,18 @@ def main():
     for l in range(cfg.n_layers):
         ids = st.routes[l]
         touched = st.touched(l)
-        for which, stk, inp, out, relu, ws in (("up", st.up[l], x, run.h, True, run.ws_up),
-                                                ("down", st.down[l], run.h, run.y, False, run.ws_down)):
+        for which, stk, inp, out, relu, ws, rms in (("up", st.up[l], x, run.h, True, run.ws_up, l > 0),
+                                                     ("down", st.down[l], run.h, run.y, False, run.ws_down, False)):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            S.api.moe_fused_decode_matvec(stk, st.image, inp, ids, relu=relu, workspace=ws, y=out, stream=stream)
+            S.api.moe_fused_decode_matvec(stk, st.image, inp, ids, relu=relu, workspace=ws, y=out, stream=stream,
+                                          in_rms=rms)
             b.record(stream)
             b.synchronize()
             durs.append(a.elapsed_time(b))
             byts.append(sum(stk.matrix_bytes(int(e)) for e in touched))
-        x = S.api.rms_glue(run.y, out=run.x[l % 2])
+        x = run.y
     torch.cuda.synchronize()
     achieved = sum(byts) / (sum(durs) * 1e-3) / 1e9
     traffic, traffic_src = measured_traffic()

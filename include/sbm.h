@@ -71,6 +71,8 @@ typedef enum {
 /* Flags of sbm_moe_fused_decode_matvec. */
 #define SBM_F_RELU    1u  /* y = max(y, 0) after scaling (Switch experts are ReLU FFNs) */
 #define SBM_F_OUT_F32 2u  /* y is float32 (default fp16) */
+#define SBM_F_IN_RMS  4u  /* each x row is first scaled to unit RMS as sbm_rms_glue does (fp32
+                             sum of squares, rounded to fp16); lets stacked layers skip that launch */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);

@@ -470,7 +470,7 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
 
 // One block of SBM_BLOCK codewords, kK per lane.
 template <int TC, bool SMALL>
-__device__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
+__device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
                               uint32_t ctab_v) {
   const int lane = threadIdx.x & 63;
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
@@ -633,34 +633,61 @@ __device__ __forceinline__ bool x_vec(const FusedArgs& a) {
   return (a.cols % 8) == 0 && ((uintptr_t)a.x & 15u) == 0;
 }
 
+// fp16 pairs of 8 columns of TC token rows (zero past cols or for tok < 0).
 template <int TC>
-__device__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
-                        uint32_t nt) {
-  int32_t tok[TC];
+__device__ __forceinline__ void load_x_group(const FusedArgs& a, const int32_t (&tok)[TC], int32_t c0, bool vec,
+                                             uint32_t (&p)[TC][4]) {
 #pragma unroll
-  for (int t = 0; t < TC; ++t) tok[t] = (uint32_t)t < nt ? perm[tb + t] : -1;
-  const int32_t n8 = a.xcols / 8;
-  const bool vec = x_vec(a);
-  for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
-    const int32_t c0 = 8 * i;
-    uint32_t p[TC][4];                       // [token][column pair] fp16x2
+  for (int t = 0; t < TC; ++t) {
+    if (tok[t] >= 0 && c0 + 8 <= a.cols && vec) {
+      const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + c0);
+      p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
+    } else {
 #pragma unroll
-    for (int t = 0; t < TC; ++t) {
-      if (tok[t] >= 0 && c0 + 8 <= a.cols && vec) {
-        const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + c0);
-        p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          uint32_t lo = 0, hi = 0;
-          if (tok[t] >= 0 && c0 + 2 * m < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m];
-          if (tok[t] >= 0 && c0 + 2 * m + 1 < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m + 1];
-          p[t][m] = lo | (hi << 16);
-        }
+      for (int m = 0; m < 4; ++m) {
+        uint32_t lo = 0, hi = 0;
+        if (tok[t] >= 0 && c0 + 2 * m < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m];
+        if (tok[t] >= 0 && c0 + 2 * m + 1 < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m + 1];
+        p[t][m] = lo | (hi << 16);
       }
     }
-    store_x_group<TC>(a, smem, c0, p);
   }
+}
+
+// SBM_F_IN_RMS: per-token sums of squares -> 1 / rms over the workgroup
+// (wave scans, then the 8 wave totals in a fixed order; a zero row keeps scale 1).
+__shared__ float s_ssq[kFWaves][4];
+
+__device__ __forceinline__ float h2_ssq(uint32_t w) {
+  const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  return lo * lo + hi * hi;
+}
+
+__device__ __forceinline__ uint32_t h2_scale(uint32_t w, float s) {
+  const _Float16 lo = (_Float16)((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)) * s);
+  const _Float16 hi = (_Float16)((float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) * s);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+template <int TC>
+__device__ __forceinline__ void wg_inv_rms(const FusedArgs& a, const float (&ss)[TC], float (&inv)[TC]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < TC; ++t) {
+    const float S = wave_incl_scan_f(ss[t]);
+    if (lane == 63) s_ssq[wave][t] = S;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TC; ++t) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFWaves; ++w) tot += s_ssq[w][t];
+    const float ms = tot / (float)a.cols;
+    inv[t] = ms > 0.f ? 1.0f / sqrtf(ms) : 1.0f;
+  }
+  __syncthreads();
 }
 
 // Activations of the next item, requested before the drain barrier of the
@@ -693,6 +720,24 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
 template <int TC>
 __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* smem, const XPre& r) {
   const int32_t n8 = a.xcols / 8;
+  float inv[TC];
+  const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
+  if (rms) {
+    float ss[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4 / TC; ++j) {
+      if ((int32_t)threadIdx.x + j * kFThreads < n8) {
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+          const uint4 v = r.v[j * TC + t];
+          ss[t] += h2_ssq(v.x) + h2_ssq(v.y) + h2_ssq(v.z) + h2_ssq(v.w);
+        }
+      }
+    }
+    wg_inv_rms<TC>(a, ss, inv);
+  }
 #pragma unroll
   for (int j = 0; j < 4 / TC; ++j) {
     const int32_t i = (int32_t)threadIdx.x + j * kFThreads;
@@ -702,9 +747,57 @@ __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* sm
       for (int t = 0; t < TC; ++t) {
         const uint4 v = r.v[j * TC + t];
         p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
+        if (rms) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) p[t][m] = h2_scale(p[t][m], inv[t]);
+        }
       }
       store_x_group<TC>(a, smem, 8 * i, p);
     }
+  }
+}
+
+template <int TC>
+__device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
+                        uint32_t nt) {
+  if (x_prefetchable(a, TC)) {
+    // one round trip: the rows stay in registers for the RMS scale
+    XPre r;
+    xpre_load<TC>(a, perm, tb, nt, r);
+    xpre_store<TC>(a, smem, r);
+    return;
+  }
+  int32_t tok[TC];
+#pragma unroll
+  for (int t = 0; t < TC; ++t) tok[t] = (uint32_t)t < nt ? perm[tb + t] : -1;
+  const int32_t n8 = a.xcols / 8;
+  const bool vec = x_vec(a);
+  const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
+  float inv[TC];
+  if (rms) {
+    float ss[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) ss[t] = 0.f;
+    for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
+      uint32_t p[TC][4];
+      load_x_group<TC>(a, tok, 8 * i, vec, p);
+#pragma unroll
+      for (int t = 0; t < TC; ++t)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ss[t] += h2_ssq(p[t][m]);
+    }
+    wg_inv_rms<TC>(a, ss, inv);
+  }
+  for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
+    uint32_t p[TC][4];
+    load_x_group<TC>(a, tok, 8 * i, vec, p);
+    if (rms) {
+#pragma unroll
+      for (int t = 0; t < TC; ++t)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) p[t][m] = h2_scale(p[t][m], inv[t]);
+    }
+    store_x_group<TC>(a, smem, 8 * i, p);
   }
 }
 
@@ -1075,30 +1168,35 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
 
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // requests in order of need: token ids, then the decode image (stored to LDS
-  // once the slice is known), so waiting for the ids never waits for the image
-  int32_t my_id = -1;
-  if (a.group_in_lds && (int32_t)threadIdx.x < a.n_tokens) my_id = a.ids[threadIdx.x];
+  // Requests in order of need: token ids (every thread, no branch, so the
+  // request goes out with the first argument loads), the image header in one
+  // scalar load, then the decode image (stored to LDS once the slice is
+  // known), so waiting for the ids never waits for the image.
+  const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
+  const int32_t my_id = a.ids[tq];
+  const uint4 hdr = *(const uint4*)a.image;       // magic, version, n_classes
   const ImgRegs img = stage_tables_load(a.image);
   const uint32_t ctab_v = a.image->ctab[threadIdx.x & 63];   // lane k: class k's word
-  if (a.image->magic != kImageMagic || a.image->version != kImageVersion ||
-      a.image->n_classes == 0 || a.image->n_classes > (uint32_t)kMaxClasses) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      if (a.group_in_lds) a.ws[0] = kErrBadImage;
-      else atomicOr(&a.ws[0], kErrBadImage);
-    }
-    return;
-  }
+  const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z != 0 &&
+                        hdr.z <= (uint32_t)kMaxClasses;
   const int32_t* perm;
   const uint4* items;
   uint64_t g0, g1;
   if (a.group_in_lds) {
-    group_lds(a, (uint32_t*)smem, my_id);
+    group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
+    if (!image_ok) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = kErrBadImage;   // after the grouping's write
+      return;
+    }
     g0 = s_slice[0];
     g1 = s_slice[1];
     perm = s_perm;
     items = s_items;
   } else {
+    if (!image_ok) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ws[0], kErrBadImage);
+      return;
+    }
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
     g0 = bounds[blockIdx.x];
@@ -1214,7 +1312,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
-  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
   if (n_tokens == 0) return SBM_OK;
   if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
       !workspace)

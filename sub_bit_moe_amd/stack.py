@@ -11,7 +11,8 @@ A pass sends T tokens through all layers: per layer each token's top-1 expert
 (Zipf popularity, the cache-amplification page's routing statistics) applies
 up + ReLU + down through the fused decode + matvec; between layers the token
 is RMS-normalised (benchmark glue standing in for the absent transformer
-block).  Every step runs in libsbm's HIP kernels.
+block), inside the next up projection's activation staging, and once more
+after the last layer.  Every step runs in libsbm's HIP kernels.
 """
 from __future__ import annotations
 
@@ -112,16 +113,19 @@ class Runner:
 
     def run(self, keep=None):
         """One pass over all layers.  keep: optional dict filled with the
-        per-layer (input, h, y) device tensors for checking."""
+        per-layer (input, h, y) device tensors for checking; from layer 1 on
+        the input is the previous y, which the up projection scales to unit
+        RMS itself (the glue fused into its activation staging)."""
         st = self.st
         x = st.x0
         for l in range(st.cfg.n_layers):
             ids = st.routes[l]
-            api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h)
+            api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h,
+                                        in_rms=l > 0)
+            if keep is not None:
+                keep[l] = (x.clone(), self.h.clone())
             api.moe_fused_decode_matvec(st.down[l], st.image, self.h, ids, workspace=self.ws_down, y=self.y)
             if keep is not None:
-                keep[l] = (x.clone(), self.h.clone(), self.y.clone())
-            nxt = self.x[l % 2]
-            api.rms_glue(self.y, out=nxt)
-            x = nxt
-        return x
+                keep[l] = keep[l] + (self.y.clone(),)
+            x = self.y
+        return api.rms_glue(self.y, out=self.x[0])

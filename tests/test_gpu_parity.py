@@ -85,6 +85,34 @@ def test_fused_single_expert(dev, lib_state, odict, rows, cols, p0, T):
             P.assert_close(y, ref, 2e-6, 2e-5, what="fp32 output")
 
 
+@pytest.mark.parametrize("rows,cols,T", [(300, 2080, 3), (130, 6144, 2), (64, 98, 5), (40, 512, 9)])
+def test_fused_input_rms(dev, lib_state, odict, rows, cols, T):
+    """SBM_F_IN_RMS: each token row is first scaled to unit RMS (the stack
+    glue), including a zero row, which stays zero."""
+    from oracle import matvec as OM
+    api = lib_state["api"]
+    E = 3
+    ex = P.host_experts(E, rows, cols, 0.886, rows + 7)
+    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev)
+    rng = np.random.default_rng(cols)
+    x = (rng.standard_normal((T, cols)) * rng.uniform(0.01, 40, (T, 1))).astype(np.float16)
+    x[1] = 0
+    ids = (np.arange(T) % E).astype(np.int32)
+    ws = api.alloc_workspace(E, T, dev)
+    y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
+                                    torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, in_rms=True)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 0
+    yn = y.cpu().numpy().astype(np.float64)
+    xn = OM.rms_glue(x)
+    for t in range(T):
+        ref = P.oracle_matvec_from_symbols(*ex[ids[t]], xn[t:t + 1])[0]
+        if t == 1:
+            assert not np.any(yn[t])
+        else:
+            P.assert_close(yn[t], ref, what=f"in_rms token {t}")
+
+
 def test_fused_exact_special_inputs(dev, lib_state, odict):
     rows, cols = 257, 2080
     sym, sc = P.host_experts(1, rows, cols, 0.886, 77)[0]

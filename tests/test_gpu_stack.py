@@ -72,11 +72,14 @@ def test_small_stack_pass_against_oracle(dev, odict):
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     for l in range(cfg.n_layers):
-        xin, h, y = (t.float().cpu().numpy() for t in keep[l])
+        xraw, h, y = (t.float().cpu().numpy() for t in keep[l])
         ids = st.routes_host[l]
         if l > 0:
             prev_y = keep[l - 1][2].float().cpu().numpy()
-            P.assert_close(xin, OM.rms_glue(prev_y).astype(np.float64), 2e-3, 2e-3, what=f"glue {l}")
+            assert np.array_equal(xraw, prev_y)
+            xin = OM.rms_glue(prev_y).astype(np.float64)     # applied inside the up projection
+        else:
+            xin = xraw
         for t in rng.choice(cfg.n_tokens, 6, replace=False):
             e = int(ids[t])
             for mat, inp, out, relu in ((0, xin[t], h[t], True), (1, h[t], y[t], False)):
