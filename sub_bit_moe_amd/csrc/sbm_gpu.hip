@@ -329,32 +329,24 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
 }
 
 // ------------------------------------------------------------ fused kernel
-// Copy of the decode image into LDS: loads issued at kernel entry, stores
-// after the first blocks have been requested.
-constexpr int kImgPer = (kImageCopyU4 + kFThreads - 1) / kFThreads;
-struct ImgRegs {
-  uint4 v[kImgPer];
-};
+// Copy of the decode image into LDS with direct-to-LDS loads issued at kernel
+// entry: each wave moves 1 KB per instruction (lane l's 16 bytes land at the
+// wave's LDS base + 16 l), so the copy holds no registers and completes while
+// the tokens are grouped.  Readers wait for vmcnt(0) and a barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ ImgRegs stage_tables_load(const DictImage* __restrict__ im) {
+__device__ __forceinline__ void stage_tables_dma(const DictImage* __restrict__ im) {
   const uint4* src = (const uint4*)im->cls_base;
-  ImgRegs r;
-#pragma unroll
-  for (int j = 0; j < kImgPer; ++j) {
-    const uint32_t i = threadIdx.x + j * kFThreads;
-    r.v[j] = i < kImageCopyU4 ? src[i] : make_uint4(0, 0, 0, 0);
+  uint4* dst = (uint4*)g_tab.bases;
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (uint32_t q = wave; q * 64 < kImageCopyU4; q += kFWaves) {
+    const uint32_t i = q * 64 + lane;
+    if (i < kImageCopyU4)
+      __builtin_amdgcn_global_load_lds((const void*)(src + i), (lds_void_t*)(dst + q * 64), 16, 0, 0);
   }
-  return r;
 }
 
-__device__ __forceinline__ void stage_tables(const ImgRegs& r) {
-  uint4* dst = (uint4*)g_tab.bases;
-#pragma unroll
-  for (int j = 0; j < kImgPer; ++j) {
-    const uint32_t i = threadIdx.x + j * kFThreads;
-    if (i < kImageCopyU4) dst[i] = r.v[j];
-  }
-}
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // acc += (float)x  with x the low / high fp16 half of v: one fp32 rounding.
 __device__ __forceinline__ float acc_lo(float acc, uint32_t v) {
@@ -866,7 +858,7 @@ __device__ __forceinline__ void build_chunks(const FusedArgs& a, const uint4* it
     }
     if (lane == 0) {
       s_nchunks = nch;
-      s_next_seq = 0;
+      s_next_seq = 2 * kFWaves;     // blocks 0 .. 2*waves-1 are the waves' first two
       if (nch == 0) {
         s_nseq = 0;
         s_gnext = g1;
@@ -911,10 +903,16 @@ struct Slot {
   uint32_t seq;         // 0xFFFFFFFF when empty
 };
 
-__device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t nch) {
+// first >= 0: take that block sequence number (the waves' first two blocks of
+// a round are fixed); otherwise draw the next one from the counter.
+__device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t nch, int32_t first = -1) {
   uint32_t q = 0;
-  if ((threadIdx.x & 63) == 0) q = atomicAdd(&s_next_seq, 1u);
-  q = __builtin_amdgcn_readfirstlane(q);
+  if (first >= 0) {
+    q = (uint32_t)first;
+  } else {
+    if ((threadIdx.x & 63) == 0) q = atomicAdd(&s_next_seq, 1u);
+    q = __builtin_amdgcn_readfirstlane(q);
+  }
   Slot sl;
   sl.seq = 0xFFFFFFFFu;
   sl.v.a = make_uint4(0, 0, 0, 0);
@@ -940,19 +938,23 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 
 template <bool SMALL>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
-                          uint64_t g0, uint64_t g1, const ImgRegs& img, uint32_t ctab_v) {
+                          uint64_t g0, uint64_t g1, uint32_t ctab_v) {
   float* racc = (float*)(smem + a.lds_racc);
-  // the image arrived while the slice was computed; storing it before any
-  // block is requested keeps these stores from waiting for block loads
-  stage_tables(img);
-  for (int32_t i = threadIdx.x; i < a.tcmax * (a.rmax + 2); i += kFThreads) racc[i] = 0.f;
+  // the image copy was issued at kernel entry; this wave's part has landed
+  // once its vector memory count drains, every wave's after build_chunks' barrier
+  wait_vmem_all();
+  {
+    const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;   // lds_racc region is 16B-aligned
+    for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
+  }
   build_chunks(a, items, g0, g1);
   uint32_t cur_q = 0xFFFFFFFFu;
   while (true) {
     const uint32_t nch = __builtin_amdgcn_readfirstlane(s_nchunks), nseq = __builtin_amdgcn_readfirstlane(s_nseq);
     if (nch == 0) break;
     // prefetch: the next block is requested before the current one is decoded
-    Slot r0 = grab(a, nseq, nch), r1 = grab(a, nseq, nch);
+    const int32_t wave = (int32_t)(threadIdx.x >> 6);
+    Slot r0 = grab(a, nseq, nch, wave), r1 = grab(a, nseq, nch, wave + kFWaves);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
       const int tc = tc_of(ch.nt);
@@ -1175,7 +1177,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
   const int32_t my_id = a.ids[tq];
   const uint4 hdr = *(const uint4*)a.image;       // magic, version, n_classes
-  const ImgRegs img = stage_tables_load(a.image);
+  stage_tables_dma(a.image);
   const uint32_t ctab_v = a.image->ctab[threadIdx.x & 63];   // lane k: class k's word
   const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z != 0 &&
                         hdr.z <= (uint32_t)kMaxClasses;
@@ -1205,8 +1207,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, img, ctab_v);
-  else run_slice<false>(a, smem, perm, items, g0, g1, img, ctab_v);
+  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, ctab_v);
+  else run_slice<false>(a, smem, perm, items, g0, g1, ctab_v);
 }
 
 // ------------------------------------------------------------ host entries
