@@ -112,10 +112,16 @@ class Runner:
         self.x = [torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev) for _ in range(2)]
 
     def run(self, keep=None):
-        """One pass over all layers.  keep: optional dict filled with the
-        per-layer (input, h, y) device tensors for checking; from layer 1 on
-        the input is the previous y, which the up projection scales to unit
-        RMS itself (the glue fused into its activation staging)."""
+        """One pass over all layers, then the glue on the last output.  keep:
+        optional dict filled with the per-layer (input, h, y) device tensors
+        for checking; from layer 1 on the input is the previous y, which the up
+        projection scales to unit RMS itself (the glue fused into its
+        activation staging)."""
+        self.run_layers(keep)
+        return api.rms_glue(self.y, out=self.x[0])
+
+    def run_layers(self, keep=None):
+        """The fused launches of one pass (2 per layer), nothing else."""
         st = self.st
         x = st.x0
         for l in range(st.cfg.n_layers):
@@ -128,4 +134,4 @@ class Runner:
             if keep is not None:
                 keep[l] = keep[l] + (self.y.clone(),)
             x = self.y
-        return api.rms_glue(self.y, out=self.x[0])
+        return self.y
