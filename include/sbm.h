@@ -73,6 +73,10 @@ typedef enum {
 #define SBM_F_OUT_F32 2u  /* y is float32 (default fp16) */
 #define SBM_F_IN_RMS  4u  /* each x row is first scaled to unit RMS as sbm_rms_glue does (fp32
                              sum of squares, rounded to fp16); lets stacked layers skip that launch */
+#define SBM_F_MFMA    8u  /* experts with 16 or more tokens take the dense-tile path: row tiles
+                             decoded to a ternary tile in LDS, multiplied on the matrix cores
+                             (v_mfma_f32_16x16x32_f16, fp32 accumulation).  Off by default: on
+                             gfx950 it is slower than the sparse path up to 64 tokens per expert */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);

@@ -171,9 +171,11 @@ def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
 
 
 def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
-                            out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False):
+                            out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False,
+                            mfma: bool = False):
     """y[t] = act(s * W_{expert_ids[t]} x[t]) for one projection of an MoE layer
-    (in_rms: x[t] is first scaled to unit RMS, as rms_glue does)."""
+    (in_rms: x[t] is first scaled to unit RMS, as rms_glue does; mfma=False
+    sends experts with 16 or more tokens to the dense-tile MFMA path)."""
     import torch
     T = int(x.shape[0]) if x is not None else 0
     if y is None:
@@ -182,6 +184,7 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
     if workspace is None:
         workspace = alloc_workspace(stack.n_experts, T, device=stack.codes.device)
     flags = (N.SBM_F_RELU if relu else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0) | (N.SBM_F_IN_RMS if in_rms else 0)
+    flags |= N.SBM_F_MFMA if mfma else 0
     check(lib().sbm_moe_fused_decode_matvec(
         _ptr(stack.codes), _ptr(stack.row_off), _ptr(stack.bstart), _ptr(stack.scales), _ptr(stack.desc),
         stack.n_experts, stack.rows, stack.cols, _ptr(image_t), _ptr(x), _ptr(expert_ids), T, _ptr(y),

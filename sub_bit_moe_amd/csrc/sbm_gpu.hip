@@ -67,6 +67,12 @@ __shared__ LdsTables g_tab;
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
 constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
 constexpr int kItemChangeBlocks = 12;
+// Heavy experts (at least kMfmaMinTokens tokens) take the dense-tile MFMA path:
+// items of up to kMfmaMaxTokens tokens, flagged in the item's token-count word.
+constexpr uint32_t kItemMfma = 0x80000000u;
+constexpr int kMfmaMinTokens = 16;
+constexpr int kMfmaMaxTokens = 64;
+constexpr uint32_t kMfmaWeight = 24;    // slice weight of one row of an MFMA item (measured, 1-token row = 4)
 constexpr int kMaxRmax = 4096;    // rows per chunk
 constexpr int kEpiRegs = (kMaxRmax + 2 + kFThreads - 1) / kFThreads;   // epilogue slots per thread
 constexpr int kGroupInLds = 128;  // up to this many tokens are grouped inside the fused kernel
@@ -110,6 +116,7 @@ struct FusedArgs {
   int32_t xcols;        // staged columns per token (cols + pad)
   uint32_t lds_racc;    // byte offsets in LDS
   uint32_t lds_x;
+  int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
 };
 
 // ------------------------------------------------------------ wave helpers
@@ -223,6 +230,7 @@ __device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, 
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
 __host__ __device__ inline uint32_t item_weight(uint32_t nt) {
+  if (nt & kItemMfma) return kMfmaWeight;
   return nt <= 1 ? 4u : (nt <= 2 ? 5u : 6u);
 }
 
@@ -249,7 +257,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
 
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
                                                          int32_t E, int32_t tcmax, int32_t rows, int32_t cols,
-                                                         int32_t grid, uint32_t item_cost,
+                                                         int32_t grid, uint32_t item_cost, int32_t mfma,
                                                          const sbm_matrix_desc* __restrict__ experts,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
@@ -273,7 +281,8 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   for (int base = 0; base < E; base += kThreads) {
     const int e = base + threadIdx.x;
     const uint32_t c = e < E ? cnt[e] : 0u;
-    const uint32_t nch = (c + tcmax - 1) / tcmax;
+    const uint32_t span = (mfma && c >= (uint32_t)kMfmaMinTokens) ? (uint32_t)kMfmaMaxTokens : (uint32_t)tcmax;
+    const uint32_t nch = (c + span - 1) / span;
     uint32_t tot_c, tot_n;
     const uint32_t ex_c = block_excl_scan(c, sh_tot, &tot_c);
     const uint32_t ex_n = block_excl_scan(nch, sh_tot, &tot_n);
@@ -301,8 +310,10 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const uint32_t s0 = start[e], n = start[e + 1] - s0;
     uint32_t q = chunk[e];
-    for (uint32_t k = 0; k < n; k += (uint32_t)tcmax, ++q) {
-      const uint32_t nt = (n - k) < (uint32_t)tcmax ? (n - k) : (uint32_t)tcmax;
+    const bool heavy = mfma && n >= (uint32_t)kMfmaMinTokens;
+    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)tcmax;
+    for (uint32_t k = 0; k < n; k += span, ++q) {
+      const uint32_t nt = ((n - k) < span ? (n - k) : span) | (heavy ? kItemMfma : 0u);
       items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt));
     }
     if (n && !desc_ok(experts[e], rows, cols)) atomicOr(&hdr[0], kErrBadDesc);
@@ -399,14 +410,15 @@ struct BlockCodes {
 
 // Everything a workgroup needs about one chunk: rows [ra, rb) of item q.
 struct Chunk {
-  uint32_t q, tb, nt;
+  uint32_t q, tb, nt;     // nt: token count (without the MFMA flag)
   int32_t ra, rb;
   uint32_t b0, b1;        // block range (inclusive); b0 > b1 when empty
   uint64_t code_base;
   uint32_t n_codes;
-  uint64_t blk_base, scale_base;
+  uint64_t blk_base, scale_base, off_base;
   uint32_t seq0;          // first block sequence number of the chunk in its round
   bool ok;
+  bool mfma;              // dense-tile MFMA item: no blocks in the round's sequence
 };
 
 // Rows [ra, rb) of item q.
@@ -418,16 +430,18 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   ch.rb = rb;
   const uint4 it = items[ch.q];
   ch.tb = it.y;
-  ch.nt = it.z;
+  ch.nt = it.z & ~kItemMfma;
+  ch.mfma = (it.z & kItemMfma) != 0;
   const sbm_matrix_desc d = a.experts[it.x];
   ch.ok = desc_ok(d, a.rows, a.cols);
   ch.code_base = d.code_base;
   ch.n_codes = d.n_codes;
   ch.blk_base = d.blk_base;
   ch.scale_base = d.scale_base;
+  ch.off_base = d.off_base;
   ch.b0 = 1;
   ch.b1 = 0;
-  if (ch.ok) {
+  if (ch.ok && !ch.mfma) {
     const uint32_t c0 = a.row_off[d.off_base + ch.ra], c1 = a.row_off[d.off_base + ch.rb];
     if (c1 > c0 && c1 <= d.n_codes) {
       ch.b0 = c0 / SBM_BLOCK;
@@ -803,6 +817,235 @@ __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, con
   else process_block<4, SMALL>(a, ch, smem, raw, ctab_v);
 }
 
+// ------------------------------------------------------------ dense-tile MFMA path
+// Heavy experts ([QMoE] "The GPU Decoding Kernel" decodes each weight once;
+// with many tokens per expert the multiply is a dense contraction): rows
+// [ra, rb) of the item are taken R = mfma_rows at a time.  The tile's
+// codewords (row_off[r0] .. row_off[r0 + R]) are decoded by the whole
+// workgroup, 16 per thread, with a workgroup prefix of run lengths from the
+// position r0 * cols; every nonzero sets a 2-bit code (1: -1, 2: +1) in an LDS
+// tile of 16 codes per dword.  Then v_mfma_f32_16x16x32_f16 multiplies 16-row
+// tiles of it, expanded to fp16 through a 256-entry table, with 32-column
+// slices of the tokens' activations read from global memory; waves split rows
+// and K, and partial products meet in fp32 LDS accumulators.  The epilogue is
+// the sparse path's.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+struct MfmaLds {
+  uint32_t w, lut, acc, scan, rms, total;   // byte offsets in dynamic LDS, total bytes
+};
+__host__ __device__ inline MfmaLds mfma_lds(int32_t R, int32_t cols) {
+  MfmaLds m;
+  const uint32_t wpr = ((uint32_t)cols + 15u) / 16u;
+  m.w = 0;
+  m.lut = (4u * (uint32_t)R * wpr + 15u) & ~15u;
+  m.acc = m.lut + 256u * 8u;
+  m.scan = m.acc + 4u * (uint32_t)R * kMfmaMaxTokens;
+  m.rms = m.scan + 4u * (kFWaves + 1);
+  m.total = m.rms + 4u * kMfmaMaxTokens;
+  return m;
+}
+
+__device__ __forceinline__ uint32_t div6_exact(uint32_t x) {   // x a multiple of 6
+  return (uint32_t)(((uint64_t)x * 0xAAAAAAABull) >> 34);
+}
+
+// B fragment of v_mfma_f32_16x16x32_f16: 8 consecutive K of one token
+// (with SBM_F_IN_RMS each value is first scaled by the token's 1 / rms and
+// rounded to fp16, as the sparse path stages it).
+template <bool VEC>
+__device__ __forceinline__ half8_t mfma_b_frag(const FusedArgs& a, int32_t tok, int32_t k0, bool rms, float inv) {
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (tok >= 0 && k0 < a.cols) {
+    const uint16_t* p = a.x + (int64_t)tok * a.cols + k0;
+    if (VEC) {
+      v = *(const uint4*)p;                      // cols % 8 == 0: k0 + 8 <= cols
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = k0 + i < a.cols ? p[i] : 0u;
+      v = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+    }
+    if (rms) v = make_uint4(h2_scale(v.x, inv), h2_scale(v.y, inv), h2_scale(v.z, inv), h2_scale(v.w, inv));
+  }
+  return __builtin_bit_cast(half8_t, v);
+}
+
+template <bool VEC>
+__device__ void mfma_chunk(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const Chunk& ch,
+                           uint32_t ctab_v) {
+  const int32_t R = a.mfma_rows;
+  const uint32_t wpr = ((uint32_t)a.cols + 15u) / 16u;
+  const MfmaLds L = mfma_lds(R, a.cols);
+  uint32_t* W = (uint32_t*)(smem + L.w);
+  uint2* lut = (uint2*)(smem + L.lut);
+  float* acc = (float*)(smem + L.acc);
+  uint32_t* scan = (uint32_t*)(smem + L.scan);
+  float* s_inv = (float*)(smem + L.rms);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t nt = (int32_t)ch.nt;
+  const int ntiles = (nt + 15) / 16;
+  const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
+  if (rms) {
+    // 1 / rms of every token row: wave w takes tokens w, w + 8, ...
+    for (int32_t t = wave; t < nt; t += kFWaves) {
+      const uint16_t* p = a.x + (int64_t)perm[ch.tb + t] * a.cols;
+      float ss = 0.f;
+      if (VEC) {
+        for (int32_t c = 8 * lane; c < a.cols; c += 8 * 64) {
+          const uint4 v = *(const uint4*)(p + c);
+          ss += h2_ssq(v.x) + h2_ssq(v.y) + h2_ssq(v.z) + h2_ssq(v.w);
+        }
+      } else {
+        for (int32_t c = lane; c < a.cols; c += 64) {
+          const float f = (float)__builtin_bit_cast(_Float16, p[c]);
+          ss += f * f;
+        }
+      }
+      const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_scan_f(ss)), 63));
+      const float ms = tot / (float)a.cols;
+      if (lane == 0) s_inv[t] = ms > 0.f ? 1.0f / sqrtf(ms) : 1.0f;
+    }
+    __syncthreads();
+  }
+  for (int b = threadIdx.x; b < 256; b += kFThreads) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = (b >> (2 * i)) & 3u;
+      h[i] = c == 1u ? 0xBC00u : (c == 2u ? 0x3C00u : 0u);
+    }
+    lut[b] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  }
+  // B-fragment tokens of this lane, one per 16-token tile
+  int32_t tok[kMfmaMaxTokens / 16];
+  float inv[kMfmaMaxTokens / 16];
+#pragma unroll
+  for (int n = 0; n < kMfmaMaxTokens / 16; ++n) {
+    const int32_t t = n * 16 + (lane & 15);
+    tok[n] = t < nt ? perm[ch.tb + t] : -1;
+    inv[n] = (rms && t < nt) ? s_inv[t] : 1.0f;
+  }
+  const int nm = R / 16, kparts = kFWaves / nm;
+  const int mt = wave % nm, kp = wave / nm;
+  const int32_t nks = (a.cols + 31) / 32;
+  for (int32_t r0 = ch.ra; r0 < ch.rb; r0 += R) {
+    const int32_t Rt = ch.rb - r0 < R ? ch.rb - r0 : R;
+    for (uint32_t i = threadIdx.x; i < (uint32_t)R * wpr; i += kFThreads) W[i] = 0u;
+    for (uint32_t i = threadIdx.x; i < (uint32_t)R * kMfmaMaxTokens; i += kFThreads) acc[i] = 0.f;
+    uint32_t c_lo = a.row_off[ch.off_base + r0], c_hi = a.row_off[ch.off_base + r0 + Rt];
+    c_hi = c_hi < ch.n_codes ? c_hi : ch.n_codes;          // offsets are trusted, indexes still bounded
+    c_lo = c_lo < c_hi ? c_lo : c_hi;
+    __syncthreads();
+    // decode: passes of kFThreads * kK codewords
+    uint32_t done6 = 0;                        // 6 * columns of the tile decoded by earlier passes
+    for (uint32_t cb = c_lo; cb < c_hi; cb += (uint32_t)kFThreads * kK) {
+      const uint32_t i0 = cb + threadIdx.x * kK;
+      uint32_t off[kK], cw[kK];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        const uint32_t idx = i0 + j;
+        off[j] = idx < c_hi ? (uint32_t)a.codes[ch.code_base + idx] : 0u;
+      }
+      uint32_t kk[kK];
+#pragma unroll
+      for (int j = 0; j < kK; ++j) kk[j] = g_tab.cls[off[j]];
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        cw[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)kk[j], (int)ctab_v);
+        off[j] += (uint32_t)(((int32_t)(cw[j] << 15)) >> 15);
+        tot += i0 + j < c_hi ? (cw[j] >> 24) : 0u;
+      }
+      const uint32_t incl = wave_incl_scan(tot);
+      if (lane == 63) scan[wave] = incl;
+      __syncthreads();
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) {
+        const uint32_t v = scan[w];
+        before += w < wave ? v : 0u;
+        all += v;
+      }
+      uint32_t p6 = a.colsB * (uint32_t)r0 + done6 + before + incl - tot;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        if (i0 + j < c_hi) {
+          uint32_t sw = g_tab.post[off[j] >> ((cw[j] >> 17) & 3u)];
+          sw += ((off[j] & 7u) * 0x8102u) & 0x20202u;
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const uint32_t byte = (sw >> (8 * i)) & 0xFFu;
+            const uint32_t p6i = 6u * ((byte * 171u) >> 10);          // 6 * position in the run
+            const uint32_t k = byte - p6i;                            // 0: -1, 2: +1, 4: zero
+            if (k != 4u) {
+              const uint32_t q6 = p6 + p6i;
+              const uint32_t row = div_magic_dev(q6, a.magic_m, a.magic_s);
+              const uint32_t col = div6_exact(q6 - row * a.colsB);
+              const int32_t rr = (int32_t)row - r0;
+              if (rr >= 0 && rr < Rt)
+                atomicOr(&W[(uint32_t)rr * wpr + (col >> 4)], (k == 0u ? 1u : 2u) << ((col & 15u) * 2u));
+            }
+          }
+          p6 += cw[j] >> 24;
+        }
+      }
+      done6 += all;
+      __syncthreads();                         // scan reused by the next pass; W complete after the last
+    }
+    // multiply: wave (mt, kp) takes rows mt*16.. and K-steps kp, kp + kparts, ...
+    float4_t cacc[kMfmaMaxTokens / 16];
+#pragma unroll
+    for (int n = 0; n < kMfmaMaxTokens / 16; ++n) cacc[n] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t arow = (uint32_t)(mt * 16 + (lane & 15)) * wpr;
+    // K-steps in groups of kU: every A and B fragment of a group is requested
+    // before its first product, so the global B loads overlap
+    constexpr int kU = 4;
+    for (int32_t ks0 = kp; ks0 < nks; ks0 += kparts * kU) {
+      half8_t A[kU], B[kU][kMfmaMaxTokens / 16];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int32_t k0 = (ks0 + u * kparts) * 32 + 8 * (lane >> 4);
+        uint4 av = make_uint4(0, 0, 0, 0);
+        if (k0 < a.cols) {
+          const uint32_t wv = W[arow + ((uint32_t)k0 >> 4)] >> (((uint32_t)k0 & 15u) * 2u);
+          const uint2 lo = lut[wv & 0xFFu], hi = lut[(wv >> 8) & 0xFFu];
+          av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        A[u] = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+        for (int n = 0; n < kMfmaMaxTokens / 16; ++n)
+          B[u][n] = n < ntiles ? mfma_b_frag<VEC>(a, tok[n], k0, rms, inv[n]) : half8_t{};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int n = 0; n < kMfmaMaxTokens / 16; ++n)
+          if (n < ntiles) cacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u], B[u][n], cacc[n], 0, 0, 0);
+    }
+    // C layout: lane holds column (token) lane % 16, rows 4 * (lane / 16) + i
+#pragma unroll
+    for (int n = 0; n < kMfmaMaxTokens / 16; ++n)
+      if (n < ntiles) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          atomicAdd(&acc[(mt * 16 + 4 * (lane >> 4) + i) * kMfmaMaxTokens + n * 16 + (lane & 15)], cacc[n][i]);
+      }
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < Rt * nt; i += kFThreads) {
+      const int32_t r = i / nt, t = i - r * nt;
+      float v = acc[r * kMfmaMaxTokens + t];
+      v *= (float)(*(const _Float16*)(a.scales + ch.scale_base + r0 + r));
+      if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+      const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + r0 + r;
+      if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+      else ((_Float16*)a.y)[o] = (_Float16)v;
+    }
+    __syncthreads();
+  }
+}
+
 // Chunks of the current round of a workgroup's slice (LDS) and the block
 // sequence counter the waves draw from.
 constexpr int kMaxChunks = 16;
@@ -885,8 +1128,10 @@ __device__ __forceinline__ Chunk load_chunk(uint32_t c) {
   ch.n_codes = u32(m.n_codes);
   ch.blk_base = u64(m.blk_base);
   ch.scale_base = u64(m.scale_base);
+  ch.off_base = u64(m.off_base);
   ch.seq0 = u32(m.seq0);
   ch.ok = u32((uint32_t)m.ok) != 0;
+  ch.mfma = u32((uint32_t)m.mfma) != 0;
   return ch;
 }
 
@@ -957,6 +1202,18 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
     Slot r0 = grab(a, nseq, nch, wave), r1 = grab(a, nseq, nch, wave + kFWaves);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
+      if (ch.mfma) {
+        // dense tiles overwrite the accumulators and the staged activations
+        if (ch.ok) {
+          if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, ctab_v);
+          else mfma_chunk<false>(a, smem, perm, ch, ctab_v);
+        }
+        const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;
+        for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
+        cur_q = 0xFFFFFFFFu;
+        __syncthreads();
+        continue;
+      }
       const int tc = tc_of(ch.nt);
       if (ch.q != cur_q) {
         if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
@@ -987,7 +1244,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       XPre xp;
       if (c + 1 < nch) {
         nx = load_chunk(c + 1);
-        next_new = nx.q != ch.q;
+        next_new = nx.q != ch.q && !nx.mfma;
         const int ntc = tc_of(nx.nt);
         if (next_new && x_prefetchable(a, ntc)) {
           next_pre = true;
@@ -1105,10 +1362,11 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     const bool valid = key != kNone;
     if (valid) {
       const uint32_t rank = rk[tid], off = rank - lt[tid], cnt = eq[tid];
-      const uint32_t tcm = (uint32_t)a.tcmax;
+      const bool heavy = a.mfma_rows > 0 && cnt >= (uint32_t)kMfmaMinTokens;
+      const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.tcmax;
       s_perm[rank] = tid;
       ks[rank] = key;
-      if (off % tcm == 0) nts[rank] = cnt - off < tcm ? cnt - off : tcm;
+      if (off % span == 0) nts[rank] = (cnt - off < span ? cnt - off : span) | (heavy ? kItemMfma : 0u);
     }
     const uint64_t b = __ballot(valid);
     if ((tid & 63) == 0 && b) atomicAdd(&s_ghdr[2], (uint32_t)__popcll(b));
@@ -1314,7 +1572,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
-  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
   if (n_tokens == 0) return SBM_OK;
   if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
       !workspace)
@@ -1363,16 +1621,24 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   // rows (activation restaging, drain, epilogue); a one-token row of cols
   // columns is about cols / 22 codewords and weighs 4
   a.item_cost = (uint32_t)std::min<int64_t>(4ll * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
+  // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
+  const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
+  // dense MFMA tiles for heavy experts reuse the same dynamic LDS
+  a.mfma_rows = 0;
+  for (int R : {64, 32, 16})
+    if ((flags & SBM_F_MFMA) && mfma_lds(R, cols).total <= lds) {
+      a.mfma_rows = R;
+      break;
+    }
   a.group_in_lds = n_tokens <= kGroupInLds && n_experts < (1 << 24);
   hipError_t e;
   if (!a.group_in_lds) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                       plan.tcmax, rows, cols, (int32_t)grid, a.item_cost, experts, (uint32_t*)workspace);
+                       plan.tcmax, rows, cols, (int32_t)grid, a.item_cost, (int32_t)(a.mfma_rows > 0), experts,
+                       (uint32_t*)workspace);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }
-  // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
-  const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
   hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));

@@ -56,7 +56,8 @@ def test_decode_ref_flags_truncated_rows(dev, lib_state, odict):
     assert int(bad.item()) == 2
 
 
-def _run(lib_state, experts, rows, cols, x, ids, dev, odict, relu=False, out_f32=False, check_every=1):
+def _run(lib_state, experts, rows, cols, x, ids, dev, odict, relu=False, out_f32=False, check_every=1,
+         mfma=False):
     api = lib_state["api"]
     mats = P.encode_all(experts, odict["words"], odict, check_every)
     stack = api.ExpertStack.from_host(mats, rows, cols, dev)
@@ -64,7 +65,7 @@ def _run(lib_state, experts, rows, cols, x, ids, dev, odict, relu=False, out_f32
     it = torch.from_numpy(np.asarray(ids, np.int32)).to(dev)
     ws = api.alloc_workspace(stack.n_experts, x.shape[0], dev)
     y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], xt, it, relu=relu, out_f32=out_f32,
-                                    workspace=ws)
+                                    workspace=ws, mfma=mfma)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), api.workspace_error(ws)
 
@@ -85,10 +86,12 @@ def test_fused_single_expert(dev, lib_state, odict, rows, cols, p0, T):
             P.assert_close(y, ref, 2e-6, 2e-5, what="fp32 output")
 
 
-@pytest.mark.parametrize("rows,cols,T", [(300, 2080, 3), (130, 6144, 2), (64, 98, 5), (40, 512, 9)])
+@pytest.mark.parametrize("rows,cols,T", [(300, 2080, 3), (130, 6144, 2), (64, 98, 5), (40, 512, 9),
+                                         (200, 512, 50), (90, 770, 48)])
 def test_fused_input_rms(dev, lib_state, odict, rows, cols, T):
     """SBM_F_IN_RMS: each token row is first scaled to unit RMS (the stack
-    glue), including a zero row, which stays zero."""
+    glue), including a zero row, which stays zero; at T >= 48 every expert
+    has at least 16 tokens and the call asks for the dense-tile path."""
     from oracle import matvec as OM
     api = lib_state["api"]
     E = 3
@@ -100,7 +103,8 @@ def test_fused_input_rms(dev, lib_state, odict, rows, cols, T):
     ids = (np.arange(T) % E).astype(np.int32)
     ws = api.alloc_workspace(E, T, dev)
     y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
-                                    torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, in_rms=True)
+                                    torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, in_rms=True,
+                                    mfma=T >= 48)
     torch.cuda.synchronize()
     assert api.workspace_error(ws) == 0
     yn = y.cpu().numpy().astype(np.float64)
@@ -145,6 +149,36 @@ def test_fused_grouped_routing_and_edges(dev, lib_state, odict):
         for t in range(T):
             ref = np.maximum(P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0], 0)
             P.assert_close(y[t], ref, what=f"T={T} token {t}")
+
+
+@pytest.mark.parametrize("rows,cols,counts", [(300, 512, (16, 3, 40)), (130, 6144, (17, 1)),
+                                               (77, 98, (64, 65, 2)), (100, 2080, (100, 16)),
+                                               (45, 770, (33,)), (6, 4, (20, 1))])
+def test_fused_heavy_experts_dense_tiles(dev, lib_state, odict, rows, cols, counts):
+    """With SBM_F_MFMA, experts with 16 or more tokens run on the dense-tile
+    path (items of up to 64 tokens, row tiles with a ragged last tile), the
+    rest on the sparse path; both, and the sparse path alone, against the
+    oracle."""
+    E = len(counts)
+    ex = P.host_experts(E, rows, cols, 0.886, rows * 7 + cols)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = ids[np.random.default_rng(cols).permutation(ids.size)]
+    T = ids.size
+    x = np.random.default_rng(rows).standard_normal((T, cols)).astype(np.float16)
+    ref = np.empty((T, rows))
+    for e in range(E):
+        tok = np.flatnonzero(ids == e)
+        ref[tok] = P.oracle_matvec_from_symbols(*ex[e], x[tok])
+    for mfma in (True, False):
+        print(f"heavy {rows}x{cols} counts={counts} mfma={mfma}", flush=True)
+        for out_f32 in (True, False):
+            y, err = _run(lib_state, ex, rows, cols, x, ids, dev, odict, out_f32=out_f32, mfma=mfma)
+            assert err == 0
+            for e in range(E):
+                tok = np.flatnonzero(ids == e)
+                P.assert_close(y[tok], ref[tok], what=f"expert {e} ({counts[e]} tokens) mfma={mfma} f32={out_f32}")
+                if out_f32:
+                    P.assert_close(y[tok], ref[tok], 2e-6, 2e-5, what="fp32 output")
 
 
 @pytest.mark.parametrize("T", [4, 140])
