@@ -873,7 +873,7 @@ __device__ __forceinline__ half8_t mfma_b_frag(const FusedArgs& a, int32_t tok, 
 }
 
 template <bool VEC>
-__device__ void mfma_chunk(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const Chunk& ch,
+__device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const Chunk& ch,
                            uint32_t ctab_v) {
   const int32_t R = a.mfma_rows;
   const uint32_t wpr = ((uint32_t)a.cols + 15u) / 16u;
@@ -1181,7 +1181,9 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
   return sl;
 }
 
-template <bool SMALL>
+// MFMA: the kernel instance that runs dense-tile items (SBM_F_MFMA); the
+// default instance has no call in its loop, which keeps its registers unspilled.
+template <bool SMALL, bool MFMA>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1, uint32_t ctab_v) {
   float* racc = (float*)(smem + a.lds_racc);
@@ -1202,7 +1204,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
     Slot r0 = grab(a, nseq, nch, wave), r1 = grab(a, nseq, nch, wave + kFWaves);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
-      if (ch.mfma) {
+      if (MFMA && ch.mfma) {
         // dense tiles overwrite the accumulators and the staged activations
         if (ch.ok) {
           if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, ctab_v);
@@ -1426,6 +1428,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
   }
 }
 
+template <bool MFMA>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   // Requests in order of need: token ids (every thread, no branch, so the
@@ -1465,8 +1468,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true>(a, smem, perm, items, g0, g1, ctab_v);
-  else run_slice<false>(a, smem, perm, items, g0, g1, ctab_v);
+  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, ctab_v);
+  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, ctab_v);
 }
 
 // ------------------------------------------------------------ host entries
@@ -1496,13 +1499,17 @@ static int dev_info(DevInfo** out) {
     di.max_lds = v;
   }
   if (!di.attr_set) {
-    hipFuncAttributes fa;
-    if ((e = hipFuncGetAttributes(&fa, (const void*)fused_kernel)) != hipSuccess)
-      return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
-    di.static_lds = (int)fa.sharedSizeBytes;
-    e = hipFuncSetAttribute((const void*)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            di.max_lds - di.static_lds);
-    if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    di.static_lds = 0;
+    for (const void* k : {(const void*)fused_kernel<false>, (const void*)fused_kernel<true>}) {
+      hipFuncAttributes fa;
+      if ((e = hipFuncGetAttributes(&fa, k)) != hipSuccess)
+        return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
+      di.static_lds = std::max(di.static_lds, (int)fa.sharedSizeBytes);
+    }
+    for (const void* k : {(const void*)fused_kernel<false>, (const void*)fused_kernel<true>}) {
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, di.max_lds - di.static_lds);
+      if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    }
     di.attr_set = true;
   }
   *out = &di;
@@ -1639,7 +1646,8 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
     e = hipGetLastError();
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(fused_kernel, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
   return SBM_OK;
