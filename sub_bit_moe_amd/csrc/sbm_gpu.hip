@@ -343,14 +343,18 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
 // Copy of the decode image into LDS with direct-to-LDS loads issued at kernel
 // entry: each wave moves 1 KB per instruction (lane l's 16 bytes land at the
 // wave's LDS base + 16 l), so the copy holds no registers and completes while
-// the tokens are grouped.  Readers wait for vmcnt(0) and a barrier.
+// the tokens are grouped.  Wave 0 issues none of it: its loads (ids,
+// descriptors, row offsets) form the prologue's dependent chain, and a wait
+// for them would also wait for every load issued before them.  Readers wait
+// for vmcnt(0) and then a barrier.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void stage_tables_dma(const DictImage* __restrict__ im) {
   const uint4* src = (const uint4*)im->cls_base;
   uint4* dst = (uint4*)g_tab.bases;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (uint32_t q = wave; q * 64 < kImageCopyU4; q += kFWaves) {
+  if (wave == 0) return;
+  for (uint32_t q = wave - 1; q * 64 < kImageCopyU4; q += kFWaves - 1) {
     const uint32_t i = q * 64 + lane;
     if (i < kImageCopyU4)
       __builtin_amdgcn_global_load_lds((const void*)(src + i), (lds_void_t*)(dst + q * 64), 16, 0, 0);
@@ -887,6 +891,7 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
   const int32_t nt = (int32_t)ch.nt;
   const int ntiles = (nt + 15) / 16;
   const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
+  wait_vmem_all();        // this wave's part of the image has landed (barriers below)
   if (rms) {
     // 1 / rms of every token row: wave w takes tokens w, w + 8, ...
     for (int32_t t = wave; t < nt; t += kFWaves) {
@@ -1187,9 +1192,9 @@ template <bool SMALL, bool MFMA>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1, uint32_t ctab_v) {
   float* racc = (float*)(smem + a.lds_racc);
-  // the image copy was issued at kernel entry; this wave's part has landed
-  // once its vector memory count drains, every wave's after build_chunks' barrier
-  wait_vmem_all();
+  // the image copy issued at kernel entry is waited for just before the
+  // barrier that follows the first activation staging (or inside the first
+  // dense tile), so the chunk table and first blocks are fetched meanwhile
   {
     const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;   // lds_racc region is 16B-aligned
     for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
@@ -1222,6 +1227,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
         else stage_x<4>(a, smem, perm, ch.tb, ch.nt);
         cur_q = ch.q;
+        wait_vmem_all();      // this wave's part of the image has landed
         __syncthreads();
       }
       const uint32_t seq_end = c + 1 < nch ? __builtin_amdgcn_readfirstlane(s_chunks[c + 1].seq0) : nseq;
@@ -1428,6 +1434,83 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
   }
 }
 
+// Token grouping for n_tokens <= 64 by wave 0 alone, with no workgroup
+// barrier until the results are published: lane t holds token t's key
+// (expert << 6 | t); its rank among the keys (a readlane loop over the
+// tokens) is its place in perm.  Lane r then reads the r-th smallest key back;
+// expert runs and item starts are ballots over the sorted keys, item numbers
+// are prefix popcounts and item weights a wave scan.  Items, perm and the
+// workgroup's slice are the same as group_lds derives.
+__device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int32_t my_id) {
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  const int32_t T = a.n_tokens;
+  if (threadIdx.x < 64) {
+    const uint32_t lane = threadIdx.x;
+    const bool valid = (int32_t)lane < T && my_id >= 0 && my_id < a.n_experts;
+    const uint32_t key = valid ? (((uint32_t)my_id << 6) | lane) : kNone;
+    uint32_t rank = 0;
+    for (int32_t u = 0; u < T; ++u) rank += (uint32_t)__builtin_amdgcn_readlane((int)key, u) < key ? 1u : 0u;
+    const uint32_t nv = (uint32_t)__popcll(__ballot(valid));
+    if (valid) sc[rank] = key;              // valid keys rank below every kNone
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t r = lane;
+    const bool in = r < nv;
+    const uint32_t k = in ? sc[r] : kNone;
+    const uint32_t kp = (in && r > 0) ? sc[r - 1] : kNone;
+    const uint32_t e = k >> 6;
+    const bool start = in && (r == 0 || (kp >> 6) != e);
+    const uint64_t sb = __ballot(start);
+    const uint64_t upto = ((uint64_t)2 << r) - 1;      // bits 0..r (r = 63: all)
+    const uint64_t below = sb & upto, above = sb & ~upto;
+    const uint32_t rs = below ? 63u - (uint32_t)__builtin_clzll(below) : 0u;   // this run's first place
+    const uint32_t re = above ? (uint32_t)__builtin_ctzll(above) : nv;   // next run's first place
+    const uint32_t off = r - rs, cnt = re - rs;
+    const bool heavy = a.mfma_rows > 0 && cnt >= (uint32_t)kMfmaMinTokens;
+    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.tcmax;
+    const bool istart = in && off % span == 0;
+    const uint32_t nt = istart ? ((cnt - off < span ? cnt - off : span) | (heavy ? kItemMfma : 0u)) : 0u;
+    const uint64_t ib = __ballot(istart);
+    const uint32_t q = (uint32_t)__popcll(ib & (((uint64_t)1 << r) - 1));
+    const uint32_t w = istart ? item_weight(nt) : 0u;
+    const uint32_t wi = wave_incl_scan(w);
+    const uint32_t wq = wi - w;
+    if (in) s_perm[r] = (int32_t)(k & 63u);
+    if (istart) s_items[q] = make_uint4(e, r, nt, wq);
+    const uint32_t n_items = (uint32_t)__popcll(ib), wtot = __builtin_amdgcn_readlane(wi, 63);
+    // this workgroup's slice [u0, u1) of the weighted (item, row) space
+    const uint32_t F = a.item_cost;
+    const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
+    const uint64_t u[2] = {udiv_small(wall * blockIdx.x, (uint32_t)a.grid),
+                           udiv_small(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
+    if (istart) {
+      const uint64_t pq = (uint64_t)wq * rows + (uint64_t)q * F;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (u[h] >= pq && u[h] < pq + F + (uint64_t)w * rows) s_slice[h] = boundary_in_item(u[h], pq, q, w, F, rows);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (u[h] >= wall) s_slice[h] = (uint64_t)n_items * rows;
+      s_ghdr[0] = n_items;
+      s_ghdr[1] = wtot;
+      s_ghdr[2] = nv;
+      s_ghdr[3] = 0;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    // descriptors of the touched experts; workgroup 0 alone writes the error word
+    const uint32_t n_items = s_ghdr[0];
+    for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
+      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols)) atomicOr(&s_ghdr[3], 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
+  }
+}
+
 template <bool MFMA>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1446,7 +1529,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const uint4* items;
   uint64_t g0, g1;
   if (a.group_in_lds) {
-    group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
+    if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
+    else group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
     if (!image_ok) {
       if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = kErrBadImage;   // after the grouping's write
       return;

@@ -181,7 +181,7 @@ def test_fused_heavy_experts_dense_tiles(dev, lib_state, odict, rows, cols, coun
                     P.assert_close(y[tok], ref[tok], 2e-6, 2e-5, what="fp32 output")
 
 
-@pytest.mark.parametrize("T", [4, 140])
+@pytest.mark.parametrize("T", [4, 64, 100, 140])
 def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict, T):
     """Up to 128 tokens are grouped inside the fused kernel, more by the
     grouping kernel: both count out-of-range ids and leave their rows alone."""
@@ -206,7 +206,7 @@ def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict, T):
         P.assert_close(yn[t], P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0])
 
 
-@pytest.mark.parametrize("T", [5, 150])
+@pytest.mark.parametrize("T", [5, 90, 150])
 def test_fused_bad_descriptor_is_flagged(dev, lib_state, odict, T):
     """An expert whose descriptor disagrees with the call's shape produces no
     rows and sets the descriptor bit of the error word; the others are exact."""
