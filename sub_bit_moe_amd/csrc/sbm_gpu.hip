@@ -193,8 +193,26 @@ __global__ void decode_ref_kernel(const uint16_t* __restrict__ codes,
 // leading F charges the activation restaging and drain of an item change to
 // the slice that contains it.  Positions map monotonically to global row
 // indices (item * rows + row), so consecutive workgroups tile the row space.
+// floor(n / d) for d > 0: a double quotient corrected to the exact floor when
+// n < 2^52, else the 64-bit division.  On per-lane (vector) values this stays
+// in VALU instructions.
 __device__ __forceinline__ uint64_t udiv_small(uint64_t n, uint32_t d) {
-  return (n >> 32) == 0 ? (uint64_t)((uint32_t)n / d) : n / d;
+  if (n < (1ull << 52)) {
+    uint64_t q = (uint64_t)((double)n / (double)d);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+  }
+  return n / d;
+}
+
+// A zero the compiler cannot see through: adding it makes a value per-lane,
+// so arithmetic on it is done in vector registers instead of scalar ones
+// (which would need vector -> scalar round trips for divisions).
+__device__ __forceinline__ uint32_t vzero() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
 }
 
 __device__ __forceinline__ uint64_t boundary_in_item(uint64_t u, uint64_t pq, uint32_t q, uint32_t wq, uint32_t F,
@@ -1066,7 +1084,7 @@ __device__ __forceinline__ void build_chunks(const FusedArgs& a, const uint4* it
   static_assert(kMaxChunks <= 64, "one lane per chunk");
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    uint32_t q = (uint32_t)udiv_small(g, (uint32_t)a.rows);
+    uint32_t q = (uint32_t)udiv_small(g + vzero(), (uint32_t)a.rows);
     int32_t ra = (int32_t)(g - (uint64_t)q * a.rows);
     uint64_t gg = g;
     // end row of the chunk starting at row ra of an item, global index gg
@@ -1436,8 +1454,9 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
 
 // Token grouping for n_tokens <= 64 by wave 0 alone, with no workgroup
 // barrier until the results are published: lane t holds token t's key
-// (expert << 6 | t); its rank among the keys (a readlane loop over the
-// tokens) is its place in perm.  Lane r then reads the r-th smallest key back;
+// (expert << 6 | t); its rank among the keys (a count over all 64 keys, read
+// back from LDS as broadcasts) is its place in perm.  Lane r then reads the
+// r-th smallest key back;
 // expert runs and item starts are ballots over the sorted keys, item numbers
 // are prefix popcounts and item weights a wave scan.  Items, perm and the
 // workgroup's slice are the same as group_lds derives.
@@ -1448,17 +1467,26 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     const uint32_t lane = threadIdx.x;
     const bool valid = (int32_t)lane < T && my_id >= 0 && my_id < a.n_experts;
     const uint32_t key = valid ? (((uint32_t)my_id << 6) | lane) : kNone;
+    uint32_t* ks = sc + 64;                 // keys by lane, then by sorted place
+    sc[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint32_t rank = 0;
-    for (int32_t u = 0; u < T; ++u) rank += (uint32_t)__builtin_amdgcn_readlane((int)key, u) < key ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < 64; u += 4) {       // every lane reads the same words
+      const uint4 k4 = *(const uint4*)(sc + u);
+      rank += (k4.x < key ? 1u : 0u) + (k4.y < key ? 1u : 0u) + (k4.z < key ? 1u : 0u) + (k4.w < key ? 1u : 0u);
+    }
     const uint32_t nv = (uint32_t)__popcll(__ballot(valid));
-    if (valid) sc[rank] = key;              // valid keys rank below every kNone
+    if (valid) ks[rank] = key;              // valid keys rank below every kNone
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t r = lane;
     const bool in = r < nv;
-    const uint32_t k = in ? sc[r] : kNone;
-    const uint32_t kp = (in && r > 0) ? sc[r - 1] : kNone;
+    const uint32_t k = in ? ks[r] : kNone;
+    const uint32_t kp = (in && r > 0) ? ks[r - 1] : kNone;
     const uint32_t e = k >> 6;
     const bool start = in && (r == 0 || (kp >> 6) != e);
     const uint64_t sb = __ballot(start);
@@ -1482,8 +1510,13 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     // this workgroup's slice [u0, u1) of the weighted (item, row) space
     const uint32_t F = a.item_cost;
     const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
-    const uint64_t u[2] = {udiv_small(wall * blockIdx.x, (uint32_t)a.grid),
-                           udiv_small(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
+    // lane h computes u_h, then both are broadcast
+    const uint64_t uh = udiv_small(wall * (blockIdx.x + (lane & 1u) + vzero()), (uint32_t)a.grid);
+    const uint64_t u[2] = {
+        (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)uh, 0) |
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uh >> 32), 0) << 32),
+        (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)uh, 1) |
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uh >> 32), 1) << 32)};
     if (istart) {
       const uint64_t pq = (uint64_t)wq * rows + (uint64_t)q * F;
 #pragma unroll
