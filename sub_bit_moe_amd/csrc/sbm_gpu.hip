@@ -215,11 +215,19 @@ __device__ __forceinline__ uint32_t vzero() {
   return z;
 }
 
+// Slice arithmetic needs no exact quotient: a boundary is computed by the
+// same expression in the two workgroups it separates, so any deterministic
+// rounding that is monotone in n keeps the slices tiling the row space.  A
+// double quotient stays in vector registers.
+__device__ __forceinline__ uint64_t slice_div(uint64_t n, uint32_t d) {
+  return (uint64_t)((double)n / (double)d);
+}
+
 __device__ __forceinline__ uint64_t boundary_in_item(uint64_t u, uint64_t pq, uint32_t q, uint32_t wq, uint32_t F,
                                                      uint64_t rows) {
   uint64_t r = 0;
   if (u > pq + F) {
-    r = udiv_small(u - pq - F + wq - 1, wq);
+    r = slice_div(u - pq - F + wq - 1, wq);
     if (r > rows) r = rows;
   }
   return (uint64_t)q * rows + r;
@@ -1420,8 +1428,8 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     const uint32_t n_items = __builtin_amdgcn_readlane(ci, 63), wtot = __builtin_amdgcn_readlane(wi, 63);
     const uint32_t F = a.item_cost;
     const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
-    const uint64_t u[2] = {udiv_small(wall * blockIdx.x, (uint32_t)a.grid),
-                           udiv_small(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
+    const uint64_t u[2] = {slice_div(wall * blockIdx.x, (uint32_t)a.grid),
+                           slice_div(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
     uint32_t qi = ci - c, wq = wi - w0 - w1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1461,7 +1469,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
 // are prefix popcounts and item weights a wave scan.  Items, perm and the
 // workgroup's slice are the same as group_lds derives.
 __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int32_t my_id) {
-  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  constexpr uint32_t kNone = 0x7FFFFFFFu;   // above every valid key (< 2^30)
   const int32_t T = a.n_tokens;
   if (threadIdx.x < 64) {
     const uint32_t lane = threadIdx.x;
@@ -1472,12 +1480,17 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint32_t rank = 0;
+    // keys are below 2^31, so the sign bit of kk - key is [kk < key]
+    uint32_t rk[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < 64; u += 4) {       // every lane reads the same words
       const uint4 k4 = *(const uint4*)(sc + u);
-      rank += (k4.x < key ? 1u : 0u) + (k4.y < key ? 1u : 0u) + (k4.z < key ? 1u : 0u) + (k4.w < key ? 1u : 0u);
+      rk[0] += (k4.x - key) >> 31;
+      rk[1] += (k4.y - key) >> 31;
+      rk[2] += (k4.z - key) >> 31;
+      rk[3] += (k4.w - key) >> 31;
     }
+    const uint32_t rank = rk[0] + rk[1] + rk[2] + rk[3];
     const uint32_t nv = (uint32_t)__popcll(__ballot(valid));
     if (valid) ks[rank] = key;              // valid keys rank below every kNone
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1506,12 +1519,13 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     const uint32_t wq = wi - w;
     if (in) s_perm[r] = (int32_t)(k & 63u);
     if (istart) s_items[q] = make_uint4(e, r, nt, wq);
+
     const uint32_t n_items = (uint32_t)__popcll(ib), wtot = __builtin_amdgcn_readlane(wi, 63);
     // this workgroup's slice [u0, u1) of the weighted (item, row) space
     const uint32_t F = a.item_cost;
     const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
     // lane h computes u_h, then both are broadcast
-    const uint64_t uh = udiv_small(wall * (blockIdx.x + (lane & 1u) + vzero()), (uint32_t)a.grid);
+    const uint64_t uh = slice_div(wall * (blockIdx.x + (lane & 1u) + vzero()), (uint32_t)a.grid);
     const uint64_t u[2] = {
         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)uh, 0) |
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uh >> 32), 0) << 32),
