@@ -526,8 +526,10 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    const uint32_t off = c[j] + (uint32_t)(((int32_t)(ca[j] << 15)) >> 15);
-    const uint32_t pidx = off >> ((ca[j] >> 17) & 3u);
+    // c + K(k) taken modulo 2^17 straight from the class word: the bits the
+    // word holds above K only reach bit 17 and up, and c + K < 2^15
+    const uint32_t off = c[j] + ca[j];
+    const uint32_t pidx = __builtin_amdgcn_ubfe(off, (ca[j] >> 17) & 3u, 14);
     sp[j] = ((off & 7u) * 0x8102u) & 0x20202u;           // sign bit i -> +2 in byte i
     slots[j] = g_tab.post[pidx];
     ls[j] = tot;
@@ -552,9 +554,6 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
     // is formed and its loads issued before the first sum, so up to 15 LDS
     // reads are in flight instead of three.
     constexpr int kXB = TC == 4 ? 4 : 8;
-    uint32_t frm = 0;                         // bit j: codeword j starts in row rl
-#pragma unroll
-    for (int j = 0; j < kK; ++j) frm |= (ls[j] < thr ? 1u : 0u) << j;
 #pragma unroll
     for (int j0 = 0; j0 < kK; j0 += kXB) {
       XVal<TC> xv[kXB][3];
@@ -564,12 +563,12 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
         const uint32_t s = slots[j];
         if constexpr (TC == 1) {
           // one add per slot: the byte operand is taken straight from s
-          const uint32_t bx = (((frm >> j) & 1u) ? base0x : base1x) + ls[j];
+          const uint32_t bx = (ls[j] < thr ? base0x : base1x) + ls[j];   // codeword j starts in row rl?
           xv[jj][0] = lds_x<TC>(smem, bx + (s & 0xFFu));
           xv[jj][1] = lds_x<TC>(smem, bx + ((s >> 8) & 0xFFu));
           xv[jj][2] = lds_x<TC>(smem, bx + ((s >> 16) & 0xFFu));
         } else {
-          const uint32_t base = (((frm >> j) & 1u) ? base0 : base1) + ls[j];
+          const uint32_t base = (ls[j] < thr ? base0 : base1) + ls[j];
           xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
           xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
           xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
@@ -582,7 +581,7 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
         acc_x<TC>(acc, xv[jj][0]);
         acc_x<TC>(acc, xv[jj][1]);
         acc_x<TC>(acc, xv[jj][2]);
-        const bool first_row = (frm >> j) & 1u;
+        const bool first_row = ls[j] < thr;
 #pragma unroll
         for (int t = 0; t < TC; ++t) snap[t] = first_row ? acc[t] : snap[t];
       }
