@@ -103,6 +103,103 @@ def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
                       f"multiplied in fp64 for their routed tokens, {reps} repetitions, {t_total:.1f} s timed"}
 
 
+def fusion_baselines(st, run, reps: int = 5):
+    """The touched experts of layer 0 three ways, same inputs: the fused
+    decode + matvec (two launches), the unfused path (GPU reference decode of
+    each matrix to symbols, dequantised to bf16, then a bf16 GEMM), and dense
+    bf16 GEMMs on uncompressed weights (decoded once, untimed).  The GEMMs are
+    the library's (hipBLASLt / rocBLAS through torch.matmul); these are
+    comparators for the fusion argument, not the product path."""
+    import numpy as np
+    import torch
+    from sub_bit_moe_amd import api
+    c = st.cfg
+    dev = st.x0.device
+    words, _ = api.build_dictionary(c.dict_p0)
+    words_t = torch.from_numpy(words.view(np.int32)).to(dev)
+    ids_h = st.routes_host[0]
+    experts = [int(e) for e in np.unique(ids_h)]
+    tok = {e: torch.from_numpy(np.flatnonzero(ids_h == e)).to(dev) for e in experts}
+    x = st.x0
+    stacks = (st.up[0], st.down[0])
+    sym_buf = [torch.empty((s.rows, s.cols), dtype=torch.uint8, device=dev) for s in stacks]
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def views(s, e):
+        d = s.host_desc[e]
+        return (s.codes[d.code_base:d.code_base + d.n_codes], s.row_off[d.off_base:d.off_base + s.rows + 1],
+                s.scales[d.scale_base:d.scale_base + s.rows])
+
+    def dequant(s, e, buf):
+        codes, off, sc = views(s, e)
+        api.decode_ref(codes, off, s.rows, s.cols, words_t, out=buf, bad=bad)
+        w = (buf == 2).to(torch.bfloat16) - (buf == 1).to(torch.bfloat16)
+        return (w * sc.to(torch.bfloat16)[:, None]).t().contiguous()      # [cols, rows]
+
+    dense = {e: [dequant(s, e, sym_buf[m]) for m, s in enumerate(stacks)] for e in experts}
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    xb = x.to(torch.bfloat16)
+
+    def run_dense():
+        out = {}
+        for e in experts:
+            h = torch.relu(xb[tok[e]] @ dense[e][0])
+            out[e] = h @ dense[e][1]
+        return out
+
+    def run_unfused():
+        for e in experts:
+            h = torch.relu(xb[tok[e]] @ dequant(stacks[0], e, sym_buf[0]))
+            h @ dequant(stacks[1], e, sym_buf[1])
+
+    def run_fused():
+        ids = st.routes[0]
+        api.moe_fused_decode_matvec(st.up[0], st.image, x, ids, relu=True, workspace=run.ws_up, y=run.h)
+        api.moe_fused_decode_matvec(st.down[0], st.image, run.h, ids, workspace=run.ws_down, y=run.y)
+
+    def timed(fn):
+        # each path captured in a graph, so launch overheads are the graph's
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / reps
+
+    t_fused, t_dense, t_unfused = timed(run_fused), timed(run_dense), timed(run_unfused)
+    yd = run_dense()
+    torch.cuda.synchronize()
+    yf = run.y.float()
+    num = sum(float(((yd[e].float() - yf[tok[e]]) ** 2).sum()) for e in experts)
+    den = sum(float((yf[tok[e]] ** 2).sum()) for e in experts)
+    comp = sum(s.matrix_bytes(e) for e in experts for s in stacks)
+    dense_bytes = sum(2 * s.rows * s.cols for e in experts for s in stacks)
+    return {"layer": 0, "experts": len(experts), "tokens": int(c.n_tokens),
+            "fused_us": round(t_fused, 1), "unfused_decode_bf16_gemm_us": round(t_unfused, 1),
+            "dense_bf16_gemm_us": round(t_dense, 1),
+            "dense_over_fused": round(t_dense / t_fused, 2), "unfused_over_fused": round(t_unfused / t_fused, 2),
+            "fused_compressed_GBps": round(comp / t_fused / 1e3, 1),
+            "dense_bf16_GBps": round(dense_bytes / t_dense / 1e3, 1),
+            "dense_bf16_hbm_floor_us": round(dense_bytes / (HBM_PEAK_GBPS * 1e3), 1),
+            "unfused_hbm_floor_us": round(3 * dense_bytes / (HBM_PEAK_GBPS * 1e3), 1),
+            "dense_vs_fused_rel_l2": round((num / den) ** 0.5, 4),
+            "note": "each path graph-captured; fused = two launches of the library; unfused = reference "
+                    "decode kernel (one thread per row) + torch dequantise + bf16 GEMM per matrix; dense = "
+                    "bf16 GEMMs per expert on weights decoded beforehand (bf16 scales, hence the rel-L2 "
+                    "against the fused output); floors = bf16 weight bytes read once (dense) or written, "
+                    "read back and read again (unfused) at 8 TB/s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +208,8 @@ def main():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--experts", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fusion-baselines", action="store_true",
+                    help="skip the unfused and dense bf16 comparators on layer 0")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-size kernel for scaling "
                          "hardware byte counters)")
@@ -189,6 +288,12 @@ def main():
                 "kernel": "sbm::fused_kernel (token grouping inside; 2 launches per layer)",
                 "avg_launch_us": round(launch_us, 2),
                 "bytes_per_launch": int(bytes_per_launch)}
+    fusion = None
+    if not args.no_fusion_baselines:
+        log("fusion baselines (layer 0: unfused decode -> bf16 -> GEMM, dense bf16 GEMM) ...")
+        fusion = fusion_baselines(st, run)
+        log(f"layer 0: fused {fusion['fused_us']} us, unfused {fusion['unfused_decode_bf16_gemm_us']} us, "
+            f"dense bf16 {fusion['dense_bf16_gemm_us']} us")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -216,6 +321,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fusion_baselines": fusion,
     }
     print(json.dumps(out), flush=True)
 

@@ -151,11 +151,13 @@ def device_image(words: np.ndarray, device="cuda"):
 
 # ------------------------------------------------------------------ GPU calls
 
-def decode_ref(codes_t, row_off_t, rows: int, cols: int, words_t, stream=None):
+def decode_ref(codes_t, row_off_t, rows: int, cols: int, words_t, stream=None, out=None, bad=None):
     """GPU reference decode of one matrix -> (symbols uint8 [rows, cols], bad_rows)."""
     import torch
-    out = torch.empty((rows, cols), dtype=torch.uint8, device=codes_t.device)
-    bad = torch.zeros(1, dtype=torch.int32, device=codes_t.device)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=codes_t.device)
+    if bad is None:
+        bad = torch.zeros(1, dtype=torch.int32, device=codes_t.device)
     check(lib().sbm_decode_ref(_ptr(codes_t), _ptr(row_off_t), rows, cols, _ptr(words_t), _ptr(out),
                                _ptr(bad), _stream(stream)))
     return out, bad
