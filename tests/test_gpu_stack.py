@@ -20,6 +20,11 @@ def dev():
     return torch.device("cuda:0")
 
 
+def api_error(ws):
+    from sub_bit_moe_amd import api
+    return api.workspace_error(ws)
+
+
 @pytest.fixture(scope="module")
 def gen_state(dev, odict):
     from sub_bit_moe_amd import api
@@ -114,3 +119,79 @@ def test_graph_replay_matches_eager(dev):
         P.assert_close(out.float().cpu().numpy(), ref.float().cpu().numpy(), 2e-3, 2e-3, what="replay")
         run.run()              # eager work in between
         torch.cuda.synchronize()
+
+
+def _check_sampled(cfg, layer, xin, h, y, ids, experts, n_tok, n_rows, rng):
+    """Oracle check of sampled rows of the up (ReLU) and down outputs of the
+    given experts for up to n_tok of their tokens, on the GPU's own inputs."""
+    for e in experts:
+        toks = np.flatnonzero(ids == e)
+        toks = toks if toks.size <= n_tok else rng.choice(toks, n_tok, replace=False)
+        for mat in (0, 1):
+            rows, cols = (cfg.d_ff, cfg.d_model) if mat == 0 else (cfg.d_model, cfg.d_ff)
+            key = synth.matrix_key(cfg.seed, layer, int(e), mat, cfg.n_experts)
+            rsel = np.sort(rng.choice(rows, n_rows, replace=False))
+            sym = np.concatenate([synth.counter_symbols(key, 1, cols, cfg.p0, row0=int(r)) for r in rsel])
+            sc = synth.scale_table()[synth.counter_scale_index(key, rows)][rsel]
+            inp = (xin if mat == 0 else h)[toks].astype(np.float16)
+            ref = P.oracle_matvec_from_symbols(sym, sc, inp)
+            if mat == 0:
+                ref = np.maximum(ref, 0)
+            out = (h if mat == 0 else y)[toks][:, rsel]
+            for i, t in enumerate(toks):
+                P.assert_close(out[i], ref[i], what=f"layer {layer} expert {e} token {t} mat {mat}")
+
+
+def _sample_experts(ids, k, rng):
+    """Seeded sample of touched experts, always with the most loaded one."""
+    touched, counts = np.unique(ids, return_counts=True)
+    pick = set(rng.choice(touched, min(k, touched.size), replace=False).tolist())
+    pick.add(int(touched[np.argmax(counts)]))
+    return sorted(pick)
+
+
+def test_c2048_layer_256_tokens(dev):
+    """One c2048-shaped layer at full size: 2048 experts of 6144x2080 and
+    2080x6144, 256 Zipf tokens (grouped by the separate grouping launch): 32
+    sampled experts plus the most loaded one, 32 rows per matrix, against the
+    oracle."""
+    from sub_bit_moe_amd import stack as S
+    cfg = S.StackConfig(n_layers=1, n_experts=2048, n_tokens=256, seed=31)
+    st = S.build(cfg, dev)
+    run = S.Runner(st)
+    keep = {}
+    run.run(keep)
+    torch.cuda.synchronize()
+    assert api_error(run.ws_up) == 0 and api_error(run.ws_down) == 0
+    xin, h, y = (t.float().cpu().numpy() for t in keep[0])
+    rng = np.random.default_rng(32)
+    _check_sampled(cfg, 0, xin, h, y, st.routes_host[0], _sample_experts(st.routes_host[0], 32, rng), 4, 32, rng)
+    del st, run, keep
+    torch.cuda.empty_cache()
+
+
+def test_full_bench_stack_sampled(dev):
+    """The benchmark's own workload and launch configuration: 30 layers x 2048
+    experts (~148 GB generated on the GPU), 64 tokens through every layer;
+    per layer 2 sampled experts (one of them the most loaded), 2 of their
+    tokens and 24 rows per matrix against the oracle on the GPU's inputs."""
+    from oracle import matvec as OMv
+    from sub_bit_moe_amd import stack as S
+    torch.cuda.empty_cache()
+    cfg = S.StackConfig()
+    st = S.build(cfg, dev)
+    run = S.Runner(st)
+    keep = {}
+    run.run(keep)
+    torch.cuda.synchronize()
+    assert api_error(run.ws_up) == 0 and api_error(run.ws_down) == 0
+    rng = np.random.default_rng(41)
+    prev_y = None
+    for l in range(cfg.n_layers):
+        xraw, h, y = (t.float().cpu().numpy() for t in keep[l])
+        xin = xraw if l == 0 else OMv.rms_glue(prev_y).astype(np.float64)
+        ids = st.routes_host[l]
+        _check_sampled(cfg, l, xin, h, y, ids, _sample_experts(ids, 1, rng), 2, 24, rng)
+        prev_y = y
+    del st, run, keep
+    torch.cuda.empty_cache()
