@@ -66,7 +66,7 @@ __shared__ LdsTables g_tab;
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
 constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
-constexpr int kItemChangeBlocks = 12;
+constexpr int kItemChangeBlocks = 20;   // measured: a chunk change costs ~16 one-token blocks
 // Heavy experts (at least kMfmaMinTokens tokens) take the dense-tile MFMA path:
 // items of up to kMfmaMaxTokens tokens, flagged in the item's token-count word.
 constexpr uint32_t kItemMfma = 0x80000000u;
