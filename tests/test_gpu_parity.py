@@ -280,3 +280,22 @@ def test_c2048_pair(dev, lib_state, odict, T):
     for t in range(T):
         P.assert_close(h[t], ref_h[t], what=f"up t={t}")
         P.assert_close(y[t], ref_y[t], what=f"down t={t}")
+
+
+@pytest.mark.parametrize("T,d", [(64, 2080), (3, 6144), (5, 98)])
+def test_rms_glue_kernel(dev, T, d):
+    """The stack glue launch (once per pass) against its fp64 form: fp16 of
+    y / rms(y) per token, a zero row staying zero; at most one fp16 ulp apart
+    (fp32 against fp64 sums of squares)."""
+    from oracle import matvec as OM
+    from sub_bit_moe_amd import api
+    rng = np.random.default_rng(d)
+    y = (rng.standard_normal((T, d)) * rng.uniform(0.01, 30, (T, 1))).astype(np.float16)
+    y[T // 2] = 0
+    out = api.rms_glue(torch.from_numpy(y).to(dev))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = OM.rms_glue(y)
+    assert not np.any(got[T // 2])
+    ulp = np.abs(got.view(np.int16).astype(np.int32) - ref.view(np.int16).astype(np.int32))
+    assert ulp.max() <= 1, f"max {ulp.max()} fp16 ulps"
