@@ -22,5 +22,6 @@ Modules:
 
 Parity-pinning status of every function is listed in its docstring; the only
 function without an external pin is ``matvec.rms_glue`` (harness glue between
-stacked layers, not part of the method; parity unpinned).
+stacked layers, not part of the method; pinned by its defining properties:
+unit RMS, a positive multiple of the input, zero rows kept zero).
 """

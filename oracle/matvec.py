@@ -46,8 +46,9 @@ def relu(v):
 
 
 def rms_glue(y) -> np.ndarray:
-    """Harness glue between stacked layers (not part of the method; parity
-    unpinned): x_next = y / sqrt(mean(y^2)) per token, fp64, then fp16."""
+    """Harness glue between stacked layers (not part of the method): x_next =
+    y / sqrt(mean(y^2)) per token, fp64, then fp16.  Pinned by its defining
+    properties (unit RMS, a positive multiple of the input, zero rows stay zero)."""
     y = np.asarray(y, dtype=np.float64)
     r = np.sqrt(np.mean(y * y, axis=-1, keepdims=True))
     r = np.where(r > 0, r, 1.0)

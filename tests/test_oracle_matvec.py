@@ -63,3 +63,21 @@ def test_dequantize_symbol_map():
     sym = np.array([[0, 1, 2]], np.uint8)
     w = C.dequantize(sym, np.array([0.5], np.float16))
     assert w.tolist() == [[0.0, -0.5, 0.5]]
+
+
+def test_rms_glue_properties():
+    """The stack glue pinned by what it must satisfy rather than by its
+    formula: every nonzero output row has unit RMS (up to fp16 rounding) and is
+    a positive multiple of its input row; a zero row stays zero."""
+    rng = np.random.default_rng(3)
+    y = (rng.standard_normal((6, 300)) * rng.uniform(1e-3, 1e3, (6, 1))).astype(np.float16)
+    y[2] = 0
+    x = M.rms_glue(y).astype(np.float64)
+    for t in range(6):
+        if t == 2:
+            assert not np.any(x[t])
+            continue
+        assert abs(np.sqrt(np.mean(x[t] ** 2)) - 1.0) < 2e-3
+        yt = y[t].astype(np.float64)
+        k = np.dot(x[t], yt) / np.dot(yt, yt)
+        assert k > 0 and np.allclose(x[t], k * yt, rtol=2e-3, atol=2e-3)
