@@ -20,8 +20,8 @@ Modules:
   codec      -- trie encoder, reference decoder, row/block offset tables
   matvec     -- fp64 matrix-vector products, the MoE layer, stack glue
 
-Parity-pinning status of every function is listed in its docstring; the only
-function without an external pin is ``matvec.rms_glue`` (harness glue between
-stacked layers, not part of the method; pinned by its defining properties:
-unit RMS, a positive multiple of the input, zero rows kept zero).
+Parity-pinning status of every function is listed in its docstring.
+``matvec.rms_glue`` (harness glue between stacked layers, not part of the
+method) is pinned by its defining properties: unit RMS, a positive multiple of
+the input, zero rows kept zero.
 """
