@@ -12,14 +12,14 @@
 //  * Work: the output rows of every (expert, token chunk) item form one index
 //    space; each persistent workgroup owns a contiguous, row-aligned slice, so
 //    every output row is finished inside one workgroup (no global atomics).
-//  * Stream fetch: a wave handles one block of SBM_BLOCK = 512 codewords, 8
-//    per lane, read as one 16-byte load per lane (1 KiB per wave, coalesced).
+//  * Stream fetch: a wave handles one block of SBM_BLOCK = 1024 codewords, 16
+//    per lane, read as two 16-byte loads per lane (2 KiB per wave, coalesced).
 //    The block's start position comes from the per-block offset table.
-//  * Decode: the dictionary is held in LDS as a compact image (class per
-//    codeword, class table, colex position table); every entry has at most 3
-//    nonzeros, so a codeword yields its length and 3 "slots" (byte offsets of
-//    signed activations, or of a zero).  Work scales with nonzeros, never with
-//    the 28 symbols of a run.
+//  * Decode: the dictionary is held in LDS as one 60 KB table of 32-bit words
+//    (the image built on the host); every entry has at most 3 nonzeros, so a
+//    codeword yields its length and 3 "slots" (byte offsets of signed
+//    activations, or of a zero) from one table read plus its sign bits.  Work
+//    scales with nonzeros, never with the 28 symbols of a run.
 //  * Positions: lane-local prefix of run lengths plus one wave scan (DPP).
 //  * Accumulate: activations live in LDS as triples [-x, +x, 0] per column
 //    (fp16), so each nonzero is one LDS read and one fp32 add; zeros are never
@@ -48,17 +48,10 @@ constexpr int kSmallCols = 512;       // below this a lane (<= 448 symbols) may 
 // LDS: the decode tables are static arrays (compile-time addresses fold into
 // instruction offsets); accumulators and activations are dynamic LDS.
 struct __align__(16) LdsTables {
-  uint32_t bases[kMaxClasses + 4];    // first codeword of each class
-  uint32_t ctab[kMaxClasses];         // class words (the kernel keeps them in a VGPR)
-  uint32_t post[kPostEntries + 1];
-  uint8_t cls[65536];                 // 4 * class of every codeword
+  uint32_t tab[kTabEntries];          // the image's decode table
 };
-// bases..cls are one contiguous copy of the image's cls_base..cls
-static_assert(offsetof(DictImage, cls) - offsetof(DictImage, cls_base) ==
-              offsetof(LdsTables, cls) - offsetof(LdsTables, bases), "image and LDS layouts agree");
-static_assert(offsetof(DictImage, cls_base) % 16 == 0 && offsetof(LdsTables, bases) % 16 == 0, "16B copies");
-constexpr uint32_t kImageCopyU4 =
-    (uint32_t)((offsetof(DictImage, cls) - offsetof(DictImage, cls_base) + 65536) / 16);
+static_assert(offsetof(DictImage, tab) % 16 == 0, "16B copies");
+constexpr uint32_t kImageCopyU4 = kTabEntries / 4;
 constexpr uint32_t kLdsFixed = (uint32_t)sizeof(LdsTables);
 static_assert(kLdsFixed % 16 == 0, "align");
 __shared__ LdsTables g_tab;
@@ -376,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void stage_tables_dma(const DictImage* __restrict__ im) {
-  const uint4* src = (const uint4*)im->cls_base;
-  uint4* dst = (uint4*)g_tab.bases;
+  const uint4* src = (const uint4*)im->tab;
+  uint4* dst = (uint4*)g_tab.tab;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) return;
   for (uint32_t q = wave - 1; q * 64 < kImageCopyU4; q += kFWaves - 1) {
@@ -504,39 +497,36 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
   return r;
 }
 
+// Decode-table index of codeword c for split H: c itself below H, else the
+// codeword's group of 8 sign variants stored after H (c - H wraps to a huge
+// value below H, so the minimum picks c).
+__device__ __forceinline__ uint32_t table_index(uint32_t c, uint32_t split) {
+  return min(c, split + ((c - split) >> 3));
+}
+// 2 * bit i of the sign index d & 7 into byte i (+2: the +x slot of the triple).
+__device__ __forceinline__ uint32_t sign_spread(uint32_t d) { return ((d & 7u) * 0x8102u) & 0x20202u; }
+
 // One block of SBM_BLOCK codewords, kK per lane.
 template <int TC, bool SMALL>
 __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
-                              uint32_t ctab_v) {
+                              uint32_t split) {
   const int lane = threadIdx.x & 63;
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
-  uint32_t c[kK], kk[kK];
+  uint32_t c[kK];
 #pragma unroll
   for (int j = 0; j < kK; ++j) c[j] = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-  // phase A: class of every codeword (LDS byte = 4 * class)
+  // one table word per codeword: nonzero slots and 6 * run length, signs of
+  // the 3-nonzero groups added back from the codeword's low bits
+  uint32_t slots[kK], ls[kK];
 #pragma unroll
-  for (int j = 0; j < kK; ++j) kk[j] = g_tab.cls[c[j]];
-  // phase B: class words, lane k of ctab_v holding class k's (a permute,
-  // which has no LDS bank conflicts)
-  uint32_t ca[kK];
-#pragma unroll
-  for (int j = 0; j < kK; ++j) ca[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)kk[j], (int)ctab_v);
-  // phase C: nonzero positions, signs, run lengths
-  uint32_t slots[kK], ls[kK], sp[kK];
+  for (int j = 0; j < kK; ++j) slots[j] = g_tab.tab[table_index(c[j], split)];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    // c + K(k) taken modulo 2^17 straight from the class word: the bits the
-    // word holds above K only reach bit 17 and up, and c + K < 2^15
-    const uint32_t off = c[j] + ca[j];
-    const uint32_t pidx = __builtin_amdgcn_ubfe(off, (ca[j] >> 17) & 3u, 14);
-    sp[j] = ((off & 7u) * 0x8102u) & 0x20202u;           // sign bit i -> +2 in byte i
-    slots[j] = g_tab.post[pidx];
+    slots[j] += sign_spread(c[j] - split);
     ls[j] = tot;
-    tot += ca[j] >> 24;
+    tot += slots[j] >> 24;
   }
-#pragma unroll
-  for (int j = 0; j < kK; ++j) slots[j] += sp[j];
   const uint32_t excl = wave_incl_scan(tot) - tot;
   const uint32_t pl = 6u * raw.bst + excl;   // lane start, bytes
   float* racc = (float*)(smem + a.lds_racc);
@@ -840,10 +830,10 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
-                                                 const BlockCodes& raw, uint32_t ctab_v) {
-  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, ctab_v);
-  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, ctab_v);
-  else process_block<4, SMALL>(a, ch, smem, raw, ctab_v);
+                                                 const BlockCodes& raw, uint32_t split) {
+  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, split);
+  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, split);
+  else process_block<4, SMALL>(a, ch, smem, raw, split);
 }
 
 // ------------------------------------------------------------ dense-tile MFMA path
@@ -903,7 +893,7 @@ __device__ __forceinline__ half8_t mfma_b_frag(const FusedArgs& a, int32_t tok, 
 
 template <bool VEC>
 __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const Chunk& ch,
-                           uint32_t ctab_v) {
+                           uint32_t split) {
   const int32_t R = a.mfma_rows;
   const uint32_t wpr = ((uint32_t)a.cols + 15u) / 16u;
   const MfmaLds L = mfma_lds(R, a.cols);
@@ -972,22 +962,16 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
     uint32_t done6 = 0;                        // 6 * columns of the tile decoded by earlier passes
     for (uint32_t cb = c_lo; cb < c_hi; cb += (uint32_t)kFThreads * kK) {
       const uint32_t i0 = cb + threadIdx.x * kK;
-      uint32_t off[kK], cw[kK];
+      uint32_t sw[kK];
       uint32_t tot = 0;
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
         const uint32_t idx = i0 + j;
-        off[j] = idx < c_hi ? (uint32_t)a.codes[ch.code_base + idx] : 0u;
+        const uint32_t c = idx < c_hi ? (uint32_t)a.codes[ch.code_base + idx] : 0u;
+        sw[j] = g_tab.tab[table_index(c, split)] + sign_spread(c - split);
       }
-      uint32_t kk[kK];
 #pragma unroll
-      for (int j = 0; j < kK; ++j) kk[j] = g_tab.cls[off[j]];
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        cw[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)kk[j], (int)ctab_v);
-        off[j] += (uint32_t)(((int32_t)(cw[j] << 15)) >> 15);
-        tot += i0 + j < c_hi ? (cw[j] >> 24) : 0u;
-      }
+      for (int j = 0; j < kK; ++j) tot += i0 + j < c_hi ? (sw[j] >> 24) : 0u;
       const uint32_t incl = wave_incl_scan(tot);
       if (lane == 63) scan[wave] = incl;
       __syncthreads();
@@ -1002,11 +986,9 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
         if (i0 + j < c_hi) {
-          uint32_t sw = g_tab.post[off[j] >> ((cw[j] >> 17) & 3u)];
-          sw += ((off[j] & 7u) * 0x8102u) & 0x20202u;
 #pragma unroll
           for (int i = 0; i < 3; ++i) {
-            const uint32_t byte = (sw >> (8 * i)) & 0xFFu;
+            const uint32_t byte = (sw[j] >> (8 * i)) & 0xFFu;
             const uint32_t p6i = 6u * ((byte * 171u) >> 10);          // 6 * position in the run
             const uint32_t k = byte - p6i;                            // 0: -1, 2: +1, 4: zero
             if (k != 4u) {
@@ -1018,7 +1000,7 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
                 atomicOr(&W[(uint32_t)rr * wpr + (col >> 4)], (k == 0u ? 1u : 2u) << ((col & 15u) * 2u));
             }
           }
-          p6 += cw[j] >> 24;
+          p6 += sw[j] >> 24;
         }
       }
       done6 += all;
@@ -1215,7 +1197,7 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 // default instance has no call in its loop, which keeps its registers unspilled.
 template <bool SMALL, bool MFMA>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
-                          uint64_t g0, uint64_t g1, uint32_t ctab_v) {
+                          uint64_t g0, uint64_t g1, uint32_t split) {
   float* racc = (float*)(smem + a.lds_racc);
   // the image copy issued at kernel entry is waited for just before the
   // barrier that follows the first activation staging (or inside the first
@@ -1237,8 +1219,8 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       if (MFMA && ch.mfma) {
         // dense tiles overwrite the accumulators and the staged activations
         if (ch.ok) {
-          if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, ctab_v);
-          else mfma_chunk<false>(a, smem, perm, ch, ctab_v);
+          if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, split);
+          else mfma_chunk<false>(a, smem, perm, ch, split);
         }
         const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;
         for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
@@ -1260,7 +1242,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         const Slot cur = r0;
         r0 = r1;
         r1 = grab(a, nseq, nch);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, ctab_v);
+        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, split);
       }
       // This wave has no more blocks of the chunk.  While the others finish,
       // request the row scales of this thread's epilogue rows and, when the
@@ -1566,11 +1548,12 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   // known), so waiting for the ids never waits for the image.
   const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
   const int32_t my_id = a.ids[tq];
-  const uint4 hdr = *(const uint4*)a.image;       // magic, version, n_classes
+  const uint4 hdr = *(const uint4*)a.image;       // magic, version, split, n_tab
   stage_tables_dma(a.image);
-  const uint32_t ctab_v = a.image->ctab[threadIdx.x & 63];   // lane k: class k's word
-  const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z != 0 &&
-                        hdr.z <= (uint32_t)kMaxClasses;
+  // the table indexes stay below n_tab <= kTabEntries for every codeword
+  const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
+                        hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
+  const uint32_t split = hdr.z;
   const int32_t* perm;
   const uint4* items;
   uint64_t g0, g1;
@@ -1598,8 +1581,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, ctab_v);
-  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, ctab_v);
+  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, split);
+  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, split);
 }
 
 // ------------------------------------------------------------ host entries

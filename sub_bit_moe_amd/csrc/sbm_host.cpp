@@ -65,8 +65,6 @@ static double binom(int n, int k) {
   return r;
 }
 
-static uint32_t ubinom(int n, int k) { return (uint32_t)std::llround(binom(n, k)); }
-
 // Next n-subset of {0..L-1} in colexicographic order; false after the last.
 static bool colex_next(std::vector<int>& p, int L) {
   const int n = (int)p.size();
@@ -148,74 +146,61 @@ uint64_t checksum(const uint32_t* words) {
 }
 
 // ------------------------------------------------------------ decode image
+static uint32_t spread3(uint32_t sg) { return ((sg & 7u) * 0x8102u) & 0x20202u; }
+
 int dict_image(const uint32_t* words, void* out, size_t bytes) {
   if (!words || !out) return fail(SBM_EINVAL, "null pointer");
   if (bytes < sizeof(DictImage)) return fail(SBM_ENOSPACE, "image buffer too small");
+  // the word of every codeword: slot bytes and 6 L; nonzero count and signs
+  std::vector<uint32_t> word(SBM_DICT_ENTRIES);
+  std::vector<uint8_t> nnz(SBM_DICT_ENTRIES), sidx(SBM_DICT_ENTRIES);
+  uint8_t sym[SBM_MAX_RUN];
+  for (uint32_t c = 0; c < SBM_DICT_ENTRIES; ++c) {
+    const int L = unpack(words[2 * c], words[2 * c + 1], sym);
+    if (L < 0) return fail(SBM_EDICT, "entry %u: malformed pair count or symbols", c);
+    uint32_t w = (uint32_t)(6 * L) << 24, n = 0, sg = 0;
+    for (int p = 0; p < L; ++p)
+      if (sym[p]) {
+        if (n >= 3) return fail(SBM_EDICT, "entry %u has more than 3 nonzeros", c);
+        if (sym[p] == 2) sg |= 1u << n;
+        w |= (uint32_t)(6 * p + (sym[p] == 2 ? 2 : 0)) << (8 * n);
+        ++n;
+      }
+    for (uint32_t i = n; i < 3; ++i) w |= 4u << (8 * i);
+    word[c] = w;
+    nnz[c] = (uint8_t)n;
+    sidx[c] = (uint8_t)sg;
+  }
+  // split: the first codeword from which on every entry has 3 nonzeros and
+  // groups of 8 align (same positions and length, sign index = (c - H) & 7)
+  uint32_t H = SBM_DICT_ENTRIES;
+  while (H > 0 && nnz[H - 1] == 3) --H;
+  auto aligned = [&](uint32_t h) {
+    for (uint32_t c = h; c < SBM_DICT_ENTRIES; ++c) {
+      const uint32_t s = (c - h) & 7u, c0 = c - s;
+      if (sidx[c] != s || (word[c] - spread3(s)) != word[c0]) return false;
+    }
+    return true;
+  };
+  while (H < SBM_DICT_ENTRIES && !aligned(H)) ++H;
+  const uint32_t n_tab = H + (SBM_DICT_ENTRIES - H + 7) / 8;
+  if (n_tab > kTabEntries)
+    return fail(SBM_EDICT, "dictionary needs %u decode-table entries (at most %u): fewer entries with 3 "
+                           "nonzeros in aligned sign groups than the fused kernel assumes", n_tab, kTabEntries);
   DictImage* im = (DictImage*)out;
   std::memset(im, 0, sizeof(DictImage));
   im->magic = kImageMagic;
   im->version = kImageVersion;
+  im->split = H;
+  im->n_tab = n_tab;
   im->checksum = checksum(words);
-  // position table: colex combos of {0..27}, segments for n = 0..3
-  const uint32_t seg[4] = {kPostSeg0, kPostSeg1, kPostSeg2, kPostSeg3};
-  for (int n = 0; n <= 3; ++n) {
-    std::vector<int> pos(n);
-    for (int i = 0; i < n; ++i) pos[i] = i;
-    uint32_t m = 0;
-    bool more = true;
-    while (more) {
-      uint32_t e = 0;
-      const uint32_t pidx = seg[n] + m;
-      for (int i = 0; i < 3; ++i) {
-        // 4 = the zero element; for i >= n bit i of the shifted offset is bit
-        // (i - n) of pidx, which the sign spread adds back as 2*bit.
-        const uint32_t b = i < n ? (uint32_t)(6 * pos[i]) : 4u - 2u * ((pidx >> (i - n)) & 1u);
-        e |= b << (8 * i);
-      }
-      im->postab[seg[n] + m] = e;
-      ++m;
-      more = colex_next(pos, 28);
-    }
-    if (m != ubinom(28, n)) return fail(SBM_EDICT, "internal: combo count");
-  }
-  // classes: contiguous runs of (L, n); in-class rank = colex * 2^n + sign index
-  uint8_t s[SBM_MAX_RUN];
-  int cur_L = -1, cur_n = -1;
-  uint32_t base = 0;
-  uint32_t k = 0;
-  std::vector<int> seen(32 * 4, 0);
+  for (uint32_t c = 0; c < H; ++c) im->tab[c] = word[c] - spread3(c - H);
+  for (uint32_t c = H; c < SBM_DICT_ENTRIES; c += 8) im->tab[H + (c - H) / 8] = word[c];
+  // the kernel's two steps must rebuild every codeword's word
   for (uint32_t c = 0; c < SBM_DICT_ENTRIES; ++c) {
-    const int L = unpack(words[2 * c], words[2 * c + 1], s);
-    if (L < 0) return fail(SBM_EDICT, "entry %u: malformed pair count or symbols", c);
-    int n = 0, p[4];
-    uint32_t sidx = 0;
-    for (int i = 0; i < L; ++i)
-      if (s[i]) {
-        if (n >= 3) return fail(SBM_EDICT, "entry %u has more than 3 nonzeros", c);
-        if (s[i] == 2) sidx |= 1u << n;
-        p[n++] = i;
-      }
-    if (L != cur_L || n != cur_n) {
-      if (seen[L * 4 + n]) return fail(SBM_EDICT, "class (%d,%d) is not contiguous", L, n);
-      seen[L * 4 + n] = 1;
-      if (k >= kMaxClasses) return fail(SBM_EDICT, "too many classes");
-      cur_L = L;
-      cur_n = n;
-      base = c;
-      im->cls_base[k] = c;
-      const int32_t K = (int32_t)(seg[n] << n) - (int32_t)c;
-      im->ctab[k] = ((uint32_t)K & 0x1FFFFu) | ((uint32_t)n << 17) | ((uint32_t)(6 * L) << 24);
-      ++k;
-    }
-    uint32_t colex = 0;
-    for (int i = 0; i < n; ++i) colex += ubinom(p[i], i + 1);
-    if (c - base != colex * (1u << n) + sidx)
-      return fail(SBM_EDICT, "entry %u is not in canonical in-class order", c);
+    const uint32_t d = c - H, idx = std::min(c, H + (d >> 3));
+    if (im->tab[idx] + spread3(d) != word[c]) return fail(SBM_EDICT, "internal: entry %u does not rebuild", c);
   }
-  im->n_classes = k;
-  im->cls_base[k] = SBM_DICT_ENTRIES;
-  for (uint32_t j = 0; j < k; ++j)
-    for (uint32_t c = im->cls_base[j]; c < im->cls_base[j + 1]; ++c) im->cls[c] = (uint8_t)(4u * j);
   return SBM_OK;
 }
 

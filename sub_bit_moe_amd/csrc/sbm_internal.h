@@ -11,45 +11,34 @@
 namespace sbm {
 
 constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
-constexpr uint32_t kImageVersion = 4;
-constexpr int kMaxClasses = 64;
+constexpr uint32_t kImageVersion = 5;
+constexpr uint32_t kTabEntries = 15360;        // decode-table capacity: 60 KB
 
-// Position table segments: colex-ordered n-subsets of {0..27} for n = 0..3.
-// For a class of length L every rank below C(L, n) names a subset of {0..L-1},
-// because colex order lists the subsets of a smaller ground set first.
-constexpr uint32_t kPostSeg0 = 0;
-constexpr uint32_t kPostSeg1 = 1;
-constexpr uint32_t kPostSeg2 = 29;
-constexpr uint32_t kPostSeg3 = 407;
-constexpr uint32_t kPostEntries = 3683;
-
-// Compact decode image of a canonical dictionary (device copy read by the
-// fused kernel).  Codeword c of class k (cls_base[k] <= c < cls_base[k+1],
-// n(k) nonzeros, length L(k)):
-//   off   = c + K(k),  K(k) = seg(n) * 2^n - cls_base[k]
-//   pidx  = off >> n                    (seg(n) + colex rank of the positions)
-//   sg    = off & 7                     (bit i < n set: nonzero i is positive)
-//   slots = postab[pidx] + spread(sg)
-// Adding a multiple of 2^n keeps the sign bits of the in-class offset and
-// moves the colex rank into the class's position-table segment.  spread puts
-// 2*bit i of sg into byte i.  Byte i of a slot word is the byte offset
-// 6*p_i + 2*positive of nonzero i in the [-x, +x, 0] triple layout, or 4 (the
-// zero) when i >= n.  For i >= n, bit i of off is bit i - n of pidx, so those
-// postab bytes are stored as 4 - 2*bit_{i-n}(pidx), which the spread brings
-// back to 4.
-// ctab[k] = (K(k) & 0x1FFFF) | n << 17 | (6*L) << 24   (K: 17-bit two's complement)
-// cls[c]  = 4*k                                          (byte offset of ctab[k])
+// Decode image of a dictionary (device copy read by the fused kernel): one
+// 32-bit word per codeword says everything the kernel needs,
+//   byte i (i = 0, 1, 2): 6*p_i + 2*[nonzero i is positive] for the i-th
+//                         nonzero at run position p_i, or 4 when the entry has
+//                         fewer than i+1 nonzeros (the byte offsets of the
+//                         activation triple [-x, +x, 0] of a column);
+//   byte 3:               6*L for a run of L symbols.
+// The words are stored compressed.  From split H on every entry has 3
+// nonzeros, and entries come in aligned groups of 8 that share positions and
+// length and differ only in their signs: entry H + 8g + s has sign bit i of s
+// for nonzero i (the canonical in-class order, colex rank * 8 + sign index).
+// A group is stored once, without signs; entries below H are stored one by
+// one.  With d = c - H (mod 2^32):
+//   idx(c)  = min(c, H + (d >> 3))      (d >> 3 is huge when c < H)
+//   word(c) = tab[idx(c)] + spread(d & 7),   spread(s) = ((s * 0x8102) & 0x20202)
+// (spread puts 2 * bit i of s into byte i).  Entries below H are stored as
+// word(c) - spread(d & 7), so the same two steps rebuild every codeword.
 struct DictImage {
   uint32_t magic;
   uint32_t version;
-  uint32_t n_classes;
-  uint32_t reserved0;
+  uint32_t split;        // H
+  uint32_t n_tab;        // used entries of tab: H + ceil((65536 - H) / 8)
   uint64_t checksum;
   uint64_t reserved1;
-  uint32_t cls_base[kMaxClasses + 4];
-  uint32_t ctab[kMaxClasses];
-  uint32_t postab[kPostEntries + 1];
-  uint8_t cls[SBM_DICT_ENTRIES];    // 4 * class of every codeword
+  uint32_t tab[kTabEntries];
 };
 
 int fail(int status, const char* fmt, ...);

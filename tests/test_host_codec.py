@@ -115,16 +115,8 @@ def test_validate_stream_detects_corruption(odict):
 
 def _image_fields(img):
     hdr = np.frombuffer(img[:32].tobytes(), np.uint32)
-    n_classes = int(hdr[2])
-    off = 32
-    cls_base = np.frombuffer(img[off:off + 68 * 4].tobytes(), np.uint32)
-    off += 68 * 4
-    ctab = np.frombuffer(img[off:off + 64 * 4].tobytes(), np.uint32)
-    off += 64 * 4
-    post = np.frombuffer(img[off:off + 3684 * 4].tobytes(), np.uint32)
-    off += 3684 * 4
-    cls = np.frombuffer(img[off:off + 65536].tobytes(), np.uint8)
-    return n_classes, cls_base, ctab, post, cls
+    tab = np.frombuffer(img[32:].tobytes(), np.uint32)
+    return int(hdr[1]), int(hdr[2]), int(hdr[3]), tab
 
 
 def test_decode_image_reproduces_every_codeword(odict):
@@ -132,23 +124,19 @@ def test_decode_image_reproduces_every_codeword(odict):
     CPU and compare run length, nonzero positions and signs with the oracle."""
     img = api.dict_image(odict["words"])
     assert img.size == N.lib().sbm_dict_image_bytes()
-    n_classes, cls_base, ctab, post, cls = _image_fields(img)
-    assert n_classes == 54
-    k = np.zeros(65536, np.int64)
-    for j in range(n_classes):
-        k[cls_base[j]:cls_base[j + 1]] = j
-    assert np.array_equal(cls.astype(np.int64), 4 * k)
-    c = np.arange(65536, dtype=np.int64)
-    a = ctab[k].astype(np.int64)
-    K = (a & 0x1FFFF) - ((a & 0x10000) << 1)          # 17-bit two's complement
-    off = c + K
-    assert off.min() >= 0
-    pidx = off >> ((a >> 17) & 3)
-    sg = off & 7
-    e = post[pidx].astype(np.int64)
-    slots = e + ((sg * 0x8102) & 0x20202)
-    L = ((a >> 24) & 0xFF) // 6
-    assert np.array_equal(L, odict["lens"])
+    version, H, n_tab, tab = _image_fields(img)
+    assert version == 5
+    assert n_tab == H + (65536 - H + 7) // 8 and n_tab <= tab.size
+    # every codeword from the split on has 3 nonzeros, and the one before not
+    nnz = (odict["sym28"] != 0).sum(axis=1)
+    assert (nnz[H:] == 3).all() and nnz[H - 1] < 3
+    c = np.arange(65536, dtype=np.uint32)
+    d = c - np.uint32(H)                                  # mod 2^32
+    idx = np.minimum(c, np.uint32(H) + (d >> np.uint32(3)))
+    slots = tab[idx] + ((d & np.uint32(7)) * np.uint32(0x8102) & np.uint32(0x20202))
+    L = (slots >> np.uint32(24)).astype(np.int64)
+    assert (L % 6 == 0).all()
+    assert np.array_equal(L // 6, odict["lens"])
     sym28 = odict["sym28"]
     for cw in range(65536):
         exp = np.zeros(28, np.uint8)
