@@ -93,10 +93,14 @@ int sbm_build_dictionary(double p0, uint32_t* out_words, uint64_t* out_checksum)
 /* FNV-1a 64 of the 512 KB packed table (the [M8.5] 0x08B codebook checksum). */
 int sbm_dictionary_checksum(const uint32_t* words, uint64_t* out_checksum);
 
-/* Compact decode image for the fused kernel, derived from a canonical
- * dictionary (every entry has at most 3 nonzeros; classes contiguous; in-class
- * order as above).  Host in, host out; the caller uploads the image to the
- * device.  Returns SBM_EDICT if the dictionary does not have that structure. */
+/* Compact decode image for the fused kernel (one 32-bit word per codeword:
+ * nonzero positions, signs and run length), derived from a dictionary in
+ * which every entry has at most 3 nonzeros and, from some split codeword H
+ * on, every entry has exactly 3, in aligned groups of 8 that differ only in
+ * their signs (sign bit i of (c - H) & 7 for nonzero i: the canonical order
+ * above), with H + (65536 - H) / 8 at most 15360 table words.  Host in, host
+ * out; the caller uploads the image to the device.  Returns SBM_EDICT if the
+ * dictionary does not have that structure. */
 size_t sbm_dict_image_bytes(void);
 int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes);
 
