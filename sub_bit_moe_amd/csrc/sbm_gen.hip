@@ -76,7 +76,6 @@ __global__ __launch_bounds__(256) void gen_walk(GenArgs g) {
   }
   int32_t cur = kRoot;
   int32_t start = 0;    // column where the current codeword starts
-  int32_t L = 0;
   for (int32_t j = 0; j < g.cols; j += 4) {
     const uint64_t h = splitmix_at(key, (uint64_t)r * w + (uint64_t)(j / 4) + 1);
 #pragma unroll
@@ -91,7 +90,6 @@ __global__ __launch_bounds__(256) void gen_walk(GenArgs g) {
       const int32_t nx = g.trie[(int64_t)cur * 9 + pr];
       if (nx >= 0) {
         cur = nx;
-        L += 2;
       } else {
         if (WRITE) {
           const uint32_t idx = off0 + n;
@@ -101,7 +99,6 @@ __global__ __launch_bounds__(256) void gen_walk(GenArgs g) {
         ++n;
         cur = g.trie[(int64_t)kRoot * 9 + pr];
         start = col;
-        L = 2;
       }
     }
   }

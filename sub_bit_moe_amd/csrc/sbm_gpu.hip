@@ -44,6 +44,10 @@ constexpr int kFWaves = kFThreads / 64;
 constexpr int kK = 16;                // codewords per lane per block
 static_assert(kK * 64 == SBM_BLOCK, "block = 64 lanes x kK codewords");
 constexpr int kXPad = 48;             // columns past the row end: > 255/6, any slot byte stays inside
+// Wide rows (cols >= kSmallCols): the first kXWrap columns are staged again
+// after the row end, so a lane that runs into the next row (at most 448
+// columns, plus any slot byte) reads that row's activations at the same base.
+constexpr int kXWrap = 512;
 constexpr int kSmallCols = 512;       // below this a lane (<= 448 symbols) may span several rows
 // LDS: the decode tables are static arrays (compile-time addresses fold into
 // instruction offsets); accumulators and activations are dynamic LDS.
@@ -384,12 +388,14 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 // acc += (float)x  with x the low / high fp16 half of v: one fp32 rounding.
 __device__ __forceinline__ float acc_lo(float acc, uint32_t v) {
-  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(v));
-  return acc;
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(v), "v"(acc));
+  return r;
 }
 __device__ __forceinline__ float acc_hi(float acc, uint32_t v) {
-  asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(v));
-  return acc;
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(v), "v"(acc));
+  return r;
 }
 
 // The x values of TC tokens at one slot byte address a (TC=1: fp16 in the low
@@ -497,19 +503,23 @@ __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t co
   return r;
 }
 
-// Decode-table index of codeword c for split H: c itself below H, else the
-// codeword's group of 8 sign variants stored after H (c - H wraps to a huge
-// value below H, so the minimum picks c).
-__device__ __forceinline__ uint32_t table_index(uint32_t c, uint32_t split) {
-  return min(c, split + ((c - split) >> 3));
+// Decode-table index of codeword c for split H, given split7 = 7H: c itself
+// below H, else H + (c - H) / 8, the codeword's group of 8 sign variants.
+// (c + 7H) / 8 equals H + (c - H) / 8 from H on and is at least c below H,
+// so one minimum covers both.
+__device__ __forceinline__ uint32_t table_index(uint32_t c, uint32_t split7) {
+  return min(c, (c + split7) >> 3);
 }
-// 2 * bit i of the sign index d & 7 into byte i (+2: the +x slot of the triple).
-__device__ __forceinline__ uint32_t sign_spread(uint32_t d) { return ((d & 7u) * 0x8102u) & 0x20202u; }
+// 2 * bit i of the sign index (c - H) & 7 = (c + 7H) & 7 into byte i (+2: the
+// +x slot of the triple).
+__device__ __forceinline__ uint32_t sign_spread(uint32_t c, uint32_t split7) {
+  return (((c + split7) & 7u) * 0x8102u) & 0x20202u;
+}
 
 // One block of SBM_BLOCK codewords, kK per lane.
 template <int TC, bool SMALL>
 __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
-                              uint32_t split) {
+                              uint32_t split7) {
   const int lane = threadIdx.x & 63;
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
   uint32_t c[kK];
@@ -519,11 +529,11 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
   // the 3-nonzero groups added back from the codeword's low bits
   uint32_t slots[kK], ls[kK];
 #pragma unroll
-  for (int j = 0; j < kK; ++j) slots[j] = g_tab.tab[table_index(c[j], split)];
+  for (int j = 0; j < kK; ++j) slots[j] = g_tab.tab[table_index(c[j], split7)];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    slots[j] += sign_spread(c[j] - split);
+    slots[j] += sign_spread(c[j], split7);
     ls[j] = tot;
     tot += slots[j] >> 24;
   }
@@ -535,8 +545,7 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
     const uint32_t rl = div_magic_dev(pl, a.magic_m, a.magic_s);
     const uint32_t colB = pl - rl * a.colsB;
     const uint32_t thr = a.colsB - colB;
-    const uint32_t base0 = colB, base1 = colB - a.colsB;   // row rl / row rl+1 (wraps mod 2^32)
-    const uint32_t base0x = base0 + a.lds_x, base1x = base1 + a.lds_x;
+    const uint32_t basex = colB + a.lds_x;    // row rl+1 continues into the wrap copy
     float acc[TC], snap[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) { acc[t] = 0.f; snap[t] = 0.f; }
@@ -553,12 +562,12 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
         const uint32_t s = slots[j];
         if constexpr (TC == 1) {
           // one add per slot: the byte operand is taken straight from s
-          const uint32_t bx = (ls[j] < thr ? base0x : base1x) + ls[j];   // codeword j starts in row rl?
+          const uint32_t bx = basex + ls[j];
           xv[jj][0] = lds_x<TC>(smem, bx + (s & 0xFFu));
           xv[jj][1] = lds_x<TC>(smem, bx + ((s >> 8) & 0xFFu));
           xv[jj][2] = lds_x<TC>(smem, bx + ((s >> 16) & 0xFFu));
         } else {
-          const uint32_t base = (ls[j] < thr ? base0 : base1) + ls[j];
+          const uint32_t base = colB + ls[j];
           xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
           xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
           xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
@@ -658,21 +667,33 @@ __device__ __forceinline__ bool x_vec(const FusedArgs& a) {
   return (a.cols % 8) == 0 && ((uintptr_t)a.x & 15u) == 0;
 }
 
-// fp16 pairs of 8 columns of TC token rows (zero past cols or for tok < 0).
+// Wide rows stage a wrap copy of their first columns after the row end.
+__device__ __forceinline__ bool x_wrap(const FusedArgs& a) { return a.cols >= kSmallCols; }
+
+// Source column of staged column c: c itself, or c - cols in the wrap copy
+// (>= cols when there is none, i.e. zero).
+__device__ __forceinline__ int32_t x_src(const FusedArgs& a, int32_t c, bool wrap) {
+  return (wrap && c >= a.cols) ? c - a.cols : c;
+}
+
+// fp16 pairs of staged columns c0 .. c0+7 of TC token rows (zero past the
+// staged content or for tok < 0).
 template <int TC>
 __device__ __forceinline__ void load_x_group(const FusedArgs& a, const int32_t (&tok)[TC], int32_t c0, bool vec,
-                                             uint32_t (&p)[TC][4]) {
+                                             bool wrap, uint32_t (&p)[TC][4]) {
+  const int32_t s0 = x_src(a, c0, wrap);
 #pragma unroll
   for (int t = 0; t < TC; ++t) {
-    if (tok[t] >= 0 && c0 + 8 <= a.cols && vec) {
-      const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + c0);
+    if (tok[t] >= 0 && s0 + 8 <= a.cols && vec) {
+      const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + s0);
       p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
     } else {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        const int32_t sl = x_src(a, c0 + 2 * m, wrap), sh = x_src(a, c0 + 2 * m + 1, wrap);
         uint32_t lo = 0, hi = 0;
-        if (tok[t] >= 0 && c0 + 2 * m < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m];
-        if (tok[t] >= 0 && c0 + 2 * m + 1 < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + c0 + 2 * m + 1];
+        if (tok[t] >= 0 && sl < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + sl];
+        if (tok[t] >= 0 && sh < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + sh];
         p[t][m] = lo | (hi << 16);
       }
     }
@@ -733,11 +754,12 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
 #pragma unroll
   for (int j = 0; j < 4 / TC; ++j) {
     const int32_t c0 = 8 * ((int32_t)threadIdx.x + j * kFThreads);
+    const int32_t s0 = x_src(a, c0, x_wrap(a));
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
       const int32_t tok = (uint32_t)t < nt ? perm[tb + t] : -1;
-      r.v[j * TC + t] = (tok >= 0 && c0 + 8 <= a.cols && c0 < 8 * n8)
-                            ? *(const uint4*)(a.x + (int64_t)tok * a.cols + c0) : make_uint4(0, 0, 0, 0);
+      r.v[j * TC + t] = (tok >= 0 && s0 + 8 <= a.cols && c0 < 8 * n8)
+                            ? *(const uint4*)(a.x + (int64_t)tok * a.cols + s0) : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -753,7 +775,7 @@ __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* sm
     for (int t = 0; t < TC; ++t) ss[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4 / TC; ++j) {
-      if ((int32_t)threadIdx.x + j * kFThreads < n8) {
+      if (8 * ((int32_t)threadIdx.x + j * kFThreads) < a.cols) {     // the row itself, not its wrap copy
 #pragma unroll
         for (int t = 0; t < TC; ++t) {
           const uint4 v = r.v[j * TC + t];
@@ -803,9 +825,9 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
     float ss[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) ss[t] = 0.f;
-    for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
+    for (int32_t i = threadIdx.x; 8 * i < a.cols; i += kFThreads) {     // the row itself, not its wrap copy
       uint32_t p[TC][4];
-      load_x_group<TC>(a, tok, 8 * i, vec, p);
+      load_x_group<TC>(a, tok, 8 * i, vec, false, p);
 #pragma unroll
       for (int t = 0; t < TC; ++t)
 #pragma unroll
@@ -815,7 +837,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
   }
   for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
     uint32_t p[TC][4];
-    load_x_group<TC>(a, tok, 8 * i, vec, p);
+    load_x_group<TC>(a, tok, 8 * i, vec, x_wrap(a), p);
     if (rms) {
 #pragma unroll
       for (int t = 0; t < TC; ++t)
@@ -830,10 +852,10 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
-                                                 const BlockCodes& raw, uint32_t split) {
-  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, split);
-  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, split);
-  else process_block<4, SMALL>(a, ch, smem, raw, split);
+                                                 const BlockCodes& raw, uint32_t split7) {
+  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, split7);
+  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, split7);
+  else process_block<4, SMALL>(a, ch, smem, raw, split7);
 }
 
 // ------------------------------------------------------------ dense-tile MFMA path
@@ -893,7 +915,7 @@ __device__ __forceinline__ half8_t mfma_b_frag(const FusedArgs& a, int32_t tok, 
 
 template <bool VEC>
 __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const Chunk& ch,
-                           uint32_t split) {
+                           uint32_t split7) {
   const int32_t R = a.mfma_rows;
   const uint32_t wpr = ((uint32_t)a.cols + 15u) / 16u;
   const MfmaLds L = mfma_lds(R, a.cols);
@@ -968,7 +990,7 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
       for (int j = 0; j < kK; ++j) {
         const uint32_t idx = i0 + j;
         const uint32_t c = idx < c_hi ? (uint32_t)a.codes[ch.code_base + idx] : 0u;
-        sw[j] = g_tab.tab[table_index(c, split)] + sign_spread(c - split);
+        sw[j] = g_tab.tab[table_index(c, split7)] + sign_spread(c, split7);
       }
 #pragma unroll
       for (int j = 0; j < kK; ++j) tot += i0 + j < c_hi ? (sw[j] >> 24) : 0u;
@@ -1197,7 +1219,7 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 // default instance has no call in its loop, which keeps its registers unspilled.
 template <bool SMALL, bool MFMA>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
-                          uint64_t g0, uint64_t g1, uint32_t split) {
+                          uint64_t g0, uint64_t g1, uint32_t split7) {
   float* racc = (float*)(smem + a.lds_racc);
   // the image copy issued at kernel entry is waited for just before the
   // barrier that follows the first activation staging (or inside the first
@@ -1219,8 +1241,8 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       if (MFMA && ch.mfma) {
         // dense tiles overwrite the accumulators and the staged activations
         if (ch.ok) {
-          if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, split);
-          else mfma_chunk<false>(a, smem, perm, ch, split);
+          if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, split7);
+          else mfma_chunk<false>(a, smem, perm, ch, split7);
         }
         const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;
         for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
@@ -1242,7 +1264,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         const Slot cur = r0;
         r0 = r1;
         r1 = grab(a, nseq, nch);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, split);
+        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, split7);
       }
       // This wave has no more blocks of the chunk.  While the others finish,
       // request the row scales of this thread's epilogue rows and, when the
@@ -1553,7 +1575,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   // the table indexes stay below n_tab <= kTabEntries for every codeword
   const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
                         hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
-  const uint32_t split = hdr.z;
+  const uint32_t split7 = 7u * hdr.z;
   const int32_t* perm;
   const uint4* items;
   uint64_t g0, g1;
@@ -1581,8 +1603,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, split);
-  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, split);
+  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, split7);
+  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, split7);
 }
 
 // ------------------------------------------------------------ host entries
@@ -1635,7 +1657,7 @@ struct Plan {
   uint32_t lds_racc, lds_x, lds_total;
 };
 static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
-  p->xcols = (cols + kXPad + 7) / 8 * 8;
+  p->xcols = (cols + (cols >= kSmallCols ? kXWrap : kXPad) + 7) / 8 * 8;
   // prefer more tokens per item, then the longest row chunks that fit
   for (int tc : {4, 2, 1}) {
     const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);

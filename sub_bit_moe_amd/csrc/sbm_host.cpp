@@ -58,13 +58,6 @@ static std::vector<Class> ranked_classes(double p0) {
   return cs;
 }
 
-static double binom(int n, int k) {
-  if (k < 0 || k > n) return 0.0;
-  double r = 1.0;
-  for (int i = 1; i <= k; ++i) r = r * (n - k + i) / i;
-  return r;
-}
-
 // Next n-subset of {0..L-1} in colexicographic order; false after the last.
 static bool colex_next(std::vector<int>& p, int L) {
   const int n = (int)p.size();
@@ -194,12 +187,13 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
   im->split = H;
   im->n_tab = n_tab;
   im->checksum = checksum(words);
-  for (uint32_t c = 0; c < H; ++c) im->tab[c] = word[c] - spread3(c - H);
+  for (uint32_t c = 0; c < H; ++c) im->tab[c] = word[c] - spread3(c + 7 * H);
   for (uint32_t c = H; c < SBM_DICT_ENTRIES; c += 8) im->tab[H + (c - H) / 8] = word[c];
   // the kernel's two steps must rebuild every codeword's word
   for (uint32_t c = 0; c < SBM_DICT_ENTRIES; ++c) {
-    const uint32_t d = c - H, idx = std::min(c, H + (d >> 3));
-    if (im->tab[idx] + spread3(d) != word[c]) return fail(SBM_EDICT, "internal: entry %u does not rebuild", c);
+    const uint32_t e = c + 7 * H, idx = std::min(c, e >> 3);
+    if (idx >= n_tab || im->tab[idx] + spread3(e) != word[c])
+      return fail(SBM_EDICT, "internal: entry %u does not rebuild", c);
   }
   return SBM_OK;
 }

@@ -26,11 +26,12 @@ constexpr uint32_t kTabEntries = 15360;        // decode-table capacity: 60 KB
 // length and differ only in their signs: entry H + 8g + s has sign bit i of s
 // for nonzero i (the canonical in-class order, colex rank * 8 + sign index).
 // A group is stored once, without signs; entries below H are stored one by
-// one.  With d = c - H (mod 2^32):
-//   idx(c)  = min(c, H + (d >> 3))      (d >> 3 is huge when c < H)
-//   word(c) = tab[idx(c)] + spread(d & 7),   spread(s) = ((s * 0x8102) & 0x20202)
-// (spread puts 2 * bit i of s into byte i).  Entries below H are stored as
-// word(c) - spread(d & 7), so the same two steps rebuild every codeword.
+// one.  With e = c + 7H:
+//   idx(c)  = min(c, e >> 3)      (H + (c - H) / 8 from H on, at least c below)
+//   word(c) = tab[idx(c)] + spread(e & 7),   spread(s) = ((s * 0x8102) & 0x20202)
+// (e & 7 = (c - H) & 7; spread puts 2 * bit i of s into byte i).  Entries
+// below H are stored as word(c) - spread(e & 7), so the same two steps
+// rebuild every codeword.
 struct DictImage {
   uint32_t magic;
   uint32_t version;

@@ -131,9 +131,11 @@ def test_decode_image_reproduces_every_codeword(odict):
     nnz = (odict["sym28"] != 0).sum(axis=1)
     assert (nnz[H:] == 3).all() and nnz[H - 1] < 3
     c = np.arange(65536, dtype=np.uint32)
-    d = c - np.uint32(H)                                  # mod 2^32
-    idx = np.minimum(c, np.uint32(H) + (d >> np.uint32(3)))
-    slots = tab[idx] + ((d & np.uint32(7)) * np.uint32(0x8102) & np.uint32(0x20202))
+    e = c + np.uint32(7 * H)
+    idx = np.minimum(c, e >> np.uint32(3))
+    assert idx.max() < n_tab
+    assert np.array_equal(idx[H:], H + (c[H:] - H) // 8) and np.array_equal(idx[:H], c[:H])
+    slots = tab[idx] + ((e & np.uint32(7)) * np.uint32(0x8102) & np.uint32(0x20202))
     L = (slots >> np.uint32(24)).astype(np.int64)
     assert (L % 6 == 0).all()
     assert np.array_equal(L // 6, odict["lens"])
