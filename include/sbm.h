@@ -158,7 +158,9 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  * experts of the call) decoded from its code stream without materialising it.
  * Experts without tokens are skipped.  Tokens with an id outside [0, n_experts)
  * produce no output row and are counted in the workspace error word.
- *   codes/row_off/bstart/scales: device arrays addressed through `experts`
+ *   codes/row_off/bstart/scales: device arrays addressed through `experts`;
+ *               a matrix's codes are read in whole dwords (after an odd count,
+ *               the 2 bytes sharing the last codeword's dword are read and ignored)
  *   experts:    device sbm_matrix_desc[n_experts]
  *   dict_image: device copy of sbm_dict_image() output
  *   x:          device fp16 [n_tokens x cols];  expert_ids: device int32 [n_tokens]

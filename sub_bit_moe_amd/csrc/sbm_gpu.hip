@@ -432,6 +432,9 @@ __device__ __forceinline__ void acc_x(float* acc, const XVal<TC>& x) {
 
 // The codewords of one block as this lane sees them, and the block's start
 // position (bstart, in symbols from the matrix start).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+constexpr int32_t kBufferFlags = 0x00020000;   // raw 32-bit buffer resource word 3 (gfx9 family)
+
 struct BlockCodes {
   uint4 a, b;
   uint32_t bst;
@@ -480,26 +483,25 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   return ch;
 }
 
+// Codewords [b * SBM_BLOCK + 16 * lane, + 16) of a matrix's stream through a
+// range-checked buffer resource: dwords wholly past the stream's end (rounded
+// up to 4 bytes) read as zero, so every lane issues the same two loads and the
+// compiler can count them (a per-lane tail path would make it wait for all
+// loads in flight).  The rounding reads at most the rest of the dword that
+// holds the last codeword; a codeword read past the end decodes to positions
+// after the matrix's last row, which land in a clamped dummy accumulator.
 __device__ __forceinline__ BlockCodes load_block(const FusedArgs& a, uint64_t code_base, uint32_t n_codes,
                                                  uint32_t b) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t idx0 = b * SBM_BLOCK + lane * kK;
+  const uint32_t lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + code_base), (short)0, (int)((2u * n_codes + 3u) & ~3u),
+                                        kBufferFlags);
+  const uint32_t off = (b * SBM_BLOCK + lane * kK) * 2u;
   BlockCodes r;
-  if (idx0 + kK <= n_codes) {
-    const uint4* p = (const uint4*)(a.codes + code_base + idx0);
-    r.a = p[0];
-    r.b = p[1];
-  } else {
-    uint32_t w[8];
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t i0 = idx0 + 2 * j, i1 = i0 + 1;
-      const uint32_t lo = i0 < n_codes ? a.codes[code_base + i0] : 0u;
-      const uint32_t hi = i1 < n_codes ? a.codes[code_base + i1] : 0u;
-      w[j] = lo | (hi << 16);
-    }
-    r.a = make_uint4(w[0], w[1], w[2], w[3]);
-    r.b = make_uint4(w[4], w[5], w[6], w[7]);
-  }
+  const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
+  r.a = make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)lo.z, (uint32_t)lo.w);
+  r.b = make_uint4((uint32_t)hi.x, (uint32_t)hi.y, (uint32_t)hi.z, (uint32_t)hi.w);
   return r;
 }
 
@@ -516,29 +518,42 @@ __device__ __forceinline__ uint32_t sign_spread(uint32_t c, uint32_t split7) {
   return (((c + split7) & 7u) * 0x8102u) & 0x20202u;
 }
 
-// One block of SBM_BLOCK codewords, kK per lane.
-template <int TC, bool SMALL>
-__device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const BlockCodes& raw,
-                              uint32_t split7) {
-  const int lane = threadIdx.x & 63;
+// A block of SBM_BLOCK codewords, kK per lane, decoded: slot words with the
+// signs added (byte 3 = 6 * run length), the lane's total length and its start
+// position (bytes).
+struct DecBlock {
+  uint32_t s[kK];
+  uint32_t tot, pl;
+};
+
+// One table word per codeword, the signs of the 3-nonzero groups added back
+// from the codeword's low bits; run lengths summed, lane start from a wave scan.
+__device__ __forceinline__ void decode_block(const BlockCodes& raw, uint32_t split7, DecBlock& d) {
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
   uint32_t c[kK];
 #pragma unroll
   for (int j = 0; j < kK; ++j) c[j] = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-  // one table word per codeword: nonzero slots and 6 * run length, signs of
-  // the 3-nonzero groups added back from the codeword's low bits
-  uint32_t slots[kK], ls[kK];
 #pragma unroll
-  for (int j = 0; j < kK; ++j) slots[j] = g_tab.tab[table_index(c[j], split7)];
+  for (int j = 0; j < kK; ++j) d.s[j] = g_tab.tab[table_index(c[j], split7)];
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    slots[j] += sign_spread(c[j], split7);
-    ls[j] = tot;
-    tot += slots[j] >> 24;
+    d.s[j] += sign_spread(c[j], split7);
+    tot += d.s[j] >> 24;
   }
-  const uint32_t excl = wave_incl_scan(tot) - tot;
-  const uint32_t pl = 6u * raw.bst + excl;   // lane start, bytes
+  d.tot = tot;
+  d.pl = 6u * raw.bst + wave_incl_scan(tot) - tot;
+}
+
+// Multiply-accumulate of one decoded block into the row accumulators.
+template <int TC, bool SMALL>
+__device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const DecBlock& d) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tot = d.tot, pl = d.pl;
+  uint32_t ls[kK];                   // codeword starts within the lane's span
+  ls[0] = 0;
+#pragma unroll
+  for (int j = 1; j < kK; ++j) ls[j] = ls[j - 1] + (d.s[j - 1] >> 24);
   float* racc = (float*)(smem + a.lds_racc);
   const int32_t R = ch.rb - ch.ra;
   if constexpr (!SMALL) {
@@ -559,7 +574,7 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
 #pragma unroll
       for (int jj = 0; jj < kXB; ++jj) {
         const int j = j0 + jj;
-        const uint32_t s = slots[j];
+        const uint32_t s = d.s[j];
         if constexpr (TC == 1) {
           // one add per slot: the byte operand is taken straight from s
           const uint32_t bx = basex + ls[j];
@@ -610,7 +625,7 @@ __device__ __forceinline__ void process_block(const FusedArgs& a, const Chunk& c
       const uint32_t p = pl + ls[j];
       const uint32_t r = div_magic_dev(p, a.magic_m, a.magic_s);
       const uint32_t base = p - r * a.colsB;
-      const uint32_t s = slots[j];
+      const uint32_t s = d.s[j];
       const uint32_t a0 = (base + (s & 0xFFu)) * TC + a.lds_x;
       const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x;
       const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x;
@@ -852,10 +867,10 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
-                                                 const BlockCodes& raw, uint32_t split7) {
-  if (tc == 1) process_block<1, SMALL>(a, ch, smem, raw, split7);
-  else if (tc == 2) process_block<2, SMALL>(a, ch, smem, raw, split7);
-  else process_block<4, SMALL>(a, ch, smem, raw, split7);
+                                                 const DecBlock& d) {
+  if (tc == 1) accumulate<1, SMALL>(a, ch, smem, d);
+  else if (tc == 2) accumulate<2, SMALL>(a, ch, smem, d);
+  else accumulate<4, SMALL>(a, ch, smem, d);
 }
 
 // ------------------------------------------------------------ dense-tile MFMA path
@@ -1184,34 +1199,47 @@ struct Slot {
 
 // first >= 0: take that block sequence number (the waves' first two blocks of
 // a round are fixed); otherwise draw the next one from the counter.
-__device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t nch, int32_t first = -1) {
+// cur, seq_end: the chunk being processed and its end; a block inside it
+// needs no chunk-table lookup.
+__device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t nch, int32_t first = -1,
+                                     const Chunk* cur = nullptr, uint32_t seq_end = 0) {
   uint32_t q = 0;
   if (first >= 0) {
     q = (uint32_t)first;
   } else {
     if ((threadIdx.x & 63) == 0) q = atomicAdd(&s_next_seq, 1u);
-    q = __builtin_amdgcn_readfirstlane(q);
   }
-  Slot sl;
-  sl.seq = 0xFFFFFFFFu;
-  sl.v.a = make_uint4(0, 0, 0, 0);
-  sl.v.b = sl.v.a;
-  sl.v.bst = 0;
-  if (q < nseq) {
+  q = __builtin_amdgcn_readfirstlane(q);   // uniform, so the buffer resources live in scalar registers
+  // the same three loads on every path, an empty slot with empty ranges
+  uint64_t cb = 0, bb = 0;
+  uint32_t nc = 0, b = 0;
+  const bool valid = q < nseq;
+  if (valid) {
     auto u64 = [](uint64_t v) {
       return (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)v) |
              ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32);
     };
-    const uint32_t c = chunk_of_seq(q, nch);
-    const uint64_t cb = u64(s_chunks[c].code_base), bb = u64(s_chunks[c].blk_base);
-    const uint32_t nc = __builtin_amdgcn_readfirstlane(s_chunks[c].n_codes);
-    const uint32_t b = __builtin_amdgcn_readfirstlane(s_chunks[c].b0 + (q - s_chunks[c].seq0));
-    // the block start is requested with the codes, so that waiting for this
-    // block never waits for blocks requested after it
-    sl.v = load_block(a, cb, nc, b);
-    sl.v.bst = a.bstart[bb + b];
-    sl.seq = q;
+    if (cur && q < seq_end) {       // q >= cur->seq0: the counter only grows
+      cb = cur->code_base;
+      bb = cur->blk_base;
+      nc = cur->n_codes;
+      b = cur->b0 + (q - cur->seq0);
+    } else {
+      const uint32_t c = chunk_of_seq(q, nch);
+      cb = u64(s_chunks[c].code_base);
+      bb = u64(s_chunks[c].blk_base);
+      nc = __builtin_amdgcn_readfirstlane(s_chunks[c].n_codes);
+      b = __builtin_amdgcn_readfirstlane(s_chunks[c].b0 + (q - s_chunks[c].seq0));
+    }
   }
+  Slot sl;
+  // the block start is requested with the codes, so that waiting for this
+  // block never waits for blocks requested after it
+  sl.v = load_block(a, cb, nc, b);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.bstart + bb + b), (short)0, valid ? 4 : 0, kBufferFlags);
+  sl.v.bst = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, 0, 0, 0);
+  sl.seq = valid ? q : 0xFFFFFFFFu;
   return sl;
 }
 
@@ -1233,9 +1261,12 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
   while (true) {
     const uint32_t nch = __builtin_amdgcn_readfirstlane(s_nchunks), nseq = __builtin_amdgcn_readfirstlane(s_nseq);
     if (nch == 0) break;
-    // prefetch: the next block is requested before the current one is decoded
+    // Two blocks in flight per wave: A is decoded next, then B.  A block's
+    // slot is refilled as soon as its codes are decoded, and the loop is
+    // unrolled over A and B, so no slot is copied (a copy would wait for the
+    // loads still landing in it).
     const int32_t wave = (int32_t)(threadIdx.x >> 6);
-    Slot r0 = grab(a, nseq, nch, wave), r1 = grab(a, nseq, nch, wave + kFWaves);
+    Slot A = grab(a, nseq, nch, wave), B = grab(a, nseq, nch, wave + kFWaves);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
       if (MFMA && ch.mfma) {
@@ -1260,11 +1291,21 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         __syncthreads();
       }
       const uint32_t seq_end = c + 1 < nch ? __builtin_amdgcn_readfirstlane(s_chunks[c + 1].seq0) : nseq;
-      while (r0.seq < seq_end) {
-        const Slot cur = r0;
-        r0 = r1;
-        r1 = grab(a, nseq, nch);
-        process_dispatch<SMALL>(tc, a, ch, smem, cur.v, split7);
+      auto step = [&](Slot& sl) {
+        if (sl.seq >= seq_end) return false;
+        DecBlock d;
+        decode_block(sl.v, split7, d);
+        sl = grab(a, nseq, nch, -1, &ch, seq_end);
+        process_dispatch<SMALL>(tc, a, ch, smem, d);
+        return true;
+      };
+      while (step(A)) {
+        if (!step(B)) {           // B's block starts the next chunk: it goes first
+          const Slot t = A;
+          A = B;
+          B = t;
+          break;
+        }
       }
       // This wave has no more blocks of the chunk.  While the others finish,
       // request the row scales of this thread's epilogue rows and, when the
