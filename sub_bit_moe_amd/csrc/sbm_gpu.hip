@@ -103,7 +103,7 @@ struct FusedArgs {
   int32_t rows, cols, n_experts, n_tokens;
   int32_t group_in_lds; // 1: tokens grouped by every workgroup in LDS; 0: by group_kernel in ws
   int32_t grid;
-  uint32_t item_cost;   // slice weight of an item change (row weights are 4..6)
+  uint32_t item_cost;   // slice weight of an item change (row weights are 4..7)
   uint32_t flags;
   uint32_t colsB;       // 6 * cols
   uint32_t magic_s;
@@ -250,11 +250,12 @@ __device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, 
   return (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols;
 }
 
+constexpr uint32_t kRowWeight1 = 4;   // slice weight of a one-token row
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
 __host__ __device__ inline uint32_t item_weight(uint32_t nt) {
   if (nt & kItemMfma) return kMfmaWeight;
-  return nt <= 1 ? 4u : (nt <= 2 ? 5u : 6u);
+  return nt <= 1 ? kRowWeight1 : (nt <= 2 ? 5u : 7u);   // measured: 4:5:7 beats 4:5:6, 4:5:8, 4:6:7, 4:6:8
 }
 
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* total) {
@@ -1803,7 +1804,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   // an item change costs about as much as kItemChangeBlocks blocks of one-token
   // rows (activation restaging, drain, epilogue); a one-token row of cols
   // columns is about cols / 22 codewords and weighs 4
-  a.item_cost = (uint32_t)std::min<int64_t>(4ll * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
+  a.item_cost = (uint32_t)std::min<int64_t>((int64_t)kRowWeight1 * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
   // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
   const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
   // dense MFMA tiles for heavy experts reuse the same dynamic LDS

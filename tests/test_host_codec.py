@@ -51,6 +51,23 @@ def test_dictionary_other_p0_matches_oracle(p0):
     assert np.array_equal(words, ref)
 
 
+def test_dictionary_mismatch_bits():
+    """Bits per weight of the greedy encoding of seeded P(0)=0.857 symbols with
+    the page's table (p0 = 0.885) and with a table built for the data
+    (p0 = 0.857): the matched table spends fewer bits, through entries with a
+    fourth nonzero that the page's table does not hold."""
+    sym = synth.ternary_symbols(np.random.default_rng(11), 128, 2048, 0.857)
+    bits = {}
+    for key, p0 in {"static": 0.885, "matched": 0.857}.items():
+        w, _ = api.build_dictionary(p0)
+        codes, _, _ = api.encode_matrix(sym, w)
+        bits[key] = 16.0 * len(codes) / sym.size
+        sym28, _ = OD.expansion_table(w)
+        bits[key + "_entries_4nz"] = int(((sym28 != 0).sum(axis=1) >= 4).sum())
+    assert bits["static"] / bits["matched"] > 1.01, bits
+    assert bits["static_entries_4nz"] == 0 and bits["matched_entries_4nz"] > 0, bits
+
+
 def test_checksum_is_fnv1a64(odict):
     assert api.dictionary_checksum(odict["words"]) == _fnv1a64(odict["words"])
 
