@@ -18,7 +18,8 @@ Arithmetic is fp64 throughout; fp16 inputs convert exactly.
 Modules:
   dictionary -- dictionary generation and the Figure-4 entry packing
   codec      -- trie encoder, reference decoder, row/block offset tables
-  matvec     -- fp64 matrix-vector products, the MoE layer, stack glue
+  matvec     -- fp64 matrix-vector products (the symmetric grid -s_r/0/+s_r and the
+                page's per-row grid w_min/0/w_max), the MoE layer, stack glue
 
 Parity-pinning status of every function is listed in its docstring.
 ``matvec.rms_glue`` (harness glue between stacked layers, not part of the

@@ -154,6 +154,16 @@ def dequantize(sym: np.ndarray, scales) -> np.ndarray:
     return np.take_along_axis(table, sym.astype(np.int64), axis=1)
 
 
+def dequantize_minmax(sym: np.ndarray, minmax) -> np.ndarray:
+    """fp64 weights on the page's per-row grid {w_min, 0, w_max} ([QMoE]
+    "Quantization grid"; the decode table of "The GPU Decoding Kernel" maps
+    code 0 -> 0, 1 -> w_min, 2 -> w_max of the row).  minmax: [rows, 2] =
+    (w_min, w_max) per row."""
+    mm = np.asarray(minmax, dtype=np.float64).reshape(-1, 2)
+    table = np.stack([np.zeros(mm.shape[0]), mm[:, 0], mm[:, 1]], axis=1)  # [rows, 3]
+    return np.take_along_axis(table, sym.astype(np.int64), axis=1)
+
+
 def code_lengths(codes, lens) -> np.ndarray:
     return np.asarray(lens, dtype=np.int64)[np.asarray(codes, dtype=np.int64)]
 

@@ -2,20 +2,33 @@
 Kernel": y = W_hat x per row with the ternary grid {w_min, 0, w_max}; the MoE
 expert is a ReLU feed-forward pair, up then down).
 
+Two grids: the symmetric reading (-s_r, 0, +s_r) of the benchmark stacks and
+the page's per-row (w_min, 0, w_max).
+
 Pins (tests/test_oracle_matvec.py): brute force over all 3^8 ternary 2x4
-matrices, x = e_j, x = 1, W = 0, linearity.
+matrices (both grids), x = e_j, x = 1, W = 0, linearity, the symmetric grid as
+the special case w_min = -w_max.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .codec import decode_symbols_with_table, dequantize
+from .codec import decode_symbols_with_table, dequantize, dequantize_minmax
 
 
 def matvec(codes, row_off, scales, sym28, lens, cols, x) -> np.ndarray:
     """y[t, r] = sum_j W_hat[r, j] * x[t, j] in fp64.  x: [T, cols]."""
     sym = decode_symbols_with_table(codes, row_off, sym28, lens, cols)
     W = dequantize(sym, scales)
+    X = np.asarray(x, dtype=np.float64).reshape(-1, cols)
+    return X @ W.T
+
+
+def matvec_minmax(codes, row_off, minmax, sym28, lens, cols, x) -> np.ndarray:
+    """y[t, r] = sum_j W_hat[r, j] * x[t, j] in fp64 on the per-row grid
+    {w_min, 0, w_max}; minmax: [rows, 2].  x: [T, cols]."""
+    sym = decode_symbols_with_table(codes, row_off, sym28, lens, cols)
+    W = dequantize_minmax(sym, minmax)
     X = np.asarray(x, dtype=np.float64).reshape(-1, cols)
     return X @ W.T
 

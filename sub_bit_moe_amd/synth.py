@@ -44,6 +44,16 @@ def row_scales(rng: np.random.Generator, rows: int, lo: float = 0.01, hi: float 
     return rng.uniform(lo, hi, size=rows).astype(np.float16)
 
 
+def row_minmax(rng: np.random.Generator, rows: int, lo: float = 0.01, hi: float = 0.05,
+               skew: float = 0.4) -> np.ndarray:
+    """fp16 [rows, 2] per-row grid values (w_min, w_max): w_max = s*u and
+    w_min = -s*v with s ~ U(lo, hi) and u, v ~ U(1 - skew, 1 + skew)."""
+    s = rng.uniform(lo, hi, size=rows)
+    u = rng.uniform(1 - skew, 1 + skew, size=rows)
+    v = rng.uniform(1 - skew, 1 + skew, size=rows)
+    return np.stack([-s * v, s * u], axis=1).astype(np.float16)
+
+
 def activations(rng: np.random.Generator, n_tokens: int, width: int) -> np.ndarray:
     """fp16 [n_tokens, width] ~ N(0,1), rounded to nearest fp16."""
     return rng.standard_normal((n_tokens, width)).astype(np.float16)

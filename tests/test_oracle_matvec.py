@@ -59,10 +59,54 @@ def test_rows_subset_matches_full(odict):
     np.testing.assert_allclose(sub, full[:, [0, 5, 19]], rtol=1e-13)
 
 
+def test_minmax_all_2x4_ternary_matrices(odict):
+    """The page's grid by brute force: every 2x4 ternary matrix, weights looked
+    up symbol by symbol from (0, w_min, w_max) of the row, summed by loops."""
+    mats = np.array(list(product(range(3), repeat=8)), dtype=np.uint8).reshape(-1, 2, 4)
+    sym = mats.reshape(-1, 4)
+    codes, row_off = C.encode_matrix(sym, odict["child"])
+    rng = np.random.default_rng(8)
+    mm = synth.row_minmax(rng, sym.shape[0])
+    x = synth.activations(rng, 2, 4).astype(np.float64)
+    y = M.matvec_minmax(codes, row_off, mm, odict["sym28"], odict["lens"], 4, x)
+    for r in range(0, sym.shape[0], 97):
+        vals = {0: 0.0, 1: float(mm[r, 0]), 2: float(mm[r, 1])}
+        for t in range(2):
+            ref = 0.0
+            for j in range(4):
+                ref += vals[int(sym[r, j])] * x[t, j]
+            assert abs(y[t, r] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_minmax_special_cases(odict):
+    """w_min = -w_max reduces to the symmetric grid; x = e_j picks column j;
+    x = 1 gives w_min * #1 + w_max * #2 per row."""
+    rng = np.random.default_rng(12)
+    rows, cols = 29, 130
+    sym = synth.ternary_symbols(rng, rows, cols, 0.886)
+    codes, row_off = _enc(odict, sym)
+    s = synth.row_scales(rng, rows)
+    sym_mm = np.stack([-s, s], axis=1)
+    x = synth.activations(rng, 2, cols)
+    args = (odict["sym28"], odict["lens"], cols)
+    np.testing.assert_array_equal(M.matvec_minmax(codes, row_off, sym_mm, *args, x),
+                                  M.matvec(codes, row_off, s, *args, x))
+    mm = synth.row_minmax(rng, rows).astype(np.float64)
+    for j in (0, 77, cols - 1):
+        e = np.zeros((1, cols))
+        e[0, j] = 1.0
+        col = np.where(sym[:, j] == 1, mm[:, 0], np.where(sym[:, j] == 2, mm[:, 1], 0.0))
+        assert np.array_equal(M.matvec_minmax(codes, row_off, mm, *args, e)[0], col)
+    ones = M.matvec_minmax(codes, row_off, mm, *args, np.ones((1, cols)))[0]
+    np.testing.assert_allclose(ones, mm[:, 0] * (sym == 1).sum(1) + mm[:, 1] * (sym == 2).sum(1), rtol=1e-13)
+
+
 def test_dequantize_symbol_map():
     sym = np.array([[0, 1, 2]], np.uint8)
     w = C.dequantize(sym, np.array([0.5], np.float16))
     assert w.tolist() == [[0.0, -0.5, 0.5]]
+    w2 = C.dequantize_minmax(sym, np.array([[-0.25, 0.75]], np.float16))
+    assert w2.tolist() == [[0.0, -0.25, 0.75]]
 
 
 def test_rms_glue_properties():
