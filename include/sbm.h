@@ -77,6 +77,13 @@ typedef enum {
                              decoded to a ternary tile in LDS, multiplied on the matrix cores
                              (v_mfma_f32_16x16x32_f16, fp32 accumulation).  Off by default: on
                              gfx950 it is slower than the sparse path up to 64 tokens per expert */
+#define SBM_F_MINMAX 16u  /* [QMoE] "Quantization grid" and "The GPU Decoding Kernel": the per-row
+                             grid {w_min, 0, w_max}.  scales then hold two fp16 per row, (w_min,
+                             w_max) = the values of codes 1 and 2, at scales[scale_base + 2 r]
+                             (scale_base even, scales 4-byte aligned); without it code 1 is -s_r
+                             and code 2 is +s_r.  Each token is staged as two activation rows
+                             ([-x, +x, 0] and [+x, +x, 0]) read at the same slot offsets, so an
+                             item holds half as many tokens.  Not with SBM_F_MFMA. */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);
@@ -133,7 +140,8 @@ int sbm_validate_stream(const uint16_t* codes, uint64_t n_codes, const uint32_t*
 typedef struct {
   uint64_t code_base;   /* first codeword in `codes` (multiple of SBM_CODE_ALIGN) */
   uint64_t off_base;    /* first of the matrix's rows+1 entries in `row_off` */
-  uint64_t scale_base;  /* first of the matrix's `rows` entries in `scales` */
+  uint64_t scale_base;  /* first of the matrix's `rows` entries in `scales` (2 rows entries with
+                           SBM_F_MINMAX) */
   uint64_t blk_base;    /* first of the matrix's block starts in `bstart` */
   uint32_t n_codes;     /* codewords of the matrix */
   int32_t rows;
@@ -153,8 +161,9 @@ int sbm_decode_ref(const uint16_t* codes, const uint32_t* row_off, int32_t rows,
 size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
 
 /* [QMoE] "The GPU Decoding Kernel", grouped over experts: for every token t,
- *   y[t, r] = act( s_r * sum_j W_e[r, j] * x[t, j] ),  e = expert_ids[t],
- * where W_e is expert e's ternary matrix (rows x cols, the same shape for all
+ *   y[t, r] = act( sum_j W_e[r, j] * x[t, j] ),  e = expert_ids[t],
+ * where W_e is expert e's ternary matrix on its per-row grid (codes 1, 2 ->
+ * -s_r, +s_r, or w_min, w_max with SBM_F_MINMAX) (rows x cols, the same shape for all
  * experts of the call) decoded from its code stream without materialising it.
  * Experts without tokens are skipped.  Tokens with an id outside [0, n_experts)
  * produce no output row and are counted in the workspace error word.

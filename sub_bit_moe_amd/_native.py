@@ -15,6 +15,7 @@ SBM_F_RELU = 1
 SBM_F_OUT_F32 = 2
 SBM_F_IN_RMS = 4
 SBM_F_MFMA = 8
+SBM_F_MINMAX = 16
 
 STATUS = {0: "SBM_OK", -1: "SBM_EINVAL", -2: "SBM_EODD_WIDTH", -3: "SBM_ECORRUPT",
           -4: "SBM_EDICT", -5: "SBM_ERANGE", -6: "SBM_ENOSPACE", -7: "SBM_EHIP"}

@@ -109,7 +109,8 @@ class ExpertStack:
         + scales (row offsets are read once per slice)."""
         d = self.host_desc[e]
         nblk = (d.n_codes + N.SBM_BLOCK - 1) // N.SBM_BLOCK
-        return 2 * d.n_codes + 4 * nblk + 2 * self.rows
+        per_row = max(1, int(self.scales.numel()) // max(1, self.n_experts * self.rows))   # 1, or 2 (min/max)
+        return 2 * d.n_codes + 4 * nblk + 2 * per_row * self.rows
 
     @staticmethod
     def from_host(mats, rows: int, cols: int, device="cuda"):
@@ -121,7 +122,8 @@ class ExpertStack:
         used = 0
         for codes, row_off, bstart, scales in mats:
             n = int(codes.size)
-            assert row_off.size == rows + 1 and scales.size == rows
+            # one scale per row, or (w_min, w_max) per row for the min/max grid
+            assert row_off.size == rows + 1 and scales.size in (rows, 2 * rows)
             d = N.MatrixDesc(code_base=cb, off_base=ob, scale_base=sb, blk_base=bb, n_codes=n,
                              rows=rows, cols=cols, reserved=0)
             descs.append(d)
@@ -132,7 +134,7 @@ class ExpertStack:
             sc_parts.append(scales.astype(np.float16))
             cb += n + pad
             ob += rows + 1
-            sb += rows
+            sb += scales.size
             bb += bstart.size
             used += 2 * n
         codes = np.concatenate(code_parts) if code_parts else np.zeros(8, np.uint16)
@@ -174,10 +176,11 @@ def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
 
 def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
                             out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False,
-                            mfma: bool = False):
-    """y[t] = act(s * W_{expert_ids[t]} x[t]) for one projection of an MoE layer
-    (in_rms: x[t] is first scaled to unit RMS, as rms_glue does; mfma=False
-    sends experts with 16 or more tokens to the dense-tile MFMA path)."""
+                            mfma: bool = False, minmax: bool = False):
+    """y[t] = act(W_{expert_ids[t]} x[t]) for one projection of an MoE layer
+    (in_rms: x[t] is first scaled to unit RMS, as rms_glue does; mfma=True
+    sends experts with 16 or more tokens to the dense-tile MFMA path; minmax:
+    the stack's scales are (w_min, w_max) per row, the page's grid)."""
     import torch
     T = int(x.shape[0]) if x is not None else 0
     if y is None:
@@ -187,6 +190,7 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
         workspace = alloc_workspace(stack.n_experts, T, device=stack.codes.device)
     flags = (N.SBM_F_RELU if relu else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0) | (N.SBM_F_IN_RMS if in_rms else 0)
     flags |= N.SBM_F_MFMA if mfma else 0
+    flags |= N.SBM_F_MINMAX if minmax else 0
     check(lib().sbm_moe_fused_decode_matvec(
         _ptr(stack.codes), _ptr(stack.row_off), _ptr(stack.bstart), _ptr(stack.scales), _ptr(stack.desc),
         stack.n_experts, stack.rows, stack.cols, _ptr(image_t), _ptr(x), _ptr(expert_ids), T, _ptr(y),

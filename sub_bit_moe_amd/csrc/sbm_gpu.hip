@@ -109,7 +109,9 @@ struct FusedArgs {
   uint32_t magic_s;
   uint64_t magic_m;     // exact division by colsB for numerators < 2^30
   int32_t rmax;         // rows per chunk (LDS accumulators)
-  int32_t tcmax;        // tokens per item
+  int32_t tcmax;        // interleaved activation rows per item (LDS capacity)
+  int32_t titem;        // tokens per item: tcmax, or tcmax / 2 with the per-row min/max grid
+  int32_t minmax;       // 1: per-row grid (w_min, w_max), each token staged as two rows
   int32_t xcols;        // staged columns per token (cols + pad)
   uint32_t lds_racc;    // byte offsets in LDS
   uint32_t lds_x;
@@ -246,16 +248,19 @@ __device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint
 }
 
 // A matrix descriptor the fused kernel can use for a call of this shape.
-__device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, int32_t cols) {
-  return (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols;
+__device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, int32_t cols, int32_t minmax) {
+  return (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols &&
+         (!minmax || (d.scale_base & 1u) == 0);     // (w_min, w_max) pairs are read as one dword
 }
 
 constexpr uint32_t kRowWeight1 = 4;   // slice weight of a one-token row
 // Relative cost of one output row of an item with nt tokens (processed with
 // 1, 2 or 4 interleaved tokens); used to balance workgroup slices.
-__host__ __device__ inline uint32_t item_weight(uint32_t nt) {
+// (The min/max grid stages every token as two rows, so it weighs as twice the tokens.)
+__host__ __device__ inline uint32_t item_weight(uint32_t nt, int32_t minmax) {
   if (nt & kItemMfma) return kMfmaWeight;
-  return nt <= 1 ? kRowWeight1 : (nt <= 2 ? 5u : 7u);   // measured: 4:5:7 beats 4:5:6, 4:5:8, 4:6:7, 4:6:8
+  const uint32_t n = minmax ? 2 * nt : nt;
+  return n <= 1 ? kRowWeight1 : (n <= 2 ? 5u : 7u);   // measured: 4:5:7 beats 4:5:6, 4:5:8, 4:6:7, 4:6:8
 }
 
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* total) {
@@ -280,8 +285,8 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
 }
 
 __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
-                                                         int32_t E, int32_t tcmax, int32_t rows, int32_t cols,
-                                                         int32_t grid, uint32_t item_cost, int32_t mfma,
+                                                         int32_t E, int32_t titem, int32_t rows, int32_t cols,
+                                                         int32_t grid, uint32_t item_cost, int32_t mfma, int32_t minmax,
                                                          const sbm_matrix_desc* __restrict__ experts,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   for (int base = 0; base < E; base += kThreads) {
     const int e = base + threadIdx.x;
     const uint32_t c = e < E ? cnt[e] : 0u;
-    const uint32_t span = (mfma && c >= (uint32_t)kMfmaMinTokens) ? (uint32_t)kMfmaMaxTokens : (uint32_t)tcmax;
+    const uint32_t span = (mfma && c >= (uint32_t)kMfmaMinTokens) ? (uint32_t)kMfmaMaxTokens : (uint32_t)titem;
     const uint32_t nch = (c + span - 1) / span;
     uint32_t tot_c, tot_n;
     const uint32_t ex_c = block_excl_scan(c, sh_tot, &tot_c);
@@ -335,12 +340,12 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
     const uint32_t s0 = start[e], n = start[e + 1] - s0;
     uint32_t q = chunk[e];
     const bool heavy = mfma && n >= (uint32_t)kMfmaMinTokens;
-    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)tcmax;
+    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)titem;
     for (uint32_t k = 0; k < n; k += span, ++q) {
       const uint32_t nt = ((n - k) < span ? (n - k) : span) | (heavy ? kItemMfma : 0u);
-      items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt));
+      items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt, minmax));
     }
-    if (n && !desc_ok(experts[e], rows, cols)) atomicOr(&hdr[0], kErrBadDesc);
+    if (n && !desc_ok(experts[e], rows, cols, minmax)) atomicOr(&hdr[0], kErrBadDesc);
   }
   __syncthreads();
   // exclusive prefix of the per-row weights over items (.w), total in hdr[2]
@@ -466,7 +471,7 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   ch.nt = it.z & ~kItemMfma;
   ch.mfma = (it.z & kItemMfma) != 0;
   const sbm_matrix_desc d = a.experts[it.x];
-  ch.ok = desc_ok(d, a.rows, a.cols);
+  ch.ok = desc_ok(d, a.rows, a.cols, a.minmax);
   ch.code_base = d.code_base;
   ch.n_codes = d.n_codes;
   ch.blk_base = d.blk_base;
@@ -648,6 +653,9 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
 // tokens interleaved: element (col, k, t) at byte ((3*col + k) * TC + t) * 2.
 // Columns past cols are zero.  Each thread takes groups of 8 columns of all TC
 // tokens (one 16-byte load per token) and writes 48*TC contiguous bytes.
+// With the per-row min/max grid, rows 2u and 2u+1 both hold token u: row 2u as
+// [-x, +x, 0] (its sum is A = S2 - S1 over the row's codes 1 and 2), row 2u+1
+// as [+x, +x, 0] (B = S2 + S1), read at the same slot offsets.
 template <int TC>
 __device__ __forceinline__ void store_x_group(const FusedArgs& a, unsigned char* smem, int32_t c0,
                                               const uint32_t (&p)[TC][4]) {
@@ -668,7 +676,7 @@ __device__ __forceinline__ void store_x_group(const FusedArgs& a, unsigned char*
       for (int tp = 0; tp < TC / 2; ++tp) {                // token pair (2tp, 2tp+1)
         const uint32_t a0 = p[2 * tp][c / 2], a1 = p[2 * tp + 1][c / 2];
         const uint32_t pair = (c & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-        o[(3 * c + 0) * (TC / 2) + tp] = pair ^ 0x80008000u;
+        o[(3 * c + 0) * (TC / 2) + tp] = pair ^ (a.minmax ? 0x00008000u : 0x80008000u);
         o[(3 * c + 1) * (TC / 2) + tp] = pair;
         o[(3 * c + 2) * (TC / 2) + tp] = 0u;
       }
@@ -677,6 +685,11 @@ __device__ __forceinline__ void store_x_group(const FusedArgs& a, unsigned char*
   uint4* d = (uint4*)(smem + a.lds_x + (uint32_t)(6 * c0 * TC));
 #pragma unroll
   for (int q = 0; q < 3 * TC; ++q) d[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+}
+
+// Token place (within the item) of staged activation row t.
+__device__ __forceinline__ uint32_t x_row_token(const FusedArgs& a, int t) {
+  return a.minmax ? (uint32_t)t >> 1 : (uint32_t)t;
 }
 
 __device__ __forceinline__ bool x_vec(const FusedArgs& a) {
@@ -773,7 +786,8 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
     const int32_t s0 = x_src(a, c0, x_wrap(a));
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
-      const int32_t tok = (uint32_t)t < nt ? perm[tb + t] : -1;
+      const uint32_t u = x_row_token(a, t);
+      const int32_t tok = u < nt ? perm[tb + u] : -1;
       r.v[j * TC + t] = (tok >= 0 && s0 + 8 <= a.cols && c0 < 8 * n8)
                             ? *(const uint4*)(a.x + (int64_t)tok * a.cols + s0) : make_uint4(0, 0, 0, 0);
     }
@@ -832,7 +846,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
   }
   int32_t tok[TC];
 #pragma unroll
-  for (int t = 0; t < TC; ++t) tok[t] = (uint32_t)t < nt ? perm[tb + t] : -1;
+  for (int t = 0; t < TC; ++t) tok[t] = x_row_token(a, t) < nt ? perm[tb + x_row_token(a, t)] : -1;
   const int32_t n8 = a.xcols / 8;
   const bool vec = x_vec(a);
   const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
@@ -865,6 +879,8 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
 }
 
 __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 2 ? 2 : 4); }
+// Interleaved activation rows of an item of nt tokens.
+__device__ __forceinline__ int tc_rows(const FusedArgs& a, uint32_t nt) { return tc_of(a.minmax ? 2 * nt : nt); }
 
 template <bool SMALL>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
@@ -1282,7 +1298,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         __syncthreads();
         continue;
       }
-      const int tc = tc_of(ch.nt);
+      const int tc = tc_rows(a, ch.nt);
       if (ch.q != cur_q) {
         if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
         else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
@@ -1316,7 +1332,11 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
 #pragma unroll
       for (int k = 0; k < kEpiRegs; ++k) {
         const int32_t i = (int32_t)threadIdx.x + k * kFThreads;   // accumulator slot, row i - 1
-        sc[k] = (ch.ok && i >= 1 && i <= R) ? a.scales[ch.scale_base + ch.ra + i - 1] : 0u;
+        const bool live = ch.ok && i >= 1 && i <= R;
+        if (a.minmax)     // (w_min, w_max) of the row, one dword
+          sc[k] = live ? ((const uint32_t*)a.scales)[ch.scale_base / 2 + ch.ra + i - 1] : 0u;
+        else
+          sc[k] = live ? a.scales[ch.scale_base + ch.ra + i - 1] : 0u;
       }
       bool next_new = false, next_pre = false;
       Chunk nx;
@@ -1324,7 +1344,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       if (c + 1 < nch) {
         nx = load_chunk(c + 1);
         next_new = nx.q != ch.q && !nx.mfma;
-        const int ntc = tc_of(nx.nt);
+        const int ntc = tc_rows(a, nx.nt);
         if (next_new && x_prefetchable(a, ntc)) {
           next_pre = true;
           if (ntc == 1) xpre_load<1>(a, perm, nx.tb, nx.nt, xp);
@@ -1338,7 +1358,25 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
 #pragma unroll
       for (int k = 0; k < kEpiRegs; ++k) {
         const int32_t i = (int32_t)threadIdx.x + k * kFThreads;
-        if (i < R + 2) {
+        if (i < R + 2 && a.minmax) {
+          // y = w_min * S1 + w_max * S2 = ((w_max - w_min) * A + (w_max + w_min) * B) / 2
+          const float wmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc[k] & 0xFFFFu));
+          const float wmax = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc[k] >> 16));
+          for (int u = 0; 2 * u < tc; ++u) {
+            float* pa = racc + (2 * u) * (a.rmax + 2) + i;
+            float* pb = pa + (a.rmax + 2);
+            const float A = *pa, B = *pb;
+            *pa = 0.f;
+            *pb = 0.f;
+            if (ch.ok && i >= 1 && i <= R && (uint32_t)u < ch.nt) {
+              float v = 0.5f * ((wmax - wmin) * A + (wmax + wmin) * B);
+              if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
+              const int64_t o = (int64_t)perm[ch.tb + u] * a.rows + ch.ra + i - 1;
+              if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
+              else ((_Float16*)a.y)[o] = (_Float16)v;
+            }
+          }
+        } else if (i < R + 2) {
           const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
           for (int t = 0; t < tc; ++t) {
             float* p = racc + t * (a.rmax + 2) + i;
@@ -1355,7 +1393,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         }
       }
       if (next_new) {
-        const int ntc = tc_of(nx.nt);
+        const int ntc = tc_rows(a, nx.nt);
         if (next_pre) {
           if (ntc == 1) xpre_store<1>(a, smem, xp);
           else if (ntc == 2) xpre_store<2>(a, smem, xp);
@@ -1442,7 +1480,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     if (valid) {
       const uint32_t rank = rk[tid], off = rank - lt[tid], cnt = eq[tid];
       const bool heavy = a.mfma_rows > 0 && cnt >= (uint32_t)kMfmaMinTokens;
-      const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.tcmax;
+      const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.titem;
       s_perm[rank] = tid;
       ks[rank] = key;
       if (off % span == 0) nts[rank] = (cnt - off < span ? cnt - off : span) | (heavy ? kItemMfma : 0u);
@@ -1453,7 +1491,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
   __syncthreads();
   if (tid < 64) {
     const uint32_t n0 = nts[2 * tid], n1 = nts[2 * tid + 1];
-    const uint32_t w0 = n0 ? item_weight(n0) : 0u, w1 = n1 ? item_weight(n1) : 0u;
+    const uint32_t w0 = n0 ? item_weight(n0, a.minmax) : 0u, w1 = n1 ? item_weight(n1, a.minmax) : 0u;
     const uint32_t c = (n0 != 0) + (n1 != 0);
     const uint32_t ci = wave_incl_scan(c), wi = wave_incl_scan(w0 + w1);
     uint32_t q = ci - c, wp = wi - w0 - w1;
@@ -1499,7 +1537,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols)) atomicOr(&s_ghdr[3], 1u);
+      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols, a.minmax)) atomicOr(&s_ghdr[3], 1u);
     __syncthreads();
     if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
   }
@@ -1554,12 +1592,12 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     const uint32_t re = above ? (uint32_t)__builtin_ctzll(above) : nv;   // next run's first place
     const uint32_t off = r - rs, cnt = re - rs;
     const bool heavy = a.mfma_rows > 0 && cnt >= (uint32_t)kMfmaMinTokens;
-    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.tcmax;
+    const uint32_t span = heavy ? (uint32_t)kMfmaMaxTokens : (uint32_t)a.titem;
     const bool istart = in && off % span == 0;
     const uint32_t nt = istart ? ((cnt - off < span ? cnt - off : span) | (heavy ? kItemMfma : 0u)) : 0u;
     const uint64_t ib = __ballot(istart);
     const uint32_t q = (uint32_t)__popcll(ib & (((uint64_t)1 << r) - 1));
-    const uint32_t w = istart ? item_weight(nt) : 0u;
+    const uint32_t w = istart ? item_weight(nt, a.minmax) : 0u;
     const uint32_t wi = wave_incl_scan(w);
     const uint32_t wq = wi - w;
     if (in) s_perm[r] = (int32_t)(k & 63u);
@@ -1597,14 +1635,19 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols)) atomicOr(&s_ghdr[3], 1u);
+      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols, a.minmax)) atomicOr(&s_ghdr[3], 1u);
     __syncthreads();
     if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
   }
 }
 
-template <bool MFMA>
+// Instances: MODE 0 the sparse path, 1 with dense-tile MFMA items, 2 with the
+// per-row min/max grid.  The grid flag is made a constant of each instance, so
+// the default instance carries none of its code.
+template <int MODE>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
+  constexpr bool MFMA = MODE == 1;
+  a.minmax = MODE == 2 ? 1 : 0;
   extern __shared__ __align__(16) unsigned char smem[];
   // Requests in order of need: token ids (every thread, no branch, so the
   // request goes out with the first argument loads), the image header in one
@@ -1677,13 +1720,13 @@ static int dev_info(DevInfo** out) {
   }
   if (!di.attr_set) {
     di.static_lds = 0;
-    for (const void* k : {(const void*)fused_kernel<false>, (const void*)fused_kernel<true>}) {
+    for (const void* k : {(const void*)fused_kernel<0>, (const void*)fused_kernel<1>, (const void*)fused_kernel<2>}) {
       hipFuncAttributes fa;
       if ((e = hipFuncGetAttributes(&fa, k)) != hipSuccess)
         return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
       di.static_lds = std::max(di.static_lds, (int)fa.sharedSizeBytes);
     }
-    for (const void* k : {(const void*)fused_kernel<false>, (const void*)fused_kernel<true>}) {
+    for (const void* k : {(const void*)fused_kernel<0>, (const void*)fused_kernel<1>, (const void*)fused_kernel<2>}) {
       e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, di.max_lds - di.static_lds);
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
@@ -1756,7 +1799,10 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
-  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA)) return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX))
+    return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & SBM_F_MINMAX) && (flags & SBM_F_MFMA))
+    return fail(SBM_EINVAL, "SBM_F_MINMAX and SBM_F_MFMA cannot be combined");
   if (n_tokens == 0) return SBM_OK;
   if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
       !workspace)
@@ -1770,6 +1816,11 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   Plan plan;
   if (!make_plan(cols, di->max_lds, di->static_lds, &plan))
     return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
+  const bool minmax = (flags & SBM_F_MINMAX) != 0;
+  if (minmax && plan.tcmax < 2)
+    return fail(SBM_ERANGE, "cols=%d: the min/max grid needs two activation rows per token in LDS", cols);
+  if (minmax && ((uintptr_t)scales & 3u))
+    return fail(SBM_EINVAL, "SBM_F_MINMAX: scales must be 4-byte aligned");
   FusedArgs a;
   a.codes = codes;
   a.row_off = row_off;
@@ -1790,11 +1841,13 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   div_magic(a.colsB, &a.magic_m, &a.magic_s);
   a.rmax = plan.rmax;
   a.tcmax = plan.tcmax;
+  a.minmax = minmax ? 1 : 0;
+  a.titem = minmax ? plan.tcmax / 2 : plan.tcmax;
   a.xcols = plan.xcols;
   a.lds_racc = plan.lds_racc;
   a.lds_x = plan.lds_x;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / plan.tcmax + 1;
+  const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / a.titem + 1;
   const int64_t n_upper = max_items * rows;
   int64_t grid = (n_upper + 63) / 64;
   if (grid > di->cus) grid = di->cus;
@@ -1818,13 +1871,14 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   hipError_t e;
   if (!a.group_in_lds) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                       plan.tcmax, rows, cols, (int32_t)grid, a.item_cost, (int32_t)(a.mfma_rows > 0), experts,
+                       a.titem, rows, cols, (int32_t)grid, a.item_cost, (int32_t)(a.mfma_rows > 0), a.minmax, experts,
                        (uint32_t*)workspace);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }
-  if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
-  else hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<1>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (a.minmax) hipLaunchKernelGGL(fused_kernel<2>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else hipLaunchKernelGGL(fused_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
   return SBM_OK;

@@ -66,3 +66,10 @@ def oracle_matvec_from_codes(odict, sym, scales, x):
     """fp64 y through the oracle's own encode + reference decode."""
     codes, row_off = OC.encode_matrix(sym, odict["child"])
     return OM.matvec(codes, row_off, scales, odict["sym28"], odict["lens"], sym.shape[1], x)
+
+
+def oracle_matvec_minmax_from_codes(odict, sym, minmax, x):
+    """fp64 y on the per-row grid (w_min, w_max) through the oracle's own
+    encode + reference decode."""
+    codes, row_off = OC.encode_matrix(sym, odict["child"])
+    return OM.matvec_minmax(codes, row_off, minmax, odict["sym28"], odict["lens"], sym.shape[1], x)

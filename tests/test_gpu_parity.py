@@ -299,3 +299,74 @@ def test_rms_glue_kernel(dev, T, d):
     assert not np.any(got[T // 2])
     ulp = np.abs(got.view(np.int16).astype(np.int32) - ref.view(np.int16).astype(np.int32))
     assert ulp.max() <= 1, f"max {ulp.max()} fp16 ulps"
+
+
+@pytest.mark.parametrize("rows,cols,T,E", [(300, 2080, 5, 3), (130, 6144, 3, 2), (64, 98, 7, 2),
+                                           (45, 770, 9, 3), (200, 512, 1, 1), (40, 2080, 70, 4),
+                                           (33, 1024, 140, 5)])
+def test_fused_minmax_grid(dev, lib_state, odict, rows, cols, T, E):
+    """SBM_F_MINMAX: the page's per-row grid {w_min, 0, w_max} with
+    asymmetric values, against the oracle's dequantisation on that grid; the
+    three grouping paths (<= 64, <= 128, > 128 tokens), ReLU and fp32 output."""
+    from sub_bit_moe_amd import synth
+    print(f"fused minmax {rows}x{cols} T={T} E={E}", flush=True)
+    api = lib_state["api"]
+    rng = np.random.default_rng(rows * 7 + cols)
+    syms = [synth.ternary_symbols(rng, rows, cols, 0.886) for _ in range(E)]
+    mms = [synth.row_minmax(rng, rows) for _ in range(E)]
+    mats = P.encode_all(list(zip(syms, mms)), odict["words"], odict)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    x = rng.standard_normal((T, cols)).astype(np.float16)
+    ids = (np.arange(T) * 7 + T) % E
+    ids = ids.astype(np.int32)
+    ref = np.zeros((T, rows))
+    for e in range(E):
+        sel = np.nonzero(ids == e)[0]
+        if sel.size:
+            ref[sel] = P.oracle_matvec_minmax_from_codes(odict, syms[e], mms[e], x[sel])
+    xt = torch.from_numpy(x).to(dev)
+    it = torch.from_numpy(ids).to(dev)
+    ws = api.alloc_workspace(E, T, dev)
+    for relu, out_f32 in ((False, False), (True, True)):
+        y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], xt, it, relu=relu, out_f32=out_f32,
+                                        workspace=ws, minmax=True)
+        torch.cuda.synchronize()
+        assert api.workspace_error(ws) == 0
+        exp = np.maximum(ref, 0) if relu else ref
+        P.assert_close(y.float().cpu().numpy().astype(np.float64), exp, what=f"minmax relu={relu} f32={out_f32}")
+
+
+def test_fused_minmax_input_rms_and_symmetric_case(dev, lib_state, odict):
+    """SBM_F_MINMAX with SBM_F_IN_RMS; and w_min = -w_max gives the symmetric
+    path's result."""
+    from oracle import matvec as OM
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    rows, cols, T, E = 150, 2080, 6, 2
+    rng = np.random.default_rng(99)
+    syms = [synth.ternary_symbols(rng, rows, cols, 0.886) for _ in range(E)]
+    mms = [synth.row_minmax(rng, rows) for _ in range(E)]
+    x = rng.standard_normal((T, cols)).astype(np.float16)
+    x[1] = 0
+    ids = (np.arange(T) % E).astype(np.int32)
+    xn = OM.rms_glue(x.astype(np.float64))
+    ref = np.zeros((T, rows))
+    for e in range(E):
+        sel = np.nonzero(ids == e)[0]
+        ref[sel] = P.oracle_matvec_minmax_from_codes(odict, syms[e], mms[e], xn[sel])
+    stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, mms)), odict["words"]), rows, cols, dev)
+    xt, it = torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev)
+    y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], xt, it, in_rms=True, out_f32=True, minmax=True)
+    torch.cuda.synchronize()
+    P.assert_close(y.cpu().numpy().astype(np.float64), ref, what="minmax + in_rms")
+    # symmetric grid as a special case: (-s, s) pairs against the one-scale path
+    ss = [synth.row_scales(rng, rows) for _ in range(E)]
+    mats1 = P.encode_all(list(zip(syms, ss)), odict["words"])
+    mats2 = [(c, o, b, np.stack([-s, s], axis=1)) for (c, o, b, s) in mats1]
+    y1 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats1, rows, cols, dev), lib_state["image_t"],
+                                     xt, it, out_f32=True)
+    y2 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats2, rows, cols, dev), lib_state["image_t"],
+                                     xt, it, out_f32=True, minmax=True)
+    torch.cuda.synchronize()
+    P.assert_close(y2.cpu().numpy().astype(np.float64), y1.cpu().numpy().astype(np.float64), 1e-5, 1e-4,
+                   what="minmax(-s, s) vs symmetric")
