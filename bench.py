@@ -200,6 +200,43 @@ def fusion_baselines(st, run, reps: int = 5):
                     "read back and read again (unfused) at 8 TB/s"}
 
 
+def minmax_pass(st, steps, warmup, sym_launch_us):
+    """The same pass on the page's per-row grid {w_min, 0, w_max} (two fp16
+    per row, each token staged as two activation rows): the fused launches
+    graph-captured and timed like the main pass."""
+    import torch
+    from sub_bit_moe_amd import stack as S
+    mst = S.with_minmax(st)
+    run = S.Runner(mst, minmax=True)
+    run.run_layers()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run_layers()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    n_launch = 2 * st.cfg.n_layers
+    us = 1e3 * k0.elapsed_time(k1) / (steps * n_launch)
+    comp, _ = mst.pass_bytes()
+    out = {"avg_launch_us": round(us, 2), "bytes_per_launch": int(comp / n_launch),
+           "GBps": round(comp / n_launch / (us * 1e-6) / 1e9, 1),
+           "launch_time_vs_symmetric": round(us / sym_launch_us, 3),
+           "note": "same code streams; (w_min, w_max) = (-s v, s u) per row, u, v ~ U(0.6, 1.4); "
+                   "bytes include 4 B of scales per row"}
+    del g, run, mst
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +247,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fusion-baselines", action="store_true",
                     help="skip the unfused and dense bf16 comparators on layer 0")
+    ap.add_argument("--no-minmax", action="store_true",
+                    help="skip the pass on the page's per-row (w_min, w_max) grid")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-size kernel for scaling "
                          "hardware byte counters)")
@@ -288,6 +327,11 @@ def main():
                 "kernel": "sbm::fused_kernel (token grouping inside; 2 launches per layer)",
                 "avg_launch_us": round(launch_us, 2),
                 "bytes_per_launch": int(bytes_per_launch)}
+    minmax = None
+    if not args.no_minmax:
+        log("pass on the per-row (w_min, w_max) grid ...")
+        minmax = minmax_pass(st, args.steps, args.warmup, launch_us)
+        log(f"min/max grid: {minmax['avg_launch_us']} us per launch, {minmax['GBps']} GB/s")
     fusion = None
     if not args.no_fusion_baselines:
         log("fusion baselines (layer 0: unfused decode -> bf16 -> GEMM, dense bf16 GEMM) ...")
@@ -322,6 +366,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fusion_baselines": fusion,
+        "minmax_grid": minmax,
     }
     print(json.dumps(out), flush=True)
 

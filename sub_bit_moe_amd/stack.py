@@ -97,14 +97,47 @@ def build(cfg: StackConfig, device="cuda", log=None) -> Stack:
     return st
 
 
-class Runner:
-    """Preallocated buffers for repeated passes."""
+def with_minmax(st: Stack, seed: int = 7) -> Stack:
+    """The same code streams on the page's per-row grid {w_min, 0, w_max}:
+    (w_min, w_max) = (-s v, s u) per row, s the row's symmetric scale and u, v
+    ~ U(0.6, 1.4) from a seeded device generator; descriptors with doubled
+    scale bases (two fp16 per row)."""
+    import dataclasses
+    import ctypes
+    import torch
+    g = torch.Generator(device=st.x0.device)
+    g.manual_seed(seed)
 
-    def __init__(self, st: Stack):
+    def conv(es):
+        s = es.scales.float()
+        u = torch.empty_like(s).uniform_(0.6, 1.4, generator=g)
+        v = torch.empty_like(s).uniform_(0.6, 1.4, generator=g)
+        mm = torch.stack([-s * v, s * u], dim=1).half().contiguous()
+        d = es.desc.view(torch.int64).view(es.n_experts, 6).clone()   # field 2: scale_base
+        d[:, 2] *= 2
+        hd = []
+        for x in es.host_desc:
+            y = type(x).from_buffer_copy(bytes(x))
+            y.scale_base = 2 * x.scale_base
+            hd.append(y)
+        return dataclasses.replace(es, scales=mm, desc=d.view(torch.uint8).reshape(-1), host_desc=hd)
+
+    out = Stack(st.cfg, st.image, [conv(e) for e in st.up], [conv(e) for e in st.down], st.routes,
+                st.routes_host, st.x0)
+    torch.cuda.synchronize()
+    return out
+
+
+class Runner:
+    """Preallocated buffers for repeated passes (minmax: the stack's scales
+    are (w_min, w_max) pairs)."""
+
+    def __init__(self, st: Stack, minmax: bool = False):
         import torch
         c = st.cfg
         dev = st.x0.device
         self.st = st
+        self.minmax = minmax
         self.ws_up = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
         self.ws_down = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
         self.h = torch.empty(c.n_tokens, c.d_ff, dtype=torch.float16, device=dev)
@@ -127,10 +160,11 @@ class Runner:
         for l in range(st.cfg.n_layers):
             ids = st.routes[l]
             api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h,
-                                        in_rms=l > 0)
+                                        in_rms=l > 0, minmax=self.minmax)
             if keep is not None:
                 keep[l] = (x.clone(), self.h.clone())
-            api.moe_fused_decode_matvec(st.down[l], st.image, self.h, ids, workspace=self.ws_down, y=self.y)
+            api.moe_fused_decode_matvec(st.down[l], st.image, self.h, ids, workspace=self.ws_down, y=self.y,
+                                        minmax=self.minmax)
             if keep is not None:
                 keep[l] = keep[l] + (self.y.clone(),)
             x = self.y

@@ -73,3 +73,10 @@ def oracle_matvec_minmax_from_codes(odict, sym, minmax, x):
     encode + reference decode."""
     codes, row_off = OC.encode_matrix(sym, odict["child"])
     return OM.matvec_minmax(codes, row_off, minmax, odict["sym28"], odict["lens"], sym.shape[1], x)
+
+
+def oracle_matvec_minmax_from_symbols(sym, minmax, x):
+    """fp64 y = W_hat x on the per-row grid (w_min, w_max) via the oracle's
+    dequantisation of the symbols."""
+    W = OC.dequantize_minmax(sym, minmax)
+    return np.asarray(x, np.float64).reshape(-1, sym.shape[1]) @ W.T

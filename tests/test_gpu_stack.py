@@ -99,6 +99,38 @@ def test_small_stack_pass_against_oracle(dev, odict):
                 P.assert_close(out[rsel], ref, what=f"layer {l} token {t} mat {mat}")
 
 
+def test_small_stack_minmax_pass_against_oracle(dev, odict):
+    """The bench's pass on the per-row (w_min, w_max) grid: a 2-layer stack of
+    64 experts with c2048 widths, sampled tokens and rows of every layer's up
+    and down outputs against the oracle on the GPU's own inputs."""
+    from sub_bit_moe_amd import stack as S
+    cfg = S.StackConfig(n_layers=2, n_experts=64, seed=45)
+    st = S.with_minmax(S.build(cfg, dev))
+    run = S.Runner(st, minmax=True)
+    keep = {}
+    run.run(keep)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    for l in range(cfg.n_layers):
+        xraw, h, y = (t.float().cpu().numpy() for t in keep[l])
+        ids = st.routes_host[l]
+        xin = OM.rms_glue(keep[l - 1][2].float().cpu().numpy()).astype(np.float64) if l > 0 else xraw
+        mms = (st.up[l].scales.float().cpu().numpy(), st.down[l].scales.float().cpu().numpy())
+        for t in rng.choice(cfg.n_tokens, 5, replace=False):
+            e = int(ids[t])
+            for mat, inp, out, relu in ((0, xin[t], h[t], True), (1, h[t], y[t], False)):
+                rows, cols = (cfg.d_ff, cfg.d_model) if mat == 0 else (cfg.d_model, cfg.d_ff)
+                key = synth.matrix_key(cfg.seed, l, e, mat, cfg.n_experts)
+                rsel = np.sort(rng.choice(rows, 40, replace=False))
+                sym = np.concatenate([synth.counter_symbols(key, 1, cols, cfg.p0, row0=int(r)) for r in rsel])
+                base = (st.up if mat == 0 else st.down)[l].host_desc[e].scale_base // 2
+                mm = mms[mat][base + rsel]
+                ref = P.oracle_matvec_minmax_from_symbols(sym, mm, inp.astype(np.float16)[None, :])[0]
+                if relu:
+                    ref = np.maximum(ref, 0)
+                P.assert_close(out[rsel], ref, what=f"minmax layer {l} token {t} mat {mat}")
+
+
 def test_graph_replay_matches_eager(dev):
     """The bench captures a pass in a HIP graph: several replays, with eager
     work between them, must reproduce the eager pass.  Row sums are combined
