@@ -13,8 +13,9 @@
 //    space; each persistent workgroup owns a contiguous, row-aligned slice, so
 //    every output row is finished inside one workgroup (no global atomics).
 //  * Stream fetch: a wave handles one block of SBM_BLOCK = 1024 codewords, 16
-//    per lane, read as two 16-byte loads per lane (2 KiB per wave, coalesced).
-//    The block's start position comes from the per-block offset table.
+//    per lane, read as two range-checked 16-byte buffer loads per lane (2 KiB
+//    per wave, coalesced), two blocks in flight per wave.  The block's start
+//    position comes from the per-block offset table.
 //  * Decode: the dictionary is held in LDS as one 60 KB table of 32-bit words
 //    (the image built on the host); every entry has at most 3 nonzeros, so a
 //    codeword yields its length and 3 "slots" (byte offsets of signed
@@ -22,10 +23,12 @@
 //    scales with nonzeros, never with the 28 symbols of a run.
 //  * Positions: lane-local prefix of run lengths plus one wave scan (DPP).
 //  * Accumulate: activations live in LDS as triples [-x, +x, 0] per column
-//    (fp16), so each nonzero is one LDS read and one fp32 add; zeros are never
-//    touched.  A lane spans < one row (cols >= 256), so it splits its sum at
-//    most once; row sums are formed from a wave-wide prefix of lane sums.
-//  * Epilogue: y = act(s_r * acc) per row and token, fp16 or fp32.
+//    (fp16, up to 4 rows interleaved), so each nonzero is one LDS read and one
+//    fp32 add per row; zeros are never touched.  With cols >= 512 a lane (at
+//    most 448 symbols) splits its sum at most once; row sums are formed from a
+//    wave-wide prefix of lane sums.  Narrower rows take a per-codeword path.
+//  * Epilogue: y = act(s_r * acc) per row and token (or, on the per-row
+//    min/max grid, act(w_min * S1 + w_max * S2)), fp16 or fp32.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
