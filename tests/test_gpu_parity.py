@@ -370,3 +370,44 @@ def test_fused_minmax_input_rms_and_symmetric_case(dev, lib_state, odict):
     torch.cuda.synchronize()
     P.assert_close(y2.cpu().numpy().astype(np.float64), y1.cpu().numpy().astype(np.float64), 1e-5, 1e-4,
                    what="minmax(-s, s) vs symmetric")
+
+
+def test_fused_size_limits(dev, lib_state, odict):
+    """Widths near the LDS limit (one activation row of 15000 columns plus its
+    wrap copy), a width past it (SBM_ERANGE), and a matrix at the 30-bit
+    position limit (80000 x 2080) checked on sampled rows against the oracle's
+    dense product of the symbols."""
+    from sub_bit_moe_amd import _native as N
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    rng = np.random.default_rng(2024)
+    # near the widest row that fits
+    rows, cols, T = 70, 15000, 3
+    ex = P.host_experts(1, rows, cols, 0.886, 5)
+    x = rng.standard_normal((T, cols)).astype(np.float16)
+    y, err = _run(lib_state, ex, rows, cols, x, np.zeros(T, np.int32), dev, odict, out_f32=True)
+    assert err == 0
+    P.assert_close(y, P.oracle_matvec_from_symbols(ex[0][0], ex[0][1], x), what="cols=15000")
+    # too wide for LDS: rejected before any launch
+    wide = P.encode_all([(np.zeros((2, 16384), np.uint8), np.ones(2, np.float16))], odict["words"])
+    st = api.ExpertStack.from_host(wide, 2, 16384, dev)
+    with pytest.raises(N.SbmError) as e:
+        api.moe_fused_decode_matvec(st, lib_state["image_t"], torch.zeros((1, 16384), dtype=torch.float16, device=dev),
+                                    torch.zeros(1, dtype=torch.int32, device=dev))
+    assert e.value.status == -5
+    # at the position limit: rows * cols * 6 just under 2^30
+    rows, cols, T = 80000, 2080, 2
+    assert rows * cols * 6 + 1024 * 28 * 6 < (1 << 30)
+    sym = synth.ternary_symbols(rng, rows, cols, 0.886)
+    sc = synth.row_scales(rng, rows)
+    codes, row_off, bstart = api.encode_matrix(sym, odict["words"])
+    st = api.ExpertStack.from_host([(codes, row_off, bstart, sc)], rows, cols, dev)
+    x = rng.standard_normal((T, cols)).astype(np.float16)
+    yt = api.moe_fused_decode_matvec(st, lib_state["image_t"], torch.from_numpy(x).to(dev),
+                                     torch.zeros(T, dtype=torch.int32, device=dev), out_f32=True)
+    torch.cuda.synchronize()
+    y = yt.cpu().numpy().astype(np.float64)
+    rsel = np.sort(np.concatenate([rng.choice(rows, 60, replace=False), [0, rows - 1]]))
+    ref = P.oracle_matvec_from_symbols(sym[rsel], sc[rsel], x)
+    P.assert_close(y[:, rsel], ref, what="80000 x 2080 sampled rows")
+    assert not np.isnan(y).any()
