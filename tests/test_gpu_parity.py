@@ -411,3 +411,41 @@ def test_fused_size_limits(dev, lib_state, odict):
     ref = P.oracle_matvec_from_symbols(sym[rsel], sc[rsel], x)
     P.assert_close(y[:, rsel], ref, what="80000 x 2080 sampled rows")
     assert not np.isnan(y).any()
+
+
+def test_fused_random_shapes(dev, lib_state, odict):
+    """A seeded sweep of valid shapes: even widths 2..3000 (ragged and not
+    multiples of 8), 1..700 rows, 1..160 tokens over 1..9 experts (all three
+    grouping paths), P(0) in [0.5, 0.95], both grids, ReLU and fp32 output."""
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    rng = np.random.default_rng(77)
+    for case in range(18):
+        cols = int(rng.choice([2, 6, 30, 98, 254, 510, 512, 514, 770, 1026, 2080, 3000]))
+        rows = int(rng.integers(1, 700))
+        E = int(rng.integers(1, 10))
+        T = int(rng.choice([1, 2, 5, 17, 64, 65, 128, 129, 160]))
+        p0 = float(rng.uniform(0.5, 0.95))
+        minmax = bool(case % 3 == 2)
+        relu, out_f32 = bool(case % 2), bool(case % 4 == 1)
+        print(f"case {case}: {rows}x{cols} E={E} T={T} p0={p0:.3f} minmax={minmax}", flush=True)
+        syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
+        scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
+        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), odict["words"]), rows, cols, dev)
+        x = rng.standard_normal((T, cols)).astype(np.float16)
+        ids = rng.integers(0, E, T).astype(np.int32)
+        y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
+                                        torch.from_numpy(ids).to(dev), relu=relu, out_f32=out_f32, minmax=minmax)
+        torch.cuda.synchronize()
+        y = y.float().cpu().numpy().astype(np.float64)
+        for e in range(E):
+            sel = np.nonzero(ids == e)[0]
+            if not sel.size:
+                continue
+            if minmax:
+                ref = P.oracle_matvec_minmax_from_symbols(syms[e], scs[e], x[sel])
+            else:
+                ref = P.oracle_matvec_from_symbols(syms[e], scs[e], x[sel])
+            if relu:
+                ref = np.maximum(ref, 0)
+            P.assert_close(y[sel], ref, what=f"case {case} expert {e}")
