@@ -84,6 +84,11 @@ typedef enum {
                              and code 2 is +s_r.  Each token is staged as two activation rows
                              ([-x, +x, 0] and [+x, +x, 0]) read at the same slot offsets, so an
                              item holds half as many tokens.  Not with SBM_F_MFMA. */
+#define SBM_F_IMAGE4 32u  /* dict_image is a 4-slot image from sbm_dict_image4 (a dictionary built
+                             for the data's P(0), whose entries may hold 4 nonzeros); the kernel
+                             gathers 4 activation slots per codeword instead of 3, from an 81 KB
+                             LDS table, which leaves less LDS for activation rows.  Not with
+                             SBM_F_MFMA. */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);
@@ -110,6 +115,20 @@ int sbm_dictionary_checksum(const uint32_t* words, uint64_t* out_checksum);
  * dictionary does not have that structure. */
 size_t sbm_dict_image_bytes(void);
 int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes);
+
+/* [QMoE] "Limitations and Trade-offs" (the dictionary is static, tuned to
+ * c2048's P(0); a table per model is the suggested remedy) and Table 7: the
+ * decode image of a dictionary built for other data.  Tables built for p0
+ * below ~0.885 hold entries with 4 nonzeros (all in runs of at most 14
+ * symbols).  Word per codeword: four 7-bit slots k = 3p + [positive] (2 when
+ * empty) and L / 2 in the top 4 bits; from a split H on, every entry has 3 or
+ * 4 nonzeros in aligned groups of 8 that differ only in the signs of their
+ * first three nonzeros, stored once.  Requires at most 4 nonzeros per entry
+ * and H + (65536 - H) / 8 <= 20800 table words (canonical tables for
+ * 0.83 <= p0 < 1).  Host in, host out; SBM_EDICT otherwise.  Use the image
+ * with SBM_F_IMAGE4. */
+size_t sbm_dict_image4_bytes(void);
+int sbm_dict_image4(const uint32_t* words, void* out_image, size_t image_bytes);
 
 /* ----------------------------------------------------------- host codec */
 
@@ -171,7 +190,8 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  *               a matrix's codes are read in whole dwords (after an odd count,
  *               the 2 bytes sharing the last codeword's dword are read and ignored)
  *   experts:    device sbm_matrix_desc[n_experts]
- *   dict_image: device copy of sbm_dict_image() output
+ *   dict_image: device copy of sbm_dict_image() output (sbm_dict_image4() with SBM_F_IMAGE4);
+ *               an image of the other kind, or a damaged one, sets the workspace error word
  *   x:          device fp16 [n_tokens x cols];  expert_ids: device int32 [n_tokens]
  *   y:          device [n_tokens x rows], fp16 (or fp32 with SBM_F_OUT_F32)
  *   workspace:  device, at least sbm_workspace_bytes(n_experts, n_tokens)

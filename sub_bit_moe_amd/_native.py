@@ -16,6 +16,7 @@ SBM_F_OUT_F32 = 2
 SBM_F_IN_RMS = 4
 SBM_F_MFMA = 8
 SBM_F_MINMAX = 16
+SBM_F_IMAGE4 = 32
 
 STATUS = {0: "SBM_OK", -1: "SBM_EINVAL", -2: "SBM_EODD_WIDTH", -3: "SBM_ECORRUPT",
           -4: "SBM_EDICT", -5: "SBM_ERANGE", -6: "SBM_ENOSPACE", -7: "SBM_EHIP"}
@@ -41,6 +42,8 @@ _SIGS = {
     "sbm_dictionary_checksum": (C.c_int, [P, P]),
     "sbm_dict_image_bytes": (C.c_size_t, []),
     "sbm_dict_image": (C.c_int, [P, P, C.c_size_t]),
+    "sbm_dict_image4_bytes": (C.c_size_t, []),
+    "sbm_dict_image4": (C.c_int, [P, P, C.c_size_t]),
     "sbm_encode_size": (C.c_int, [P, C.c_int32, C.c_int32, P, P]),
     "sbm_encode_matrix": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.c_uint64, P, P, P]),
     "sbm_block_starts": (C.c_int, [P, C.c_uint64, P, P]),

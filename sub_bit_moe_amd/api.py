@@ -45,12 +45,17 @@ def dictionary_checksum(words: np.ndarray) -> int:
     return int(cs.value)
 
 
-def dict_image(words: np.ndarray) -> np.ndarray:
-    """Compact decode image (uint8 bytes) for the fused kernel."""
+def dict_image(words: np.ndarray, slots: int = 3) -> np.ndarray:
+    """Compact decode image (uint8 bytes) for the fused kernel: slots=3 for
+    tables whose entries hold at most 3 nonzeros (the page's static table),
+    slots=4 for tables built for other data (entries with 4 nonzeros)."""
     words = np.ascontiguousarray(words, np.uint32)
-    n = int(lib().sbm_dict_image_bytes())
+    if slots not in (3, 4):
+        raise ValueError("slots must be 3 or 4")
+    n = int(lib().sbm_dict_image_bytes() if slots == 3 else lib().sbm_dict_image4_bytes())
     out = np.zeros(n, np.uint8)
-    check(lib().sbm_dict_image(words.ctypes.data, out.ctypes.data, n))
+    fn = lib().sbm_dict_image if slots == 3 else lib().sbm_dict_image4
+    check(fn(words.ctypes.data, out.ctypes.data, n))
     return out
 
 # ------------------------------------------------------------------ host codec
@@ -147,9 +152,9 @@ class ExpertStack:
                            t(np.concatenate(sc_parts), np.float16), t(desc_bytes, np.uint8), descs, used)
 
 
-def device_image(words: np.ndarray, device="cuda"):
+def device_image(words: np.ndarray, device="cuda", slots: int = 3):
     import torch
-    return torch.from_numpy(dict_image(words)).to(device)
+    return torch.from_numpy(dict_image(words, slots)).to(device)
 
 # ------------------------------------------------------------------ GPU calls
 
@@ -176,11 +181,12 @@ def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
 
 def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
                             out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False,
-                            mfma: bool = False, minmax: bool = False):
+                            mfma: bool = False, minmax: bool = False, image4=None):
     """y[t] = act(W_{expert_ids[t]} x[t]) for one projection of an MoE layer
     (in_rms: x[t] is first scaled to unit RMS, as rms_glue does; mfma=True
     sends experts with 16 or more tokens to the dense-tile MFMA path; minmax:
-    the stack's scales are (w_min, w_max) per row, the page's grid)."""
+    the stack's scales are (w_min, w_max) per row, the page's grid; image4:
+    image_t is a 4-slot image, by default told from its byte size)."""
     import torch
     T = int(x.shape[0]) if x is not None else 0
     if y is None:
@@ -191,6 +197,13 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
     flags = (N.SBM_F_RELU if relu else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0) | (N.SBM_F_IN_RMS if in_rms else 0)
     flags |= N.SBM_F_MFMA if mfma else 0
     flags |= N.SBM_F_MINMAX if minmax else 0
+    n4 = int(lib().sbm_dict_image4_bytes())
+    if image4 is None:
+        image4 = int(image_t.numel()) == n4
+    need = n4 if image4 else int(lib().sbm_dict_image_bytes())
+    if int(image_t.numel()) * image_t.element_size() < need:
+        raise ValueError(f"image buffer holds {image_t.numel() * image_t.element_size()} bytes; the kernel copies {need}")
+    flags |= N.SBM_F_IMAGE4 if image4 else 0
     check(lib().sbm_moe_fused_decode_matvec(
         _ptr(stack.codes), _ptr(stack.row_off), _ptr(stack.bstart), _ptr(stack.scales), _ptr(stack.desc),
         stack.n_experts, stack.rows, stack.cols, _ptr(image_t), _ptr(x), _ptr(expert_ids), T, _ptr(y),

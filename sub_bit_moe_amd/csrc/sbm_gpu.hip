@@ -62,6 +62,14 @@ constexpr uint32_t kImageCopyU4 = kTabEntries / 4;
 constexpr uint32_t kLdsFixed = (uint32_t)sizeof(LdsTables);
 static_assert(kLdsFixed % 16 == 0, "align");
 __shared__ LdsTables g_tab;
+// The 4-slot table (dictionaries with 4-nonzero entries) is referenced only by
+// the instances that read it, so the others do not reserve its LDS.
+struct __align__(16) LdsTables4 {
+  uint32_t tab[kTab4Entries];
+};
+static_assert(offsetof(DictImage4, tab) == offsetof(DictImage, tab), "one header layout");
+static_assert(kTab4Entries % 4 == 0, "16B copies");
+__shared__ LdsTables4 g_tab4;
 
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
@@ -381,14 +389,16 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
 // for vmcnt(0) and then a barrier.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+template <int NS>
 __device__ __forceinline__ void stage_tables_dma(const DictImage* __restrict__ im) {
+  constexpr uint32_t kCopyU4 = NS == 3 ? kImageCopyU4 : kTab4Entries / 4;
   const uint4* src = (const uint4*)im->tab;
-  uint4* dst = (uint4*)g_tab.tab;
+  uint4* dst = NS == 3 ? (uint4*)g_tab.tab : (uint4*)g_tab4.tab;
   const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) return;
-  for (uint32_t q = wave - 1; q * 64 < kImageCopyU4; q += kFWaves - 1) {
+  for (uint32_t q = wave - 1; q * 64 < kCopyU4; q += kFWaves - 1) {
     const uint32_t i = q * 64 + lane;
-    if (i < kImageCopyU4)
+    if (i < kCopyU4)
       __builtin_amdgcn_global_load_lds((const void*)(src + i), (lds_void_t*)(dst + q * 64), 16, 0, 0);
   }
 }
@@ -522,14 +532,32 @@ __device__ __forceinline__ uint32_t table_index(uint32_t c, uint32_t split7) {
   return min(c, (c + split7) >> 3);
 }
 // 2 * bit i of the sign index (c - H) & 7 = (c + 7H) & 7 into byte i (+2: the
-// +x slot of the triple).
+// +x slot of the triple); with 4-slot words bit i into 7-bit field i.
+template <int NS>
 __device__ __forceinline__ uint32_t sign_spread(uint32_t c, uint32_t split7) {
-  return (((c + split7) & 7u) * 0x8102u) & 0x20202u;
+  if constexpr (NS == 3) return (((c + split7) & 7u) * 0x8102u) & 0x20202u;
+  else return (((c + split7) & 7u) * 0x1041u) & 0x4081u;
+}
+template <int NS>
+__device__ __forceinline__ uint32_t table_word(uint32_t idx) {
+  if constexpr (NS == 3) return g_tab.tab[idx];
+  else return g_tab4.tab[idx];
+}
+// Byte offset of slot i within the codeword's first activation triple, and the
+// run's length in bytes of triples (6 per column).
+template <int NS>
+__device__ __forceinline__ uint32_t slot_b(uint32_t s, int i) {
+  if constexpr (NS == 3) return (s >> (8 * i)) & 0xFFu;
+  else return ((s >> (7 * i)) & 0x7Fu) * 2u;
+}
+template <int NS>
+__device__ __forceinline__ uint32_t run_b(uint32_t s) {
+  if constexpr (NS == 3) return s >> 24;
+  else return (s >> 28) * 12u;
 }
 
 // A block of SBM_BLOCK codewords, kK per lane, decoded: slot words with the
-// signs added (byte 3 = 6 * run length), the lane's total length and its start
-// position (bytes).
+// signs added, the lane's total length and its start position (bytes).
 struct DecBlock {
   uint32_t s[kK];
   uint32_t tot, pl;
@@ -537,32 +565,33 @@ struct DecBlock {
 
 // One table word per codeword, the signs of the 3-nonzero groups added back
 // from the codeword's low bits; run lengths summed, lane start from a wave scan.
+template <int NS>
 __device__ __forceinline__ void decode_block(const BlockCodes& raw, uint32_t split7, DecBlock& d) {
   const uint32_t w[8] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
   uint32_t c[kK];
 #pragma unroll
   for (int j = 0; j < kK; ++j) c[j] = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
 #pragma unroll
-  for (int j = 0; j < kK; ++j) d.s[j] = g_tab.tab[table_index(c[j], split7)];
+  for (int j = 0; j < kK; ++j) d.s[j] = table_word<NS>(table_index(c[j], split7));
   uint32_t tot = 0;
 #pragma unroll
   for (int j = 0; j < kK; ++j) {
-    d.s[j] += sign_spread(c[j], split7);
-    tot += d.s[j] >> 24;
+    d.s[j] += sign_spread<NS>(c[j], split7);
+    tot += run_b<NS>(d.s[j]);
   }
   d.tot = tot;
   d.pl = 6u * raw.bst + wave_incl_scan(tot) - tot;
 }
 
 // Multiply-accumulate of one decoded block into the row accumulators.
-template <int TC, bool SMALL>
+template <int TC, bool SMALL, int NS>
 __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const DecBlock& d) {
   const int lane = threadIdx.x & 63;
   const uint32_t tot = d.tot, pl = d.pl;
   uint32_t ls[kK];                   // codeword starts within the lane's span
   ls[0] = 0;
 #pragma unroll
-  for (int j = 1; j < kK; ++j) ls[j] = ls[j - 1] + (d.s[j - 1] >> 24);
+  for (int j = 1; j < kK; ++j) ls[j] = ls[j - 1] + run_b<NS>(d.s[j - 1]);
   float* racc = (float*)(smem + a.lds_racc);
   const int32_t R = ch.rb - ch.ra;
   if constexpr (!SMALL) {
@@ -576,10 +605,10 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
     // Activation gathers in batches of kXB codewords: every address of a batch
     // is formed and its loads issued before the first sum, so up to 15 LDS
     // reads are in flight instead of three.
-    constexpr int kXB = TC == 4 ? 4 : 8;
+    constexpr int kXB = NS == 3 ? (TC == 4 ? 4 : 8) : (TC == 4 ? 2 : 4);
 #pragma unroll
     for (int j0 = 0; j0 < kK; j0 += kXB) {
-      XVal<TC> xv[kXB][3];
+      XVal<TC> xv[kXB][NS];
 #pragma unroll
       for (int jj = 0; jj < kXB; ++jj) {
         const int j = j0 + jj;
@@ -587,23 +616,20 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
         if constexpr (TC == 1) {
           // one add per slot: the byte operand is taken straight from s
           const uint32_t bx = basex + ls[j];
-          xv[jj][0] = lds_x<TC>(smem, bx + (s & 0xFFu));
-          xv[jj][1] = lds_x<TC>(smem, bx + ((s >> 8) & 0xFFu));
-          xv[jj][2] = lds_x<TC>(smem, bx + ((s >> 16) & 0xFFu));
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xv[jj][i] = lds_x<TC>(smem, bx + slot_b<NS>(s, i));
         } else {
           const uint32_t base = colB + ls[j];
-          xv[jj][0] = lds_x<TC>(smem, (base + (s & 0xFFu)) * TC + a.lds_x);
-          xv[jj][1] = lds_x<TC>(smem, (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x);
-          xv[jj][2] = lds_x<TC>(smem, (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xv[jj][i] = lds_x<TC>(smem, (base + slot_b<NS>(s, i)) * TC + a.lds_x);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jj = 0; jj < kXB; ++jj) {
         const int j = j0 + jj;
-        acc_x<TC>(acc, xv[jj][0]);
-        acc_x<TC>(acc, xv[jj][1]);
-        acc_x<TC>(acc, xv[jj][2]);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc_x<TC>(acc, xv[jj][i]);
         const bool first_row = ls[j] < thr;
 #pragma unroll
         for (int t = 0; t < TC; ++t) snap[t] = first_row ? acc[t] : snap[t];
@@ -635,15 +661,14 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
       const uint32_t r = div_magic_dev(p, a.magic_m, a.magic_s);
       const uint32_t base = p - r * a.colsB;
       const uint32_t s = d.s[j];
-      const uint32_t a0 = (base + (s & 0xFFu)) * TC + a.lds_x;
-      const uint32_t a1 = (base + ((s >> 8) & 0xFFu)) * TC + a.lds_x;
-      const uint32_t a2 = (base + ((s >> 16) & 0xFFu)) * TC + a.lds_x;
+      uint32_t ad[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) ad[i] = (base + slot_b<NS>(s, i)) * TC + a.lds_x;
       float v[TC];
 #pragma unroll
       for (int t = 0; t < TC; ++t) v[t] = 0.f;
-      acc_x<TC>(v, lds_x<TC>(smem, a0));
-      acc_x<TC>(v, lds_x<TC>(smem, a1));
-      acc_x<TC>(v, lds_x<TC>(smem, a2));
+#pragma unroll
+      for (int i = 0; i < NS; ++i) acc_x<TC>(v, lds_x<TC>(smem, ad[i]));
       const int32_t i0 = (int32_t)r - ch.ra + 1;
       const int32_t ii = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
 #pragma unroll
@@ -885,12 +910,12 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 // Interleaved activation rows of an item of nt tokens.
 __device__ __forceinline__ int tc_rows(const FusedArgs& a, uint32_t nt) { return tc_of(a.minmax ? 2 * nt : nt); }
 
-template <bool SMALL>
+template <bool SMALL, int NS>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
                                                  const DecBlock& d) {
-  if (tc == 1) accumulate<1, SMALL>(a, ch, smem, d);
-  else if (tc == 2) accumulate<2, SMALL>(a, ch, smem, d);
-  else accumulate<4, SMALL>(a, ch, smem, d);
+  if (tc == 1) accumulate<1, SMALL, NS>(a, ch, smem, d);
+  else if (tc == 2) accumulate<2, SMALL, NS>(a, ch, smem, d);
+  else accumulate<4, SMALL, NS>(a, ch, smem, d);
 }
 
 // ------------------------------------------------------------ dense-tile MFMA path
@@ -1025,7 +1050,7 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
       for (int j = 0; j < kK; ++j) {
         const uint32_t idx = i0 + j;
         const uint32_t c = idx < c_hi ? (uint32_t)a.codes[ch.code_base + idx] : 0u;
-        sw[j] = g_tab.tab[table_index(c, split7)] + sign_spread(c, split7);
+        sw[j] = g_tab.tab[table_index(c, split7)] + sign_spread<3>(c, split7);
       }
 #pragma unroll
       for (int j = 0; j < kK; ++j) tot += i0 + j < c_hi ? (sw[j] >> 24) : 0u;
@@ -1265,7 +1290,7 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 
 // MFMA: the kernel instance that runs dense-tile items (SBM_F_MFMA); the
 // default instance has no call in its loop, which keeps its registers unspilled.
-template <bool SMALL, bool MFMA>
+template <bool SMALL, bool MFMA, int NS>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1, uint32_t split7) {
   float* racc = (float*)(smem + a.lds_racc);
@@ -1314,9 +1339,9 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       auto step = [&](Slot& sl) {
         if (sl.seq >= seq_end) return false;
         DecBlock d;
-        decode_block(sl.v, split7, d);
+        decode_block<NS>(sl.v, split7, d);
         sl = grab(a, nseq, nch, -1, &ch, seq_end);
-        process_dispatch<SMALL>(tc, a, ch, smem, d);
+        process_dispatch<SMALL, NS>(tc, a, ch, smem, d);
         return true;
       };
       while (step(A)) {
@@ -1645,12 +1670,15 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
 }
 
 // Instances: MODE 0 the sparse path, 1 with dense-tile MFMA items, 2 with the
-// per-row min/max grid.  The grid flag is made a constant of each instance, so
-// the default instance carries none of its code.
+// per-row min/max grid; 3 and 4 are 0 and 2 with the 4-slot decode image.
+// The grid flag is made a constant of each instance, so the default instance
+// carries none of its code.
+constexpr int kModes = 5;
 template <int MODE>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   constexpr bool MFMA = MODE == 1;
-  a.minmax = MODE == 2 ? 1 : 0;
+  constexpr int NS = MODE >= 3 ? 4 : 3;
+  a.minmax = (MODE == 2 || MODE == 4) ? 1 : 0;
   extern __shared__ __align__(16) unsigned char smem[];
   // Requests in order of need: token ids (every thread, no branch, so the
   // request goes out with the first argument loads), the image header in one
@@ -1659,10 +1687,11 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
   const int32_t my_id = a.ids[tq];
   const uint4 hdr = *(const uint4*)a.image;       // magic, version, split, n_tab
-  stage_tables_dma(a.image);
-  // the table indexes stay below n_tab <= kTabEntries for every codeword
-  const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
-                        hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
+  stage_tables_dma<NS>(a.image);
+  // the table indexes stay below n_tab <= the table's capacity for every codeword
+  const bool image_ok = hdr.x == kImageMagic && hdr.y == (NS == 3 ? kImageVersion : kImage4Version) &&
+                        hdr.z <= SBM_DICT_ENTRIES && hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u &&
+                        hdr.w <= (NS == 3 ? kTabEntries : kTab4Entries);
   const uint32_t split7 = 7u * hdr.z;
   const int32_t* perm;
   const uint4* items;
@@ -1672,7 +1701,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     else group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
     if (!image_ok) {
       if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = kErrBadImage;   // after the grouping's write
-      return;
+      return;               // (s_endpgm waits for the table copy still in flight, as on an empty slice)
     }
     g0 = s_slice[0];
     g1 = s_slice[1];
@@ -1691,19 +1720,31 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true, MFMA>(a, smem, perm, items, g0, g1, split7);
-  else run_slice<false, MFMA>(a, smem, perm, items, g0, g1, split7);
+  if (a.cols < kSmallCols) run_slice<true, MFMA, NS>(a, smem, perm, items, g0, g1, split7);
+  else run_slice<false, MFMA, NS>(a, smem, perm, items, g0, g1, split7);
 }
 
 // ------------------------------------------------------------ host entries
 struct DevInfo {
   int cus = 0;
   int max_lds = 0;        // LDS per workgroup
-  int static_lds = 0;     // static LDS of the fused kernel
+  // static LDS of the fused-kernel instances, per image kind: the largest over
+  // the instances one call may launch (0-2: 3-slot image, 3-4: 4-slot image)
+  int static_lds[2] = {};
   bool attr_set = false;
 };
 static std::mutex g_mu;
 static DevInfo g_dev[64];
+
+static const void* fused_instance(int mode) {
+  switch (mode) {
+    case 1: return (const void*)fused_kernel<1>;
+    case 2: return (const void*)fused_kernel<2>;
+    case 3: return (const void*)fused_kernel<3>;
+    case 4: return (const void*)fused_kernel<4>;
+    default: return (const void*)fused_kernel<0>;
+  }
+}
 
 static int dev_info(DevInfo** out) {
   int dev = 0;
@@ -1722,15 +1763,17 @@ static int dev_info(DevInfo** out) {
     di.max_lds = v;
   }
   if (!di.attr_set) {
-    di.static_lds = 0;
-    for (const void* k : {(const void*)fused_kernel<0>, (const void*)fused_kernel<1>, (const void*)fused_kernel<2>}) {
+    di.static_lds[0] = di.static_lds[1] = 0;
+    for (int m = 0; m < kModes; ++m) {
       hipFuncAttributes fa;
-      if ((e = hipFuncGetAttributes(&fa, k)) != hipSuccess)
+      if ((e = hipFuncGetAttributes(&fa, fused_instance(m))) != hipSuccess)
         return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
-      di.static_lds = std::max(di.static_lds, (int)fa.sharedSizeBytes);
+      int& st = di.static_lds[m >= 3 ? 1 : 0];
+      st = std::max(st, (int)fa.sharedSizeBytes);
     }
-    for (const void* k : {(const void*)fused_kernel<0>, (const void*)fused_kernel<1>, (const void*)fused_kernel<2>}) {
-      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, di.max_lds - di.static_lds);
+    for (int m = 0; m < kModes; ++m) {
+      e = hipFuncSetAttribute(fused_instance(m), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              di.max_lds - di.static_lds[m >= 3 ? 1 : 0]);
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
     di.attr_set = true;
@@ -1802,10 +1845,12 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
-  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX))
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX | SBM_F_IMAGE4))
     return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & SBM_F_MINMAX) && (flags & SBM_F_MFMA))
     return fail(SBM_EINVAL, "SBM_F_MINMAX and SBM_F_MFMA cannot be combined");
+  if ((flags & SBM_F_IMAGE4) && (flags & SBM_F_MFMA))
+    return fail(SBM_EINVAL, "SBM_F_IMAGE4 and SBM_F_MFMA cannot be combined");
   if (n_tokens == 0) return SBM_OK;
   if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
       !workspace)
@@ -1816,10 +1861,11 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   DevInfo* di = nullptr;
   int st = dev_info(&di);
   if (st) return st;
-  Plan plan;
-  if (!make_plan(cols, di->max_lds, di->static_lds, &plan))
-    return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
   const bool minmax = (flags & SBM_F_MINMAX) != 0;
+  const int mode = (flags & SBM_F_MFMA) ? 1 : ((flags & SBM_F_IMAGE4) ? (minmax ? 4 : 3) : (minmax ? 2 : 0));
+  Plan plan;
+  if (!make_plan(cols, di->max_lds, di->static_lds[mode >= 3 ? 1 : 0], &plan))
+    return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
   if (minmax && plan.tcmax < 2)
     return fail(SBM_ERANGE, "cols=%d: the min/max grid needs two activation rows per token in LDS", cols);
   if (minmax && ((uintptr_t)scales & 3u))
@@ -1880,6 +1926,8 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }
   if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<1>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 3) hipLaunchKernelGGL(fused_kernel<3>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 4) hipLaunchKernelGGL(fused_kernel<4>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (a.minmax) hipLaunchKernelGGL(fused_kernel<2>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else hipLaunchKernelGGL(fused_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   e = hipGetLastError();

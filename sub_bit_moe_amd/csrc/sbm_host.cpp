@@ -198,6 +198,63 @@ int dict_image(const uint32_t* words, void* out, size_t bytes) {
   return SBM_OK;
 }
 
+// 4-slot image: 7-bit fields k = 3p + [positive] (2: empty), L / 2 on top.
+static uint32_t spread4(uint32_t sg) { return ((sg & 7u) * 0x1041u) & 0x4081u; }
+
+int dict_image4(const uint32_t* words, void* out, size_t bytes) {
+  if (!words || !out) return fail(SBM_EINVAL, "null pointer");
+  if (bytes < sizeof(DictImage4)) return fail(SBM_ENOSPACE, "image buffer too small");
+  std::vector<uint32_t> word(SBM_DICT_ENTRIES);
+  std::vector<uint8_t> nnz(SBM_DICT_ENTRIES), sidx(SBM_DICT_ENTRIES);
+  uint8_t sym[SBM_MAX_RUN];
+  for (uint32_t c = 0; c < SBM_DICT_ENTRIES; ++c) {
+    const int L = unpack(words[2 * c], words[2 * c + 1], sym);
+    if (L < 0) return fail(SBM_EDICT, "entry %u: malformed pair count or symbols", c);
+    uint32_t w = (uint32_t)(L / 2) << 28, n = 0, sg = 0;
+    for (int p = 0; p < L; ++p)
+      if (sym[p]) {
+        if (n >= 4) return fail(SBM_EDICT, "entry %u has more than 4 nonzeros", c);
+        if (sym[p] == 2) sg |= 1u << n;
+        w |= (uint32_t)(3 * p + (sym[p] == 2 ? 1 : 0)) << (7 * n);
+        ++n;
+      }
+    for (uint32_t i = n; i < 4; ++i) w |= 2u << (7 * i);
+    word[c] = w;
+    nnz[c] = (uint8_t)n;
+    sidx[c] = (uint8_t)sg;
+  }
+  // split: from H on every entry has 3 or 4 nonzeros, and groups of 8 align
+  // (same word apart from the signs of nonzeros 0..2, which are (c - H) & 7)
+  uint32_t H = SBM_DICT_ENTRIES;
+  while (H > 0 && nnz[H - 1] >= 3) --H;
+  auto aligned = [&](uint32_t h) {
+    for (uint32_t c = h; c < SBM_DICT_ENTRIES; ++c) {
+      const uint32_t s = (c - h) & 7u, c0 = c - s;
+      if ((sidx[c] & 7u) != s || (word[c] - spread4(s)) != word[c0]) return false;
+    }
+    return true;
+  };
+  while (H < SBM_DICT_ENTRIES && !aligned(H)) ++H;
+  const uint32_t n_tab = H + (SBM_DICT_ENTRIES - H + 7) / 8;
+  if (n_tab > kTab4Entries)
+    return fail(SBM_EDICT, "dictionary needs %u 4-slot decode-table entries (at most %u)", n_tab, kTab4Entries);
+  DictImage4* im = (DictImage4*)out;
+  std::memset(im, 0, sizeof(DictImage4));
+  im->magic = kImageMagic;
+  im->version = kImage4Version;
+  im->split = H;
+  im->n_tab = n_tab;
+  im->checksum = checksum(words);
+  for (uint32_t c = 0; c < H; ++c) im->tab[c] = word[c] - spread4(c + 7 * H);
+  for (uint32_t c = H; c < SBM_DICT_ENTRIES; c += 8) im->tab[H + (c - H) / 8] = word[c];
+  for (uint32_t c = 0; c < SBM_DICT_ENTRIES; ++c) {
+    const uint32_t e = c + 7 * H, idx = std::min(c, e >> 3);
+    if (idx >= n_tab || im->tab[idx] + spread4(e) != word[c])
+      return fail(SBM_EDICT, "internal: entry %u does not rebuild", c);
+  }
+  return SBM_OK;
+}
+
 // ------------------------------------------------------------------ encoder
 // Trie over pair extensions: child[node*9 + 3a+b] = codeword of the node's
 // sequence extended by (a, b), or -1; node 65536 is the root (empty sequence).
@@ -407,6 +464,11 @@ int sbm_dictionary_checksum(const uint32_t* words, uint64_t* out_checksum) {
 }
 
 size_t sbm_dict_image_bytes(void) { return sizeof(sbm::DictImage); }
+size_t sbm_dict_image4_bytes(void) { return sizeof(sbm::DictImage4); }
+
+int sbm_dict_image4(const uint32_t* words, void* out_image, size_t image_bytes) {
+  return sbm::dict_image4(words, out_image, image_bytes);
+}
 
 int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes) {
   return sbm::dict_image(words, out_image, image_bytes);

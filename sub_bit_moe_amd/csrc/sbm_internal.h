@@ -13,6 +13,8 @@ namespace sbm {
 constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
 constexpr uint32_t kImageVersion = 5;
 constexpr uint32_t kTabEntries = 15360;        // decode-table capacity: 60 KB
+constexpr uint32_t kImage4Version = 6;
+constexpr uint32_t kTab4Entries = 20800;       // 4-slot table capacity: 81.25 KB (p0 >= 0.83)
 
 // Decode image of a dictionary (device copy read by the fused kernel): one
 // 32-bit word per codeword says everything the kernel needs,
@@ -42,12 +44,35 @@ struct DictImage {
   uint32_t tab[kTabEntries];
 };
 
+// 4-slot decode image, for dictionaries whose entries hold up to 4 nonzeros
+// (those built for P(0) below about 0.885 have runs of 4 nonzeros, all of
+// length <= 14).  Same header and the same two steps with another word:
+//   bits 7i .. 7i+6 (i = 0..3): k_i = 3*p_i + [nonzero i is positive] for the
+//                         i-th nonzero at run position p_i, or 2 when the
+//                         entry has fewer than i+1 nonzeros (2*k_i is the
+//                         byte offset in the activation triples);
+//   bits 28..31:          L / 2 (pairs in the run).
+// From H on every entry has 3 or 4 nonzeros and groups of 8 share positions,
+// length and the sign of a 4th nonzero (in-class rank = colex rank * 2^n +
+// sign index, class sizes multiples of 8); spread(s) = ((s * 0x1041) & 0x4081)
+// puts bit i of s into field i.
+struct DictImage4 {
+  uint32_t magic;
+  uint32_t version;
+  uint32_t split;
+  uint32_t n_tab;
+  uint64_t checksum;
+  uint64_t reserved1;
+  uint32_t tab[kTab4Entries];
+};
+
 int fail(int status, const char* fmt, ...);
 const char* last_error();
 int unpack(uint32_t w0, uint32_t w1, uint8_t* s);
 int build_dictionary(double p0, uint32_t* words);
 uint64_t checksum(const uint32_t* words);
 int dict_image(const uint32_t* words, void* out, size_t bytes);
+int dict_image4(const uint32_t* words, void* out, size_t bytes);
 int build_trie(const uint32_t* words, std::vector<int32_t>& child);
 int encode_size(const uint8_t* sym, int32_t rows, int32_t cols, const uint32_t* words,
                 uint64_t* n_codes);

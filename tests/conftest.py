@@ -23,3 +23,25 @@ def odict():
     sym28, lens = D.expansion_table(words)
     child = C.trie_children(seqs)
     return {"seqs": seqs, "words": words, "sym28": sym28, "lens": lens, "child": child}
+
+
+_ODICTS = {}
+
+
+@pytest.fixture(scope="session")
+def odict_for(odict):
+    """The oracle's dictionary for another p0 (cached), same fields as odict."""
+    from oracle import dictionary as D
+    from oracle import codec as C
+
+    def make(p0):
+        if p0 == 0.885:
+            return odict
+        if p0 not in _ODICTS:
+            seqs = D.build_dictionary(p0)
+            words = D.dictionary_words(seqs)
+            sym28, lens = D.expansion_table(words)
+            _ODICTS[p0] = {"seqs": seqs, "words": words, "sym28": sym28, "lens": lens,
+                           "child": C.trie_children(seqs)}
+        return _ODICTS[p0]
+    return make

@@ -449,3 +449,74 @@ def test_fused_random_shapes(dev, lib_state, odict):
             if relu:
                 ref = np.maximum(ref, 0)
             P.assert_close(y[sel], ref, what=f"case {case} expert {e}")
+
+
+@pytest.mark.parametrize("p0,rows,cols,E,T,minmax,seed", [
+    (0.857, 768, 3072, 6, 64, False, 1),     # base128 down shape, table built for its P(0)
+    (0.857, 3072, 768, 6, 129, False, 2),    # up shape; > 128 tokens: grouping in its own launch
+    (0.83, 300, 514, 3, 17, False, 3),       # wrap copy, ragged rows
+    (0.857, 70, 98, 4, 100, False, 4),       # narrow rows: a lane spans several rows
+    (0.857, 257, 2080, 3, 9, True, 5),       # per-row (w_min, w_max) grid on the 4-slot image
+    (0.885, 129, 2080, 5, 33, False, 6),     # the page's static table through the 4-slot instance
+    (0.87, 1, 6144, 2, 3, False, 7),         # one 6144-wide row
+])
+def test_fused_image4_matched_dictionary(dev, lib_state, odict_for, p0, rows, cols, E, T, minmax, seed):
+    """A dictionary built for the data's P(0) (entries with 4 nonzeros) through
+    the 4-slot decode image: codes bit-exact with the oracle's encoder under
+    that table, y against the oracle's decode of those codes."""
+    print(f"image4 p0={p0} {rows}x{cols} E={E} T={T} minmax={minmax}", flush=True)
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    od = odict_for(p0)
+    rng = np.random.default_rng(100 + seed)
+    syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
+    scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
+    big = rows * cols > 500_000
+    mats = P.encode_all(list(zip(syms, scs)), od["words"], od, check_every=E if big else 1)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    image4 = api.device_image(od["words"], dev, slots=4)
+    x = synth.activations(rng, T, cols)
+    ids = synth.zipf_routing(rng, T, E)
+    ws = api.alloc_workspace(E, T, dev)
+    y = api.moe_fused_decode_matvec(stack, image4, torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev),
+                                    relu=bool(seed % 2), workspace=ws, minmax=minmax)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 0
+    y = y.float().cpu().numpy().astype(np.float64)
+    for e in range(E):
+        sel = np.nonzero(ids == e)[0]
+        if not sel.size:
+            continue
+        if not big or e == 0:        # the oracle's own encode + decode under the matched table
+            ref = (P.oracle_matvec_minmax_from_codes(od, syms[e], scs[e], x[sel]) if minmax
+                   else P.oracle_matvec_from_codes(od, syms[e], scs[e], x[sel]))
+        else:                        # codes of expert 0 were checked bit-exact; the rest via the symbols
+            ref = (P.oracle_matvec_minmax_from_symbols(syms[e], scs[e], x[sel]) if minmax
+                   else P.oracle_matvec_from_symbols(syms[e], scs[e], x[sel]))
+        if seed % 2:
+            ref = np.maximum(ref, 0)
+        P.assert_close(y[sel], ref, what=f"expert {e}")
+
+
+def test_fused_image_kind_mismatch_is_flagged(dev, lib_state, odict_for):
+    """A 3-slot image used as a 4-slot one (padded to the 4-slot size, so the
+    table copy stays inside the buffer) and a 4-slot image used as a 3-slot one
+    fail the kernel's header check: error bit 31, nothing computed."""
+    api = lib_state["api"]
+    od = odict_for(0.857)
+    sym, sc = P.host_experts(1, 64, 256, 0.857, 9)[0]
+    stack = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"]), 64, 256, dev)
+    from sub_bit_moe_amd import synth
+    from sub_bit_moe_amd import _native as N
+    x = torch.from_numpy(synth.activations(np.random.default_rng(9), 3, 256)).to(dev)
+    ids = torch.zeros(3, dtype=torch.int32, device=dev)
+    n4 = int(N.lib().sbm_dict_image4_bytes())
+    im3 = api.dict_image(odict_for(0.885)["words"])
+    padded = np.zeros(n4, np.uint8)
+    padded[:im3.size] = im3
+    im4 = api.device_image(od["words"], dev, slots=4)
+    for image_t, image4 in ((torch.from_numpy(padded).to(dev), True), (im4, False)):
+        ws = api.alloc_workspace(1, 3, dev)
+        api.moe_fused_decode_matvec(stack, image_t, x, ids, workspace=ws, image4=image4)
+        torch.cuda.synchronize()
+        assert api.workspace_error(ws) == 0x80000000

@@ -24,7 +24,7 @@ def _fnv1a64(words):
 
 def test_library_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "sbm.h")).read()
-    declared = set(re.findall(r"\b(sbm_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(sbm_[a-z0-9_]+)\s*\(", header))
     assert declared, "no declarations found"
     L = N.lib()
     missing = [s for s in declared if not hasattr(L, s)]
@@ -181,6 +181,64 @@ def test_image_rejects_non_canonical(odict):
     assert e.value.status == -4
 
 
+@pytest.mark.parametrize("p0", [0.857, 0.83, 0.885])
+def test_decode_image4_reproduces_every_codeword(odict_for, p0):
+    """The 4-slot image of a table built for P(0) = p0: the fused kernel's
+    arithmetic (idx = min(c, (c + 7H) >> 3), word = tab[idx] + spread of the
+    sign bits (c + 7H) & 7 into fields 0..2) applied to all 65536 codewords on
+    the CPU; 7-bit fields k = 3p + [positive] (2: empty) and L / 2 in bits 28..31
+    compared with the oracle's unpacking of the same table."""
+    od = odict_for(p0)
+    w, _ = api.build_dictionary(p0)
+    assert np.array_equal(w, od["words"])
+    img = api.dict_image(w, 4)
+    assert img.size == N.lib().sbm_dict_image4_bytes()
+    version, H, n_tab, tab = _image_fields(img)
+    assert version == 6
+    assert n_tab == H + (65536 - H + 7) // 8 and n_tab <= tab.size
+    nnz = (od["sym28"] != 0).sum(axis=1)
+    assert nnz.max() <= 4 and (nnz[H:] >= 3).all()
+    c = np.arange(65536, dtype=np.uint32)
+    e = c + np.uint32(7 * H)
+    idx = np.minimum(c, e >> np.uint32(3))
+    assert idx.max() < n_tab
+    word = tab[idx] + ((e & np.uint32(7)) * np.uint32(0x1041) & np.uint32(0x4081))
+    assert np.array_equal((word >> np.uint32(28)).astype(np.int64) * 2, od["lens"])
+    exp = np.zeros((65536, 28), np.uint8)
+    filled = np.zeros(65536, np.int64)
+    for i in range(4):
+        k = ((word >> np.uint32(7 * i)) & np.uint32(0x7F)).astype(np.int64)
+        live = k != 2
+        assert (k[live] % 3 != 2).all()                  # only the empty slot reads a zero
+        pos, sgn = k // 3, k % 3
+        assert (pos[live] < od["lens"][live]).all()
+        exp[c[live], pos[live]] = (1 + sgn[live]).astype(np.uint8)
+        filled += live
+    assert np.array_equal(filled, nnz)
+    assert np.array_equal(exp, od["sym28"])
+    if p0 == 0.857:
+        assert H == 9734 and n_tab == 16710 and (nnz == 4).sum() == 1376
+
+
+def test_image4_rejections(odict):
+    w = odict["words"].copy()
+    w[[2 * 100, 2 * 100 + 1, 2 * 60000, 2 * 60000 + 1]] = w[[2 * 60000, 2 * 60000 + 1, 2 * 100, 2 * 100 + 1]]
+    with pytest.raises(N.SbmError) as e:
+        api.dict_image(w, 4)
+    assert e.value.status == -4
+    for p0 in (0.5, 0.8):      # more than 4 nonzeros; 31634 table words
+        with pytest.raises(N.SbmError) as e:
+            api.dict_image(api.build_dictionary(p0)[0], 4)
+        assert e.value.status == -4
+    w857, _ = api.build_dictionary(0.857)
+    with pytest.raises(N.SbmError) as e:
+        api.dict_image(w857)                   # the 3-slot image cannot hold it
+    assert e.value.status == -4
+    with pytest.raises(N.SbmError) as e:
+        N.check(N.lib().sbm_dict_image4(w857.ctypes.data, np.zeros(64, np.uint8).ctypes.data, 64))
+    assert e.value.status == -6
+
+
 def _div_magic(d):
     l = 0
     while (1 << l) < d:
@@ -207,6 +265,7 @@ def test_fused_argument_errors_without_gpu():
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 7, z, z, z, 1, z, 0, z, 0, z) == -2
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 64, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 16 | 8, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 32 | 8, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 0, 4, 8, z, z, z, 1, z, 0, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 0, z, 0, z, 0, z) == 0
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 3, z, 0, z, 0, z) == -1
