@@ -86,9 +86,9 @@ typedef enum {
                              item holds half as many tokens.  Not with SBM_F_MFMA. */
 #define SBM_F_IMAGE4 32u  /* dict_image is a 4-slot image from sbm_dict_image4 (a dictionary built
                              for the data's P(0), whose entries may hold 4 nonzeros); the kernel
-                             gathers 4 activation slots per codeword instead of 3, from an 81 KB
-                             LDS table, which leaves less LDS for activation rows.  Not with
-                             SBM_F_MFMA. */
+                             gathers 4 activation slots per codeword instead of 3, from a 65.5 KB
+                             LDS table, which leaves less LDS for activation rows.  dict_image
+                             must then hold sbm_dict_image4_bytes() bytes.  Not with SBM_F_MFMA. */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);
@@ -124,9 +124,10 @@ int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes);
  * empty) and L / 2 in the top 4 bits; from a split H on, every entry has 3 or
  * 4 nonzeros in aligned groups of 8 that differ only in the signs of their
  * first three nonzeros, stored once.  Requires at most 4 nonzeros per entry
- * and H + (65536 - H) / 8 <= 20800 table words (canonical tables for
- * 0.83 <= p0 < 1).  Host in, host out; SBM_EDICT otherwise.  Use the image
- * with SBM_F_IMAGE4. */
+ * and H + (65536 - H) / 8 <= 16768 table words: canonical tables for
+ * 0.857 <= p0 < 1, which covers the sparsities the page reports for base128,
+ * large128 and c2048 (85.7%, 86.4%, 88.6%).  Host in, host out; SBM_EDICT
+ * otherwise.  Use the image with SBM_F_IMAGE4. */
 size_t sbm_dict_image4_bytes(void);
 int sbm_dict_image4(const uint32_t* words, void* out_image, size_t image_bytes);
 

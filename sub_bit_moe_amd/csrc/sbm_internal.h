@@ -14,7 +14,7 @@ constexpr uint32_t kImageMagic = 0x53424D31u;  // "SBM1"
 constexpr uint32_t kImageVersion = 5;
 constexpr uint32_t kTabEntries = 15360;        // decode-table capacity: 60 KB
 constexpr uint32_t kImage4Version = 6;
-constexpr uint32_t kTab4Entries = 20800;       // 4-slot table capacity: 81.25 KB (p0 >= 0.83)
+constexpr uint32_t kTab4Entries = 16768;       // 4-slot table capacity: 65.5 KB (p0 >= 0.857)
 
 // Decode image of a dictionary (device copy read by the fused kernel): one
 // 32-bit word per codeword says everything the kernel needs,

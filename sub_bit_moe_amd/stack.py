@@ -31,6 +31,7 @@ class StackConfig:
     d_ff: int = 6144
     p0: float = 0.886
     dict_p0: float = 0.885
+    image_slots: int = 3         # 4: the 4-slot decode image (tables built for P(0) < 0.885)
     seed: int = 41
     n_tokens: int = 64
     zipf_s: float = 1.1
@@ -79,7 +80,7 @@ class Stack:
 def build(cfg: StackConfig, device="cuda", log=None) -> Stack:
     import torch
     words, _ = api.build_dictionary(cfg.dict_p0)
-    st = Stack(cfg, api.device_image(words, device))
+    st = Stack(cfg, api.device_image(words, device, cfg.image_slots))
     trie = torch.from_numpy(api.build_trie(words)).to(device)
     table = torch.from_numpy(synth.scale_table().view(np.int16)).to(device)
     for l in range(cfg.n_layers):

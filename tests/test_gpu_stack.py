@@ -64,6 +64,59 @@ def test_generated_codes_bit_exact(dev, odict, gen_state, E, rows, cols, mat, la
         assert stg.host_desc[e].code_base % 8 == 0
 
 
+def test_generated_codes_matched_dictionary(dev, odict_for):
+    """The GPU generator's trie walk under a table built for P(0) = 0.857
+    (entries with 4 nonzeros): codes, offsets and block starts bit-exact with
+    the oracle's encoding under the same table."""
+    from sub_bit_moe_amd import api
+    od = odict_for(0.857)
+    trie = torch.from_numpy(api.build_trie(od["words"])).to(dev)
+    table = torch.from_numpy(synth.scale_table().view(np.int16)).to(dev)
+    E, rows, cols, mat, layer, seed = 3, 96, 3072, 1, 2, 11
+    stg = api.generate_stack(seed, layer, E, mat, rows, cols, 0.857, trie, table)
+    torch.cuda.synchronize()
+    for e in range(E):
+        sym = synth.counter_symbols(synth.matrix_key(seed, layer, e, mat, E), rows, cols, 0.857)
+        codes, row_off, bstart, _ = _host_matrix(stg, e)
+        rc, ro = OC.encode_matrix(sym, od["child"])
+        assert np.array_equal(codes, rc) and np.array_equal(row_off, ro), f"expert {e}"
+        assert np.array_equal(bstart, OC.block_starts(rc, od["lens"], 1024)), f"expert {e}"
+
+
+def test_base128_stack_matched_dictionary_pass(dev):
+    """A 2-layer base128-shaped stack (128 experts, up 3072x768, down
+    768x3072, P(0) = 0.857, 128 Zipf tokens) encoded under the table built for
+    its P(0) and run through the 4-slot image: sampled tokens of every layer
+    against the oracle on the GPU's own inputs (sampled rows; the codes under
+    that table are pinned by the generator test above)."""
+    from sub_bit_moe_amd import stack as S
+    cfg = S.StackConfig(n_layers=2, n_experts=128, d_model=768, d_ff=3072, p0=0.857, dict_p0=0.857,
+                        image_slots=4, seed=11, n_tokens=128)
+    st = S.build(cfg, dev)
+    run = S.Runner(st)
+    keep = {}
+    run.run(keep)
+    torch.cuda.synchronize()
+    assert api_error(run.ws_up) == 0 and api_error(run.ws_down) == 0
+    rng = np.random.default_rng(6)
+    for l in range(cfg.n_layers):
+        xraw, h, y = (t.float().cpu().numpy() for t in keep[l])
+        ids = st.routes_host[l]
+        xin = OM.rms_glue(keep[l - 1][2].float().cpu().numpy()).astype(np.float64) if l else xraw
+        for t in rng.choice(cfg.n_tokens, 4, replace=False):
+            e = int(ids[t])
+            for mat, inp, out, relu in ((0, xin[t], h[t], True), (1, h[t], y[t], False)):
+                rows, cols = (cfg.d_ff, cfg.d_model) if mat == 0 else (cfg.d_model, cfg.d_ff)
+                key = synth.matrix_key(cfg.seed, l, e, mat, cfg.n_experts)
+                rsel = np.sort(rng.choice(rows, 48, replace=False))
+                sym = np.concatenate([synth.counter_symbols(key, 1, cols, cfg.p0, row0=int(r)) for r in rsel])
+                sc = synth.scale_table()[synth.counter_scale_index(key, rows)][rsel]
+                ref = P.oracle_matvec_from_symbols(sym, sc, inp.astype(np.float16)[None, :])[0]
+                if relu:
+                    ref = np.maximum(ref, 0)
+                P.assert_close(out[rsel], ref, what=f"layer {l} token {t} mat {mat}")
+
+
 def test_small_stack_pass_against_oracle(dev, odict):
     """A 3-layer stack of 64 experts with c2048 widths and 64 Zipf tokens: every
     layer's up and down outputs for sampled tokens against the oracle applied

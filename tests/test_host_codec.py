@@ -181,7 +181,7 @@ def test_image_rejects_non_canonical(odict):
     assert e.value.status == -4
 
 
-@pytest.mark.parametrize("p0", [0.857, 0.83, 0.885])
+@pytest.mark.parametrize("p0", [0.857, 0.864, 0.885])
 def test_decode_image4_reproduces_every_codeword(odict_for, p0):
     """The 4-slot image of a table built for P(0) = p0: the fused kernel's
     arithmetic (idx = min(c, (c + 7H) >> 3), word = tab[idx] + spread of the
@@ -226,7 +226,7 @@ def test_image4_rejections(odict):
     with pytest.raises(N.SbmError) as e:
         api.dict_image(w, 4)
     assert e.value.status == -4
-    for p0 in (0.5, 0.8):      # more than 4 nonzeros; 31634 table words
+    for p0 in (0.5, 0.8, 0.856):      # more than 4 nonzeros; 31634 and 18250 table words
         with pytest.raises(N.SbmError) as e:
             api.dict_image(api.build_dictionary(p0)[0], 4)
         assert e.value.status == -4
