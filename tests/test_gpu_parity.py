@@ -520,3 +520,36 @@ def test_fused_image_kind_mismatch_is_flagged(dev, lib_state, odict_for):
         api.moe_fused_decode_matvec(stack, image_t, x, ids, workspace=ws, image4=image4)
         torch.cuda.synchronize()
         assert api.workspace_error(ws) == 0x80000000
+
+
+def test_fused_image4_lds_limits(dev, lib_state, odict_for):
+    """The 4-slot instance's LDS budget (65.5 KB table): a 14000-column row
+    fits, 15000 columns are rejected with SBM_ERANGE, and the per-row min/max
+    grid still fits two activation rows at 6144 columns."""
+    from sub_bit_moe_amd import _native as N
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    od = odict_for(0.857)
+    image4 = api.device_image(od["words"], dev, slots=4)
+    rng = np.random.default_rng(77)
+    for rows, cols, T, minmax in ((40, 14000, 2, False), (50, 6144, 3, True)):
+        print(f"image4 limit {rows}x{cols} minmax={minmax}", flush=True)
+        sym = synth.ternary_symbols(rng, rows, cols, 0.857)
+        sc = synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows)
+        st = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"], od), rows, cols, dev)
+        x = synth.activations(rng, T, cols)
+        ws = api.alloc_workspace(1, T, dev)
+        y = api.moe_fused_decode_matvec(st, image4, torch.from_numpy(x).to(dev),
+                                        torch.zeros(T, dtype=torch.int32, device=dev), workspace=ws,
+                                        out_f32=True, minmax=minmax)
+        torch.cuda.synchronize()
+        assert api.workspace_error(ws) == 0
+        ref = (P.oracle_matvec_minmax_from_symbols(sym, sc, x) if minmax
+               else P.oracle_matvec_from_symbols(sym, sc, x))
+        P.assert_close(y.cpu().numpy().astype(np.float64), ref, what=f"{rows}x{cols}")
+    wide = P.encode_all([(np.zeros((2, 15000), np.uint8), np.ones(2, np.float16))], od["words"])
+    st = api.ExpertStack.from_host(wide, 2, 15000, dev)
+    with pytest.raises(N.SbmError) as e:
+        api.moe_fused_decode_matvec(st, image4, torch.zeros((1, 15000), dtype=torch.float16, device=dev),
+                                    torch.zeros(1, dtype=torch.int32, device=dev))
+    assert e.value.status == -5
