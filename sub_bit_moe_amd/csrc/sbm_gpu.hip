@@ -20,7 +20,10 @@
 //    (the image built on the host); every entry has at most 3 nonzeros, so a
 //    codeword yields its length and 3 "slots" (byte offsets of signed
 //    activations, or of a zero) from one table read plus its sign bits.  Work
-//    scales with nonzeros, never with the 28 symbols of a run.
+//    scales with nonzeros, never with the 28 symbols of a run.  Tables built
+//    for other data hold entries with 4 nonzeros ([QMoE] "Limitations and
+//    Trade-offs": a table per model); their 4-slot image (65.5 KB, 7-bit
+//    slot fields) has kernel instances of its own.
 //  * Positions: lane-local prefix of run lengths plus one wave scan (DPP).
 //  * Accumulate: activations live in LDS as triples [-x, +x, 0] per column
 //    (fp16, up to 4 rows interleaved), so each nonzero is one LDS read and one
