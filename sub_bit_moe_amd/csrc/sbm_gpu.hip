@@ -608,7 +608,7 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
     // Activation gathers in batches of kXB codewords: every address of a batch
     // is formed and its loads issued before the first sum, so up to 15 LDS
     // reads are in flight instead of three.
-    constexpr int kXB = NS == 3 ? (TC == 4 ? 4 : 8) : (TC == 4 ? 2 : 4);
+    constexpr int kXB = NS == 3 ? (TC == 4 ? 4 : 8) : 2;   // 4 slots: measured best at 2
 #pragma unroll
     for (int j0 = 0; j0 < kK; j0 += kXB) {
       XVal<TC> xv[kXB][NS];
