@@ -96,11 +96,25 @@ def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
             done_bytes += 2 * codes.size + 4 * nblk + 2 * rows
             n_done += 1
         reps += 1
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s compressed", "cores": os.cpu_count(),
+    # threads actually used: the decode is numpy on one thread, the fp64 product runs in the BLAS pool
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except ImportError:
+        blas = 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s compressed", "cores": blas,
             "kind": "oracle",
             "sample": f"{len(sample)} touched c2048 matrices of layer 0 (2 experts x up/down, regenerated "
-                      f"and oracle-encoded on the host, untimed), decoded by the reference decoder and "
-                      f"multiplied in fp64 for their routed tokens, {reps} repetitions, {t_total:.1f} s timed"}
+                      f"and oracle-encoded on the host, untimed), decoded by the reference decoder (numpy, "
+                      f"one thread) and multiplied in fp64 (BLAS, {blas} threads) for their routed tokens, "
+                      f"{reps} repetitions, {t_total:.1f} s timed; host CPU: {model or 'unknown'}, "
+                      f"{os.cpu_count()} logical CPUs visible"}
 
 
 def fusion_baselines(st, run, reps: int = 5):
