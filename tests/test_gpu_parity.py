@@ -553,3 +553,45 @@ def test_fused_image4_lds_limits(dev, lib_state, odict_for):
         api.moe_fused_decode_matvec(st, image4, torch.zeros((1, 15000), dtype=torch.float16, device=dev),
                                     torch.zeros(1, dtype=torch.int32, device=dev))
     assert e.value.status == -5
+
+
+def test_fused_image4_random_shapes(dev, lib_state, odict_for):
+    """A seeded sweep through the 4-slot image with the table built for
+    P(0) = 0.857: even widths 2..3000, 1..600 rows, 1..160 tokens over 1..7
+    experts (all three grouping paths), data at P(0) in [0.6, 0.95], both
+    grids, ReLU and fp32 output; every expert's codes bit-exact with the
+    oracle's encoder under that table."""
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    od = odict_for(0.857)
+    image4 = api.device_image(od["words"], dev, slots=4)
+    rng = np.random.default_rng(4242)
+    for case in range(12):
+        cols = int(rng.choice([2, 6, 30, 98, 254, 510, 512, 514, 770, 1026, 2080, 3000]))
+        rows = int(rng.integers(1, 600))
+        E = int(rng.integers(1, 8))
+        T = int(rng.choice([1, 2, 5, 17, 64, 65, 128, 129, 160]))
+        p0 = float(rng.uniform(0.6, 0.95))
+        minmax = bool(case % 3 == 2)
+        relu, out_f32 = bool(case % 2), bool(case % 4 == 1)
+        print(f"image4 case {case}: {rows}x{cols} E={E} T={T} p0={p0:.3f} minmax={minmax}", flush=True)
+        syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
+        scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
+        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), od["words"], od), rows, cols, dev)
+        x = rng.standard_normal((T, cols)).astype(np.float16)
+        ids = rng.integers(0, E, T).astype(np.int32)
+        ws = api.alloc_workspace(E, T, dev)
+        y = api.moe_fused_decode_matvec(stack, image4, torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev),
+                                        relu=relu, out_f32=out_f32, minmax=minmax, workspace=ws)
+        torch.cuda.synchronize()
+        assert api.workspace_error(ws) == 0
+        y = y.float().cpu().numpy().astype(np.float64)
+        for e in range(E):
+            sel = np.nonzero(ids == e)[0]
+            if not sel.size:
+                continue
+            ref = (P.oracle_matvec_minmax_from_symbols(syms[e], scs[e], x[sel]) if minmax
+                   else P.oracle_matvec_from_symbols(syms[e], scs[e], x[sel]))
+            if relu:
+                ref = np.maximum(ref, 0)
+            P.assert_close(y[sel], ref, what=f"case {case} expert {e}")
