@@ -143,3 +143,35 @@ def test_first_codes_reading(odict):
     assert all(not any(s) for s in seqs[:12])
     assert seqs[12:16] == [(1, 0), (2, 0), (0, 1), (0, 2)]
     assert seqs[16] == (0,) * 26 and seqs[25] == (0,) * 28
+
+
+@pytest.mark.parametrize("p0", [0.857, 0.864])
+def test_class_ranges_closed_form_other_p0(odict_for, p0):
+    """Tables built for the sparsities the page reports for base128 and
+    large128 (Table 4: 85.7%, 86.4%): classes (L, n) of C(L,n)*2^n
+    equiprobable sequences taken in decreasing probability until 2^16, each
+    occupying one contiguous codeword range in that order.  At p0 = 0.857 the
+    4-nonzero classes are (4,4), (6,4), (8,4): 16 + 240 + 1120 = 1376 entries."""
+    od = odict_for(p0)
+    lp, lq = math.log(p0), math.log((1 - p0) / 2)
+    classes = sorted(((L, n) for L in range(2, 29, 2) for n in range(L + 1)),
+                     key=lambda c: -((c[0] - c[1]) * lp + c[1] * lq))
+    left, start, ranges = 65536, 0, []
+    for L, n in classes:
+        take = min(left, comb(L, n) * 2 ** n)
+        if take:
+            ranges.append((L, n, start, start + take))
+        start += take
+        left -= take
+    seqs = od["seqs"]
+    for L, n, a, b in ranges:
+        for c in (a, (a + b) // 2, b - 1):
+            s = seqs[c]
+            assert (len(s), sum(1 for v in s if v)) == (L, n), (p0, c, L, n)
+    got4 = {(L, n): b - a for L, n, a, b in ranges if n == 4}
+    n4 = sum(1 for s in seqs if sum(1 for v in s if v) == 4)
+    assert n4 == sum(got4.values())
+    assert max(sum(1 for v in s if v) for s in seqs) == 4
+    if p0 == 0.857:
+        assert got4 == {(4, 4): 16, (6, 4): 240, (8, 4): 1120} and n4 == 1376
+        assert next(a for L, n, a, b in ranges if n == 4) == 34534
