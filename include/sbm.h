@@ -169,6 +169,25 @@ typedef struct {
   int32_t reserved;
 } sbm_matrix_desc;
 
+/* [QMoE] "Encoding" for a whole projection (host): n_mats matrices of one
+ * shape, sym[i] host uint8 [rows x cols] with values 0/1/2, encoded into one
+ * stack in the layout sbm_moe_fused_decode_matvec reads:
+ *   codes:   every matrix's codewords from a base that is a multiple of
+ *            SBM_CODE_ALIGN, the gaps zero (codes_capacity entries);
+ *   row_off: n_mats * (rows + 1) matrix-local offsets;
+ *   bstart:  every matrix's ceil(n/SBM_BLOCK) block starts, concatenated
+ *            (bstart_capacity entries);
+ *   desc:    host sbm_matrix_desc[n_mats], scale_base = i * rows (the caller
+ *            lays out the scales, one or two fp16 per row in matrix order;
+ *            double scale_base for SBM_F_MINMAX).
+ * n_codes_total and n_blocks_total always receive the sizes needed; with a
+ * NULL output or a capacity below them the call returns SBM_ENOSPACE after
+ * writing them (the size query).  The trie is built once for all matrices. */
+int sbm_encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int32_t cols,
+                       const uint32_t* words, uint16_t* codes, uint64_t codes_capacity, uint32_t* row_off,
+                       uint32_t* bstart, uint64_t bstart_capacity, sbm_matrix_desc* desc,
+                       uint64_t* n_codes_total, uint64_t* n_blocks_total);
+
 /* [M8.5] 0x08A reference decode on the GPU: one matrix to symbols.
  * codes, row_off, words, out_sym: device.  out_sym: uint8 [rows x cols].
  * One thread per row expands its codewords from the packed words; a row whose

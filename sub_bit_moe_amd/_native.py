@@ -46,6 +46,8 @@ _SIGS = {
     "sbm_dict_image4": (C.c_int, [P, P, C.c_size_t]),
     "sbm_encode_size": (C.c_int, [P, C.c_int32, C.c_int32, P, P]),
     "sbm_encode_matrix": (C.c_int, [P, C.c_int32, C.c_int32, P, P, C.c_uint64, P, P, P]),
+    "sbm_encode_experts": (C.c_int, [C.c_int32, P, C.c_int32, C.c_int32, P, P, C.c_uint64, P, P, C.c_uint64,
+                                     P, P, P]),
     "sbm_block_starts": (C.c_int, [P, C.c_uint64, P, P]),
     "sbm_validate_stream": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P]),
     "sbm_decode_ref": (C.c_int, [P, P, C.c_int32, C.c_int32, P, P, P, P]),

@@ -77,6 +77,32 @@ def encode_matrix(sym: np.ndarray, words: np.ndarray):
     return codes[:int(n.value)], row_off, bstart[:nblk]
 
 
+def encode_experts(syms, words: np.ndarray):
+    """One projection's matrices (same shape, uint8 0/1/2) encoded natively into
+    the stack layout: (codes uint16 with aligned bases, row_off uint32
+    [E*(rows+1)], bstart uint32, list of MatrixDesc with scale_base = e*rows)."""
+    words = np.ascontiguousarray(words, np.uint32)
+    syms = [np.ascontiguousarray(m, np.uint8) for m in syms]
+    E = len(syms)
+    rows, cols = (syms[0].shape if E else (0, 2))
+    if any(m.shape != (rows, cols) for m in syms):
+        raise ValueError("all matrices of a projection share one shape")
+    ptrs = (C.c_void_p * max(E, 1))(*[m.ctypes.data for m in syms])
+    nc, nb = C.c_uint64(), C.c_uint64()
+    st = lib().sbm_encode_experts(E, ptrs, rows, cols, words.ctypes.data, None, 0, None, None, 0, None,
+                                  C.addressof(nc), C.addressof(nb))
+    if st not in (0, -6):          # -6: SBM_ENOSPACE, the size query
+        check(st)
+    codes = np.zeros(max(int(nc.value), 1), np.uint16)
+    row_off = np.zeros(max(E * (rows + 1), 1), np.uint32)
+    bstart = np.zeros(max(int(nb.value), 1), np.uint32)
+    desc = (N.MatrixDesc * max(E, 1))()
+    check(lib().sbm_encode_experts(E, ptrs, rows, cols, words.ctypes.data, codes.ctypes.data, codes.size,
+                                   row_off.ctypes.data, bstart.ctypes.data, bstart.size, C.addressof(desc),
+                                   C.addressof(nc), C.addressof(nb)))
+    return codes[:int(nc.value)], row_off[:E * (rows + 1)], bstart[:int(nb.value)], list(desc)[:E]
+
+
 def block_starts(codes: np.ndarray, words: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, np.uint16)
     nblk = (codes.size + N.SBM_BLOCK - 1) // N.SBM_BLOCK
@@ -118,9 +144,37 @@ class ExpertStack:
         return 2 * d.n_codes + 4 * nblk + 2 * per_row * self.rows
 
     @staticmethod
-    def from_host(mats, rows: int, cols: int, device="cuda"):
-        """mats: list of (codes uint16, row_off uint32, bstart uint32, scales fp16)."""
+    def from_symbols(syms, scales, words, device="cuda"):
+        """Matrices of one shape (uint8 0/1/2) encoded by sbm_encode_experts and
+        uploaded; scales: per matrix, rows fp16 (or [rows, 2] for the min/max
+        grid, whose descriptors then get doubled scale bases)."""
+        codes, row_off, bstart, descs = encode_experts(syms, words)
+        rows, cols = syms[0].shape
+        sc = [np.asarray(s, np.float16).reshape(-1) for s in scales]
+        per_row = sc[0].size // rows
+        assert all(s.size == per_row * rows for s in sc) and per_row in (1, 2)
+        for d in descs:
+            d.scale_base *= per_row
+        used = 2 * sum(int(d.n_codes) for d in descs)
+        return ExpertStack._upload(rows, cols, descs, codes, row_off, bstart, np.concatenate(sc), used, device)
+
+    @staticmethod
+    def _upload(rows, cols, descs, codes, row_off, bstart, scales, used, device):
         import torch
+        if codes.size == 0:
+            codes = np.zeros(8, np.uint16)
+        if bstart.size == 0:
+            bstart = np.zeros(1, np.uint32)
+        desc_arr = (N.MatrixDesc * len(descs))(*descs)
+        desc_bytes = np.frombuffer(bytes(desc_arr), np.uint8).copy()
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+        return ExpertStack(rows, cols, len(descs), t(codes, np.int16), t(row_off, np.int32),
+                           t(bstart, np.int32), t(scales, np.float16), t(desc_bytes, np.uint8), descs, used)
+
+    @staticmethod
+    def assemble(mats, rows: int, cols: int):
+        """Host stack layout from per-matrix encodings: (descs, codes, row_off,
+        bstart, scales, used bytes)."""
         descs = []
         code_parts, off_parts, blk_parts, sc_parts = [], [], [], []
         cb = ob = sb = bb = 0
@@ -142,14 +196,15 @@ class ExpertStack:
             sb += scales.size
             bb += bstart.size
             used += 2 * n
-        codes = np.concatenate(code_parts) if code_parts else np.zeros(8, np.uint16)
-        desc_arr = (N.MatrixDesc * len(descs))(*descs)
-        desc_bytes = np.frombuffer(bytes(desc_arr), np.uint8).copy()
-        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
-        return ExpertStack(rows, cols, len(descs), t(codes, np.int16),
-                           t(np.concatenate(off_parts), np.int32),
-                           t(np.concatenate(blk_parts) if blk_parts else np.zeros(1, np.uint32), np.int32),
-                           t(np.concatenate(sc_parts), np.float16), t(desc_bytes, np.uint8), descs, used)
+        codes = np.concatenate(code_parts) if code_parts else np.zeros(0, np.uint16)
+        bstart = np.concatenate(blk_parts) if blk_parts else np.zeros(0, np.uint32)
+        return descs, codes, np.concatenate(off_parts), bstart, np.concatenate(sc_parts), used
+
+    @staticmethod
+    def from_host(mats, rows: int, cols: int, device="cuda"):
+        """mats: list of (codes uint16, row_off uint32, bstart uint32, scales fp16)."""
+        descs, codes, row_off, bstart, scales, used = ExpertStack.assemble(mats, rows, cols)
+        return ExpertStack._upload(rows, cols, descs, codes, row_off, bstart, scales, used, device)
 
 
 def device_image(words: np.ndarray, device="cuda", slots: int = 3):

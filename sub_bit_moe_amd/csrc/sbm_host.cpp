@@ -394,6 +394,78 @@ int encode_matrix(const uint8_t* sym, int32_t rows, int32_t cols, const uint32_t
   return SBM_OK;
 }
 
+// A whole projection in the fused kernel's stack layout: one trie for all
+// matrices, every row counted first (sizes, offsets, aligned code bases),
+// then encoded in place.
+int encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int32_t cols,
+                   const uint32_t* words, uint16_t* codes, uint64_t codes_capacity, uint32_t* row_off,
+                   uint32_t* bstart, uint64_t bstart_capacity, sbm_matrix_desc* desc,
+                   uint64_t* n_codes_total, uint64_t* n_blocks_total) {
+  if (n_mats < 0 || (!sym && n_mats > 0) || !words || !n_codes_total || !n_blocks_total)
+    return fail(SBM_EINVAL, "null pointer or negative matrix count");
+  int st;
+  for (int32_t i = 0; i < n_mats; ++i)
+    if ((st = check_matrix(sym[i], rows, cols))) return st;
+  std::vector<int32_t> child;
+  if ((st = build_trie(words, child))) return st;
+  const size_t R1 = (size_t)rows + 1;
+  std::vector<uint32_t> offs((size_t)n_mats * R1);
+  std::vector<uint64_t> base(n_mats), nc(n_mats), blk(n_mats);
+  uint64_t total = 0, blocks = 0;
+  const int nt = n_threads_for(rows);
+  std::vector<uint64_t> counts(rows);
+  for (int32_t i = 0; i < n_mats; ++i) {
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; ++t)
+      th.emplace_back([&, t] {
+        for (int32_t r = t; r < rows; r += nt)
+          counts[r] = encode_row(sym[i] + (size_t)r * cols, cols, child.data(), nullptr);
+      });
+    for (auto& x : th) x.join();
+    uint64_t n = 0;
+    offs[i * R1] = 0;
+    for (int32_t r = 0; r < rows; ++r) {
+      n += counts[r];
+      if (n > 0xFFFFFFFFull) return fail(SBM_ERANGE, "matrix %d: more than 2^32-1 codewords", i);
+      offs[i * R1 + r + 1] = (uint32_t)n;
+    }
+    base[i] = total;
+    nc[i] = n;
+    blk[i] = blocks;
+    total += n + ((SBM_CODE_ALIGN - n % SBM_CODE_ALIGN) % SBM_CODE_ALIGN);
+    blocks += (n + SBM_BLOCK - 1) / SBM_BLOCK;
+  }
+  *n_codes_total = total;
+  *n_blocks_total = blocks;
+  if (!codes || !row_off || !bstart || !desc || total > codes_capacity || blocks > bstart_capacity)
+    return fail(SBM_ENOSPACE, "stack needs %llu codewords and %llu block starts",
+                (unsigned long long)total, (unsigned long long)blocks);
+  std::copy(offs.begin(), offs.end(), row_off);
+  for (int32_t i = 0; i < n_mats; ++i) {
+    uint16_t* out = codes + base[i];
+    const uint32_t* off = offs.data() + i * R1;
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; ++t)
+      th.emplace_back([&, t] {
+        for (int32_t r = t; r < rows; r += nt)
+          encode_row(sym[i] + (size_t)r * cols, cols, child.data(), out + off[r]);
+      });
+    for (auto& x : th) x.join();
+    const uint64_t end = i + 1 < n_mats ? base[i + 1] : total;
+    std::fill(out + nc[i], codes + end, (uint16_t)0);
+    if ((st = block_starts(out, nc[i], words, bstart + blk[i]))) return st;
+    desc[i].code_base = base[i];
+    desc[i].off_base = (uint64_t)i * R1;
+    desc[i].scale_base = (uint64_t)i * (uint64_t)rows;
+    desc[i].blk_base = blk[i];
+    desc[i].n_codes = (uint32_t)nc[i];
+    desc[i].rows = rows;
+    desc[i].cols = cols;
+    desc[i].reserved = 0;
+  }
+  return SBM_OK;
+}
+
 int block_starts(const uint16_t* codes, uint64_t n, const uint32_t* words, uint32_t* bstart) {
   if ((!codes && n) || !words || (!bstart && n)) return fail(SBM_EINVAL, "null pointer");
   uint64_t pos = 0;
@@ -483,6 +555,14 @@ int sbm_encode_matrix(const uint8_t* sym, int32_t rows, int32_t cols, const uint
                       uint16_t* codes, uint64_t capacity, uint32_t* row_off, uint32_t* bstart,
                       uint64_t* n_codes) {
   return sbm::encode_matrix(sym, rows, cols, words, codes, capacity, row_off, bstart, n_codes);
+}
+
+int sbm_encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int32_t cols,
+                       const uint32_t* words, uint16_t* codes, uint64_t codes_capacity, uint32_t* row_off,
+                       uint32_t* bstart, uint64_t bstart_capacity, sbm_matrix_desc* desc,
+                       uint64_t* n_codes_total, uint64_t* n_blocks_total) {
+  return sbm::encode_experts(n_mats, sym, rows, cols, words, codes, codes_capacity, row_off, bstart,
+                             bstart_capacity, desc, n_codes_total, n_blocks_total);
 }
 
 int sbm_block_starts(const uint16_t* codes, uint64_t n_codes, const uint32_t* words,

@@ -80,6 +80,10 @@ int encode_matrix(const uint8_t* sym, int32_t rows, int32_t cols, const uint32_t
                   uint16_t* codes, uint64_t capacity, uint32_t* row_off, uint32_t* bstart,
                   uint64_t* n_codes);
 int block_starts(const uint16_t* codes, uint64_t n, const uint32_t* words, uint32_t* bstart);
+int encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int32_t cols,
+                   const uint32_t* words, uint16_t* codes, uint64_t codes_capacity, uint32_t* row_off,
+                   uint32_t* bstart, uint64_t bstart_capacity, sbm_matrix_desc* desc,
+                   uint64_t* n_codes_total, uint64_t* n_blocks_total);
 int validate_stream(const uint16_t* codes, uint64_t n, const uint32_t* row_off, int32_t rows,
                     int32_t cols, const uint32_t* words);
 void div_magic(uint32_t d, uint64_t* m, uint32_t* shift);

@@ -273,3 +273,47 @@ def test_fused_argument_errors_without_gpu():
     assert L.sbm_decode_ref(z, z, 3, 5, z, z, z, z) == -2
     assert L.sbm_decode_ref(z, z, 0, 4, z, z, z, z) == 0
     assert L.sbm_workspace_bytes(10, 5) >= 4 * (16 + 10 + 11 + 11 + 5)
+
+
+@pytest.mark.parametrize("E,rows,cols,p0,dict_p0", [(5, 70, 514, 0.886, 0.885), (1, 1, 2, 0.886, 0.885),
+                                                    (3, 300, 2080, 0.857, 0.857), (2, 0, 30, 0.886, 0.885)])
+def test_encode_experts_layout(odict_for, E, rows, cols, p0, dict_p0):
+    """The native whole-projection encoder against per-matrix encodes
+    assembled by the binding: same aligned code bases, padding, offsets, block
+    starts and descriptors; the first matrix's codes bit-exact with the
+    oracle's encoder."""
+    od = odict_for(dict_p0)
+    w = od["words"]
+    rng = np.random.default_rng(rows + E)
+    syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
+    scs = [synth.row_scales(rng, rows) for _ in range(E)]
+    codes, row_off, bstart, descs = api.encode_experts(syms, w)
+    ref = api.ExpertStack.assemble([api.encode_matrix(s, w) + (sc,) for s, sc in zip(syms, scs)], rows, cols)
+    assert np.array_equal(codes, ref[1]) and np.array_equal(row_off, ref[2]) and np.array_equal(bstart, ref[3])
+    assert [bytes(a) for a in descs] == [bytes(b) for b in ref[0]]
+    assert all(d.code_base % N.SBM_CODE_ALIGN == 0 for d in descs)
+    if rows:
+        rc, ro = OC.encode_matrix(syms[0], od["child"])
+        d = descs[0]
+        assert np.array_equal(codes[d.code_base:d.code_base + d.n_codes], rc)
+        assert np.array_equal(row_off[:rows + 1], ro)
+
+
+def test_encode_experts_errors(odict):
+    w = odict["words"]
+    L = N.lib()
+    bad = np.zeros((2, 8), np.uint8)
+    bad[1, 3] = 3
+    odd = np.zeros((2, 7), np.uint8)
+    nc, nb = C.c_uint64(), C.c_uint64()
+    for m, status in ((bad, -1), (odd, -2)):
+        ptrs = (C.c_void_p * 1)(m.ctypes.data)
+        assert L.sbm_encode_experts(1, ptrs, m.shape[0], m.shape[1], w.ctypes.data, None, 0, None, None, 0, None,
+                                    C.addressof(nc), C.addressof(nb)) == status
+    good = np.full((3, 64), 2, np.uint8)                  # all nonzero: 32 codewords per row
+    ptrs = (C.c_void_p * 2)(good.ctypes.data, good.ctypes.data)
+    assert L.sbm_encode_experts(2, ptrs, 3, 64, w.ctypes.data, None, 0, None, None, 0, None,
+                                C.addressof(nc), C.addressof(nb)) == -6
+    assert nc.value == 2 * 96 and nb.value == 2      # 96 per matrix, already a multiple of 8
+    with pytest.raises(ValueError):
+        api.encode_experts([good, np.zeros((3, 62), np.uint8)], w)
