@@ -362,6 +362,14 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # per-replay spread (a separate loop, outside the timed region above)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     comp, bf16 = st.pass_bytes()
     value = comp / (ms * 1e-3) / 1e9
     log(f"pass {ms:.3f} ms, {value:.1f} GB/s compressed, {bf16 / (ms * 1e-3) / 1e9:.1f} GB/s bf16-equivalent")
@@ -425,6 +433,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(per[len(per) // 2], 4),
+        "ms_per_step_min": round(per[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
