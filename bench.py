@@ -303,6 +303,98 @@ def dictionary_match(steps, warmup):
     return out
 
 
+def decompress_hybrid(steps, warmup, thresholds=(16, 32)):
+    """Heavy experts through decompress-then-GEMM ([QMoE] suggests decompressing
+    for large batches; the two-launch form of the dense-tile idea): one c2048
+    layer of 2048 experts with 256 Zipf tokens (the heaviest expert gets ~50).
+    Experts with at least T* tokens: sbm_decode_dense of up and down to fp16
+    {-1, 0, +1}, then library fp16 GEMMs (torch.nn.functional.linear, fp32
+    accumulation) with the row scales and ReLU applied after; the other tokens
+    go through the fused kernel.  Timed like the main pass (graph replays), next
+    to the fused path alone and the opt-in dense-tile MFMA instance."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    from sub_bit_moe_amd import api, stack as S
+    cfg = S.StackConfig(n_layers=1, n_experts=2048, n_tokens=256, seed=31)
+    st = S.build(cfg, torch.device("cuda:0"))
+    up, down = st.up[0], st.down[0]
+    ids_h = st.routes_host[0]
+    ids, x = st.routes[0], st.x0
+    T = cfg.n_tokens
+    dev = x.device
+    counts = np.bincount(ids_h, minlength=cfg.n_experts)
+    ws_u, ws_d = api.alloc_workspace(cfg.n_experts, T, dev), api.alloc_workspace(cfg.n_experts, T, dev)
+    h = torch.empty(T, cfg.d_ff, dtype=torch.float16, device=dev)
+    y = torch.empty(T, cfg.d_model, dtype=torch.float16, device=dev)
+
+    def fused(mfma=False):
+        api.moe_fused_decode_matvec(up, st.image, x, ids, relu=True, workspace=ws_u, y=h, mfma=mfma)
+        api.moe_fused_decode_matvec(down, st.image, h, ids, workspace=ws_d, y=y, mfma=mfma)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / steps
+
+    out = {"workload": "one c2048 layer: 2048 experts, up 6144x2080 + down 2080x6144, P(0)=0.886, 256 fp16 "
+                       "tokens, top-1 Zipf(1.1)", "max_tokens_per_expert": int(counts.max()),
+           "fused_us": round(timed(fused), 1), "fused_mfma_us": round(timed(lambda: fused(True)), 1)}
+    y_fused = None
+    fused()
+    torch.cuda.synchronize()
+    y_fused = y.float().clone()
+    for ts in thresholds:
+        heavy = [int(e) for e in np.flatnonzero(counts >= ts)]
+        light = np.flatnonzero(~np.isin(ids_h, heavy))
+        light_t = torch.from_numpy(light.astype(np.int64)).to(dev)
+        toks = {e: torch.from_numpy(np.flatnonzero(ids_h == e).astype(np.int64)).to(dev) for e in heavy}
+        wu = {e: torch.empty(cfg.d_ff, cfg.d_model, dtype=torch.float16, device=dev) for e in heavy}
+        wd = {e: torch.empty(cfg.d_model, cfg.d_ff, dtype=torch.float16, device=dev) for e in heavy}
+        su = {e: up.scales[up.host_desc[e].scale_base:up.host_desc[e].scale_base + up.rows] for e in heavy}
+        sd = {e: down.scales[down.host_desc[e].scale_base:down.host_desc[e].scale_base + down.rows] for e in heavy}
+        bad = torch.zeros(1, dtype=torch.int32, device=dev)
+        nl = int(light.size)
+        hl = torch.empty(max(nl, 1), cfg.d_ff, dtype=torch.float16, device=dev)
+        yl = torch.empty(max(nl, 1), cfg.d_model, dtype=torch.float16, device=dev)
+
+        def hybrid():
+            if nl:
+                xl, il = x.index_select(0, light_t), ids.index_select(0, light_t)
+                api.moe_fused_decode_matvec(up, st.image, xl, il, relu=True, workspace=ws_u, y=hl[:nl])
+                api.moe_fused_decode_matvec(down, st.image, hl[:nl], il, workspace=ws_d, y=yl[:nl])
+                y.index_copy_(0, light_t, yl[:nl])
+            for e in heavy:
+                api.decode_dense(up, e, st.image, out=wu[e], bad=bad)
+                api.decode_dense(down, e, st.image, out=wd[e], bad=bad)
+                he = torch.relu(F.linear(x.index_select(0, toks[e]), wu[e]) * su[e])
+                y.index_copy_(0, toks[e], F.linear(he, wd[e]) * sd[e])
+
+        us = timed(hybrid)
+        hybrid()
+        torch.cuda.synchronize()
+        rel = float((y.float() - y_fused).norm() / y_fused.norm())
+        out[f"hybrid_T{ts}"] = {"heavy_experts": len(heavy), "heavy_tokens": int(counts[heavy].sum()),
+                                "us": round(us, 1), "vs_fused": round(us / out["fused_us"], 3),
+                                "rel_l2_vs_fused": round(rel, 5), "bad_image": int(bad.item())}
+        del wu, wd
+    del st
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +409,8 @@ def main():
                     help="skip the pass on the page's per-row (w_min, w_max) grid")
     ap.add_argument("--no-dict-match", action="store_true",
                     help="skip the table-built-for-the-data comparison (base128-shaped stack at P(0)=0.857)")
+    ap.add_argument("--no-hybrid", action="store_true",
+                    help="skip the decompress-then-GEMM comparison for heavy experts (one c2048 layer, 256 tokens)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-size kernel for scaling "
                          "hardware byte counters)")
@@ -415,6 +509,12 @@ def main():
         log(f"per layer: static {dmatch['static_3slot']['us_per_layer']} us, matched "
             f"{dmatch['matched_4slot']['us_per_layer']} us, static via 4 slots "
             f"{dmatch['static_4slot']['us_per_layer']} us")
+    hybrid = None
+    if not args.no_hybrid:
+        log("heavy experts: decompress-then-GEMM against the fused path (one c2048 layer, 256 tokens) ...")
+        hybrid = decompress_hybrid(args.steps, args.warmup)
+        log(f"hybrid: fused {hybrid['fused_us']} us, MFMA {hybrid['fused_mfma_us']} us, "
+            + ", ".join(f"{k} {v['us']} us" for k, v in hybrid.items() if k.startswith("hybrid_")))
     fusion = None
     if not args.no_fusion_baselines:
         log("fusion baselines (layer 0: unfused decode -> bf16 -> GEMM, dense bf16 GEMM) ...")
@@ -453,6 +553,7 @@ def main():
         "fusion_baselines": fusion,
         "minmax_grid": minmax,
         "dictionary_match": dmatch,
+        "decompress_hybrid": hybrid,
     }
     print(json.dumps(out), flush=True)
 

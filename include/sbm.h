@@ -188,6 +188,20 @@ int sbm_encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, 
                        uint32_t* bstart, uint64_t bstart_capacity, sbm_matrix_desc* desc,
                        uint64_t* n_codes_total, uint64_t* n_blocks_total);
 
+/* Decompression for the two-launch path ([QMoE] "The GPU Decoding Kernel":
+ * decompress, then multiply, is what the fused kernel avoids): one matrix to
+ * dense row-major fp16 values -1, 0, +1 (the row scale is left for the GEMM's
+ * epilogue, so the output is exact).  codes: device, the matrix's n_codes
+ * codewords (n_codes >= 1, < 2^32); bstart: device, its ceil(n_codes/SBM_BLOCK)
+ * block starts; dict_image: device copy of sbm_dict_image() output;
+ * out_fp16: device [rows x cols], 4-byte aligned, every element written;
+ * bad: device uint32 set to 1 if the image fails its header check (then
+ * nothing is written; the caller zeroes it beforehand).  rows * cols < 2^32,
+ * cols even.  One wave per 1024-codeword block: coalesced zero-fill of the
+ * block's element span, then a store per nonzero. */
+int sbm_decode_dense(const uint16_t* codes, uint64_t n_codes, const uint32_t* bstart, int32_t rows,
+                     int32_t cols, const void* dict_image, uint16_t* out_fp16, uint32_t* bad, void* stream);
+
 /* [M8.5] 0x08A reference decode on the GPU: one matrix to symbols.
  * codes, row_off, words, out_sym: device.  out_sym: uint8 [rows x cols].
  * One thread per row expands its codewords from the packed words; a row whose

@@ -51,6 +51,7 @@ _SIGS = {
     "sbm_block_starts": (C.c_int, [P, C.c_uint64, P, P]),
     "sbm_validate_stream": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P]),
     "sbm_decode_ref": (C.c_int, [P, P, C.c_int32, C.c_int32, P, P, P, P]),
+    "sbm_decode_dense": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P, P, P, P]),
     "sbm_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "sbm_moe_fused_decode_matvec": (C.c_int, [P, P, P, P, P, C.c_int32, C.c_int32, C.c_int32, P,
                                               P, P, C.c_int32, P, C.c_uint32, P, C.c_size_t, P]),

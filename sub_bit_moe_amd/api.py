@@ -225,6 +225,20 @@ def decode_ref(codes_t, row_off_t, rows: int, cols: int, words_t, stream=None, o
     return out, bad
 
 
+def decode_dense(stack: "ExpertStack", e: int, image_t, out=None, bad=None, stream=None):
+    """Expert e's matrix of a stack decoded to dense fp16 {-1, 0, +1}
+    [rows, cols] (sbm_decode_dense; the row scales are not applied)."""
+    import torch
+    d = stack.host_desc[e]
+    if out is None:
+        out = torch.empty((stack.rows, stack.cols), dtype=torch.float16, device=stack.codes.device)
+    if bad is None:
+        bad = torch.zeros(1, dtype=torch.int32, device=stack.codes.device)
+    check(lib().sbm_decode_dense(_ptr(stack.codes[d.code_base:]), int(d.n_codes), _ptr(stack.bstart[d.blk_base:]),
+                                 stack.rows, stack.cols, _ptr(image_t), _ptr(out), _ptr(bad), _stream(stream)))
+    return out, bad
+
+
 def workspace_bytes(n_experts: int, n_tokens: int) -> int:
     return int(lib().sbm_workspace_bytes(n_experts, n_tokens))
 

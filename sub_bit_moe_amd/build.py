@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsbm.so")
 
-SOURCES = ["sbm_host.cpp", "sbm_gpu.hip", "sbm_gen.hip"]
+SOURCES = ["sbm_host.cpp", "sbm_gpu.hip", "sbm_gen.hip", "sbm_dense.hip"]
 ARCH = os.environ.get("SBM_OFFLOAD_ARCH", "gfx950")
 
 

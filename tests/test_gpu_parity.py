@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+from oracle import codec as OC
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -626,3 +627,34 @@ def test_stack_from_native_encoder_matches(dev, lib_state, odict):
                 ref = (P.oracle_matvec_minmax_from_symbols(syms[e], scs[e], xh[sel]) if minmax
                        else P.oracle_matvec_from_symbols(syms[e], scs[e], xh[sel]))
                 P.assert_close(y[sel], ref, what=f"minmax={minmax} expert {e}")
+
+
+def test_decode_dense_bit_exact(dev, lib_state, odict):
+    """sbm_decode_dense against the oracle's decode: every element of every
+    matrix of a stack (nonzero code bases; ragged, narrow and c2048 shapes)
+    is the fp16 of -1, 0 or +1 for codes 1, 0, 2; a damaged image header
+    writes nothing and sets the flag."""
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    rng = np.random.default_rng(31)
+    to_f16 = np.array([0.0, -1.0, 1.0], np.float16)
+    for E, rows, cols, p0 in ((3, 37, 30, 0.886), (2, 5, 2, 0.5), (3, 129, 2080, 0.857), (2, 768, 3072, 0.886),
+                              (1, 6144, 2080, 0.886)):
+        print(f"decode_dense E={E} {rows}x{cols} p0={p0}", flush=True)
+        syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
+        st = api.ExpertStack.from_symbols(syms, [synth.row_scales(rng, rows) for _ in range(E)], odict["words"], dev)
+        for e in range(E):
+            out, bad = api.decode_dense(st, e, lib_state["image_t"])
+            torch.cuda.synchronize()
+            assert int(bad.item()) == 0
+            d = st.host_desc[e]
+            codes = st.codes[d.code_base:d.code_base + d.n_codes].cpu().numpy().view(np.uint16)
+            row_off = st.row_off[d.off_base:d.off_base + rows + 1].cpu().numpy().view(np.uint32)
+            ref = OC.decode_symbols_with_table(codes, row_off, odict["sym28"], odict["lens"], cols)
+            assert np.array_equal(ref, syms[e])
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), to_f16[ref].view(np.uint16)), (rows, cols, e)
+    bad_image = torch.zeros_like(lib_state["image_t"])
+    sentinel = torch.full((st.rows, st.cols), 7.0, dtype=torch.float16, device=dev)
+    out, bad = api.decode_dense(st, 0, bad_image, out=sentinel)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 1 and bool((out == 7.0).all())

@@ -271,6 +271,11 @@ def test_fused_argument_errors_without_gpu():
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 3, z, 0, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 1 << 23, 6144, z, z, z, 1, z, 0, z, 0, z) == -5
     assert L.sbm_decode_ref(z, z, 3, 5, z, z, z, z) == -2
+    assert L.sbm_decode_dense(z, 10, z, 3, 5, z, z, z, z) == -2          # odd width
+    assert L.sbm_decode_dense(z, 0, z, 0, 4, z, z, z, z) == 0            # no rows: nothing to do
+    assert L.sbm_decode_dense(z, 0, z, 3, 4, z, z, z, z) == -1           # rows without codewords
+    assert L.sbm_decode_dense(z, 10, z, 1 << 20, 1 << 12, z, z, z, z) == -5   # positions beyond 32 bits
+    assert L.sbm_decode_dense(z, 10, z, 3, 4, z, z, z, z) == -1          # null pointers
     assert L.sbm_decode_ref(z, z, 0, 4, z, z, z, z) == 0
     assert L.sbm_workspace_bytes(10, 5) >= 4 * (16 + 10 + 11 + 11 + 5)
 
