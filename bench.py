@@ -314,8 +314,8 @@ def decompress_hybrid(steps, warmup, thresholds=(16, 32)):
     to the fused path alone and the opt-in dense-tile MFMA instance."""
     import numpy as np
     import torch
-    import torch.nn.functional as F
     from sub_bit_moe_amd import api, stack as S
+    from sub_bit_moe_amd import hybrid as hybrid_mod
     cfg = S.StackConfig(n_layers=1, n_experts=2048, n_tokens=256, seed=31)
     st = S.build(cfg, torch.device("cuda:0"))
     up, down = st.up[0], st.down[0]
@@ -363,8 +363,6 @@ def decompress_hybrid(steps, warmup, thresholds=(16, 32)):
         toks = {e: torch.from_numpy(np.flatnonzero(ids_h == e).astype(np.int64)).to(dev) for e in heavy}
         wu = {e: torch.empty(cfg.d_ff, cfg.d_model, dtype=torch.float16, device=dev) for e in heavy}
         wd = {e: torch.empty(cfg.d_model, cfg.d_ff, dtype=torch.float16, device=dev) for e in heavy}
-        su = {e: up.scales[up.host_desc[e].scale_base:up.host_desc[e].scale_base + up.rows] for e in heavy}
-        sd = {e: down.scales[down.host_desc[e].scale_base:down.host_desc[e].scale_base + down.rows] for e in heavy}
         bad = torch.zeros(1, dtype=torch.int32, device=dev)
         nl = int(light.size)
         hl = torch.empty(max(nl, 1), cfg.d_ff, dtype=torch.float16, device=dev)
@@ -377,10 +375,9 @@ def decompress_hybrid(steps, warmup, thresholds=(16, 32)):
                 api.moe_fused_decode_matvec(down, st.image, hl[:nl], il, workspace=ws_d, y=yl[:nl])
                 y.index_copy_(0, light_t, yl[:nl])
             for e in heavy:
-                api.decode_dense(up, e, st.image, out=wu[e], bad=bad)
-                api.decode_dense(down, e, st.image, out=wd[e], bad=bad)
-                he = torch.relu(F.linear(x.index_select(0, toks[e]), wu[e]) * su[e])
-                y.index_copy_(0, toks[e], F.linear(he, wd[e]) * sd[e])
+                ye, _ = hybrid_mod.expert_ffn(up, down, e, st.image, x.index_select(0, toks[e]), wu=wu[e], wd=wd[e],
+                                              bad=bad)
+                y.index_copy_(0, toks[e], ye)
 
         us = timed(hybrid)
         hybrid()

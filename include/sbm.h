@@ -166,7 +166,11 @@ typedef struct {
   uint32_t n_codes;     /* codewords of the matrix */
   int32_t rows;
   int32_t cols;
-  int32_t reserved;
+  uint32_t dict_tag;    /* identity of the dictionary the codes were encoded with: the low 32 bits of
+                           its FNV-1a 64 checksum ([M8.5] 0x08B: the codebook checksum belongs to the
+                           artefact, since a reordered codebook corrupts every index).  The fused
+                           kernel and the dense decoder compare it with the decode image's checksum
+                           and refuse the matrix on a mismatch. */
 } sbm_matrix_desc;
 
 /* [QMoE] "Encoding" for a whole projection (host): n_mats matrices of one
@@ -179,7 +183,8 @@ typedef struct {
  *            (bstart_capacity entries);
  *   desc:    host sbm_matrix_desc[n_mats], scale_base = i * rows (the caller
  *            lays out the scales, one or two fp16 per row in matrix order;
- *            double scale_base for SBM_F_MINMAX).
+ *            double scale_base for SBM_F_MINMAX), dict_tag = the low 32 bits
+ *            of the FNV-1a 64 checksum of `words`.
  * n_codes_total and n_blocks_total always receive the sizes needed; with a
  * NULL output or a capacity below them the call returns SBM_ENOSPACE after
  * writing them (the size query).  The trie is built once for all matrices. */
@@ -196,11 +201,14 @@ int sbm_encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, 
  * block starts; dict_image: device copy of sbm_dict_image() output;
  * out_fp16: device [rows x cols], 4-byte aligned, every element written;
  * bad: device uint32 set to 1 if the image fails its header check (then
- * nothing is written; the caller zeroes it beforehand).  rows * cols < 2^32,
- * cols even.  One wave per 1024-codeword block: coalesced zero-fill of the
- * block's element span, then a store per nonzero. */
+ * nothing is written; the caller zeroes it beforehand) and set to 2 if
+ * dict_tag (the matrix descriptor's dictionary tag) differs from the low 32
+ * bits of the image's dictionary checksum (nothing is written either).
+ * rows * cols < 2^32, cols even.  One wave per 1024-codeword block: coalesced
+ * zero-fill of the block's element span, then a store per nonzero. */
 int sbm_decode_dense(const uint16_t* codes, uint64_t n_codes, const uint32_t* bstart, int32_t rows,
-                     int32_t cols, const void* dict_image, uint16_t* out_fp16, uint32_t* bad, void* stream);
+                     int32_t cols, const void* dict_image, uint32_t dict_tag, uint16_t* out_fp16, uint32_t* bad,
+                     void* stream);
 
 /* [M8.5] 0x08A reference decode on the GPU: one matrix to symbols.
  * codes, row_off, words, out_sym: device.  out_sym: uint8 [rows x cols].
@@ -219,11 +227,14 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  * -s_r, +s_r, or w_min, w_max with SBM_F_MINMAX) (rows x cols, the same shape for all
  * experts of the call) decoded from its code stream without materialising it.
  * Experts without tokens are skipped.  Tokens with an id outside [0, n_experts)
- * produce no output row and are counted in the workspace error word.
+ * produce no output row and are counted in the workspace error word; so are
+ * tokens routed to an expert whose descriptor disagrees with the call (shape,
+ * alignment) or whose dict_tag differs from the image's dictionary checksum:
+ * those produce no output row either, and set bits 30 / 29 of that word.
  *   codes/row_off/bstart/scales: device arrays addressed through `experts`;
  *               a matrix's codes are read in whole dwords (after an odd count,
  *               the 2 bytes sharing the last codeword's dword are read and ignored)
- *   experts:    device sbm_matrix_desc[n_experts]
+ *   experts:    device sbm_matrix_desc[n_experts] (dict_tag = the image's dictionary)
  *   dict_image: device copy of sbm_dict_image() output (sbm_dict_image4() with SBM_F_IMAGE4);
  *               an image of the other kind, or a damaged one, sets the workspace error word
  *   x:          device fp16 [n_tokens x cols];  expert_ids: device int32 [n_tokens]
@@ -265,9 +276,11 @@ int sbm_gen_count(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
                   uint32_t zero_threshold16, const int32_t* trie, uint32_t* row_counts, void* stream);
 
 /* Row offsets (E*(rows+1), matrix-local), matrix descriptors (E) and totals
- * (uint64[2]: codewords including per-matrix alignment padding, blocks). */
+ * (uint64[2]: codewords including per-matrix alignment padding, blocks).
+ * dict_checksum: FNV-1a 64 checksum of the dictionary the trie was built
+ * from (its low 32 bits become every descriptor's dict_tag). */
 int sbm_gen_layout(const uint32_t* row_counts, int32_t n_experts, int32_t rows, int32_t cols, uint32_t* row_off,
-                   sbm_matrix_desc* desc, uint64_t* totals, void* stream);
+                   sbm_matrix_desc* desc, uint64_t* totals, uint64_t dict_checksum, void* stream);
 
 /* Pass 2: codewords, block starts and row scales into arrays sized from totals. */
 int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, int32_t rows, int32_t cols,
@@ -281,10 +294,11 @@ int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
 int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint16_t* x_out, void* stream);
 
 /* Workspace error word of the last fused call (device read; synchronises the
- * stream).  Bits 0-29: number of tokens whose expert id was out of range;
- * bit 30: a touched expert's descriptor disagrees with the call's shape or
- * alignment (its tokens get no output); bit 31: the decode image failed its
- * header check (nothing was computed). */
+ * stream).  Bits 0-28: number of tokens whose expert id was out of range;
+ * bit 29: a touched expert's dict_tag differs from the image's dictionary
+ * checksum (its tokens get no output); bit 30: a touched expert's descriptor
+ * disagrees with the call's shape or alignment (its tokens get no output);
+ * bit 31: the decode image failed its header check (nothing was computed). */
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream);
 
 #ifdef __cplusplus

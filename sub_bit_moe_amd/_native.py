@@ -31,7 +31,7 @@ class SbmError(RuntimeError):
 class MatrixDesc(C.Structure):
     _fields_ = [("code_base", C.c_uint64), ("off_base", C.c_uint64), ("scale_base", C.c_uint64),
                 ("blk_base", C.c_uint64), ("n_codes", C.c_uint32), ("rows", C.c_int32),
-                ("cols", C.c_int32), ("reserved", C.c_int32)]
+                ("cols", C.c_int32), ("dict_tag", C.c_uint32)]
 
 
 P = C.c_void_p
@@ -51,7 +51,7 @@ _SIGS = {
     "sbm_block_starts": (C.c_int, [P, C.c_uint64, P, P]),
     "sbm_validate_stream": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P]),
     "sbm_decode_ref": (C.c_int, [P, P, C.c_int32, C.c_int32, P, P, P, P]),
-    "sbm_decode_dense": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P, P, P, P]),
+    "sbm_decode_dense": (C.c_int, [P, C.c_uint64, P, C.c_int32, C.c_int32, P, C.c_uint32, P, P, P]),
     "sbm_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "sbm_moe_fused_decode_matvec": (C.c_int, [P, P, P, P, P, C.c_int32, C.c_int32, C.c_int32, P,
                                               P, P, C.c_int32, P, C.c_uint32, P, C.c_size_t, P]),
@@ -61,7 +61,7 @@ _SIGS = {
     "sbm_build_trie": (C.c_int, [P, P]),
     "sbm_gen_count": (C.c_int, [C.c_uint64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                 C.c_uint32, P, P, P]),
-    "sbm_gen_layout": (C.c_int, [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]),
+    "sbm_gen_layout": (C.c_int, [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, C.c_uint64, P]),
     "sbm_gen_write": (C.c_int, [C.c_uint64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                 C.c_uint32, P, P, P, P, P, P, P, P]),
 }

@@ -45,6 +45,12 @@ def dictionary_checksum(words: np.ndarray) -> int:
     return int(cs.value)
 
 
+def dict_tag(words: np.ndarray) -> int:
+    """Dictionary identity carried by every matrix descriptor: the low 32 bits
+    of the dictionary's FNV-1a 64 checksum (also in the decode image header)."""
+    return dictionary_checksum(words) & 0xFFFFFFFF
+
+
 def dict_image(words: np.ndarray, slots: int = 3) -> np.ndarray:
     """Compact decode image (uint8 bytes) for the fused kernel: slots=3 for
     tables whose entries hold at most 3 nonzeros (the page's static table),
@@ -172,8 +178,9 @@ class ExpertStack:
                            t(bstart, np.int32), t(scales, np.float16), t(desc_bytes, np.uint8), descs, used)
 
     @staticmethod
-    def assemble(mats, rows: int, cols: int):
-        """Host stack layout from per-matrix encodings: (descs, codes, row_off,
+    def assemble(mats, rows: int, cols: int, dict_tag: int):
+        """Host stack layout from per-matrix encodings made with the dictionary
+        whose tag is dict_tag (api.dict_tag(words)): (descs, codes, row_off,
         bstart, scales, used bytes)."""
         descs = []
         code_parts, off_parts, blk_parts, sc_parts = [], [], [], []
@@ -184,7 +191,7 @@ class ExpertStack:
             # one scale per row, or (w_min, w_max) per row for the min/max grid
             assert row_off.size == rows + 1 and scales.size in (rows, 2 * rows)
             d = N.MatrixDesc(code_base=cb, off_base=ob, scale_base=sb, blk_base=bb, n_codes=n,
-                             rows=rows, cols=cols, reserved=0)
+                             rows=rows, cols=cols, dict_tag=dict_tag)
             descs.append(d)
             pad = (-n) % N.SBM_CODE_ALIGN
             code_parts.append(np.concatenate([codes.astype(np.uint16), np.zeros(pad, np.uint16)]))
@@ -201,9 +208,10 @@ class ExpertStack:
         return descs, codes, np.concatenate(off_parts), bstart, np.concatenate(sc_parts), used
 
     @staticmethod
-    def from_host(mats, rows: int, cols: int, device="cuda"):
-        """mats: list of (codes uint16, row_off uint32, bstart uint32, scales fp16)."""
-        descs, codes, row_off, bstart, scales, used = ExpertStack.assemble(mats, rows, cols)
+    def from_host(mats, rows: int, cols: int, device="cuda", *, dict_tag: int):
+        """mats: list of (codes uint16, row_off uint32, bstart uint32, scales fp16),
+        encoded with the dictionary whose tag is dict_tag (api.dict_tag(words))."""
+        descs, codes, row_off, bstart, scales, used = ExpertStack.assemble(mats, rows, cols, dict_tag)
         return ExpertStack._upload(rows, cols, descs, codes, row_off, bstart, scales, used, device)
 
 
@@ -235,7 +243,8 @@ def decode_dense(stack: "ExpertStack", e: int, image_t, out=None, bad=None, stre
     if bad is None:
         bad = torch.zeros(1, dtype=torch.int32, device=stack.codes.device)
     check(lib().sbm_decode_dense(_ptr(stack.codes[d.code_base:]), int(d.n_codes), _ptr(stack.bstart[d.blk_base:]),
-                                 stack.rows, stack.cols, _ptr(image_t), _ptr(out), _ptr(bad), _stream(stream)))
+                                 stack.rows, stack.cols, _ptr(image_t), int(d.dict_tag), _ptr(out), _ptr(bad),
+                                 _stream(stream)))
     return out, bad
 
 
@@ -295,9 +304,10 @@ def build_trie(words: np.ndarray) -> np.ndarray:
 
 
 def generate_stack(seed: int, layer: int, n_experts: int, mat: int, rows: int, cols: int, p0: float,
-                   trie_t, scale_table_t, stream=None) -> ExpertStack:
+                   trie_t, scale_table_t, stream=None, *, dict_checksum: int) -> ExpertStack:
     """Generate and encode n_experts counter-based matrices on the GPU
-    (count pass, row offsets, descriptors, write pass) as an ExpertStack."""
+    (count pass, row offsets, descriptors, write pass) as an ExpertStack;
+    dict_checksum: the checksum of the dictionary the trie was built from."""
     import torch
     from . import synth
     dev = trie_t.device
@@ -308,7 +318,8 @@ def generate_stack(seed: int, layer: int, n_experts: int, mat: int, rows: int, c
     row_off = torch.empty(n_experts * (rows + 1), dtype=torch.int32, device=dev)
     desc = torch.empty(n_experts * C.sizeof(N.MatrixDesc), dtype=torch.uint8, device=dev)
     totals = torch.zeros(2, dtype=torch.int64, device=dev)
-    check(lib().sbm_gen_layout(_ptr(counts), n_experts, rows, cols, _ptr(row_off), _ptr(desc), _ptr(totals), s))
+    check(lib().sbm_gen_layout(_ptr(counts), n_experts, rows, cols, _ptr(row_off), _ptr(desc), _ptr(totals),
+                               C.c_uint64(dict_checksum), s))
     tot = totals.cpu().tolist()
     codes = torch.empty(max(int(tot[0]), 8), dtype=torch.int16, device=dev)
     bstart = torch.empty(max(int(tot[1]), 1), dtype=torch.int32, device=dev)

@@ -41,13 +41,18 @@ __global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const uint16_t*
                                                                  uint32_t n_codes,
                                                                  const uint32_t* __restrict__ bstart,
                                                                  uint64_t n_elems, const DictImage* __restrict__ im,
-                                                                 uint16_t* __restrict__ out, uint32_t* bad) {
+                                                                 uint32_t dict_tag, uint16_t* __restrict__ out,
+                                                                 uint32_t* bad) {
   __shared__ uint32_t tab[kTabEntries];
   const uint4 hdr = *(const uint4*)im;       // magic, version, split H, n_tab (the same for every thread)
   const bool ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
                   hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
   if (!ok) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *bad = 1u;
+    return;
+  }
+  if ((uint32_t)im->checksum != dict_tag) {      // codes of another dictionary: decoding would mislabel them
+    if (blockIdx.x == 0 && threadIdx.x == 0) *bad = 2u;
     return;
   }
   for (uint32_t i = threadIdx.x; i < hdr.w; i += kDThreads) tab[i] = im->tab[i];
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const uint16_t*
 using namespace sbm;
 
 extern "C" int sbm_decode_dense(const uint16_t* codes, uint64_t n_codes, const uint32_t* bstart, int32_t rows,
-                                int32_t cols, const void* dict_image, uint16_t* out_fp16, uint32_t* bad,
-                                void* stream) {
+                                int32_t cols, const void* dict_image, uint32_t dict_tag, uint16_t* out_fp16,
+                                uint32_t* bad, void* stream) {
   if (rows < 0 || cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", rows, cols);
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if (rows == 0) return SBM_OK;
@@ -119,7 +124,7 @@ extern "C" int sbm_decode_dense(const uint16_t* codes, uint64_t n_codes, const u
   const uint64_t want = (nblk + kDWaves - 1) / kDWaves;
   const unsigned grid = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(want, 2ull * (uint64_t)cus));
   hipLaunchKernelGGL(decode_dense_kernel, dim3(grid), dim3(kDThreads), 0, (hipStream_t)stream, codes,
-                     (uint32_t)n_codes, bstart, n_elems, (const DictImage*)dict_image, out_fp16, bad);
+                     (uint32_t)n_codes, bstart, n_elems, (const DictImage*)dict_image, dict_tag, out_fp16, bad);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "decode_dense launch: %s", hipGetErrorString(e));
   return SBM_OK;

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(1024) void gen_row_scan(const uint32_t* __restrict_
 // Matrix descriptors: codeword bases (multiples of SBM_CODE_ALIGN), block
 // bases and the total, from the per-matrix codeword counts (one workgroup).
 __global__ __launch_bounds__(1024) void gen_desc(const uint32_t* __restrict__ row_off, int32_t E, int32_t rows,
-                                                 int32_t cols, sbm_matrix_desc* __restrict__ desc,
+                                                 int32_t cols, uint32_t dict_tag, sbm_matrix_desc* __restrict__ desc,
                                                  uint64_t* __restrict__ totals) {
   __shared__ uint64_t pc[1024], pb[1024];
   const int32_t per = (E + 1023) / 1024;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(1024) void gen_desc(const uint32_t* __restrict__ ro
     d.n_codes = (uint32_t)n;
     d.rows = rows;
     d.cols = cols;
-    d.reserved = 0;
+    d.dict_tag = dict_tag;
     desc[e] = d;
     rc += (n + SBM_CODE_ALIGN - 1) / SBM_CODE_ALIGN * SBM_CODE_ALIGN;
     rb += (n + SBM_BLOCK - 1) / SBM_BLOCK;
@@ -242,12 +242,13 @@ int sbm_gen_count(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
 }
 
 int sbm_gen_layout(const uint32_t* row_counts, int32_t n_experts, int32_t rows, int32_t cols, uint32_t* row_off,
-                   sbm_matrix_desc* desc, uint64_t* totals, void* stream) {
+                   sbm_matrix_desc* desc, uint64_t* totals, uint64_t dict_checksum, void* stream) {
   if (!row_counts || !row_off || !desc || !totals || n_experts <= 0 || rows <= 0 || cols <= 0)
     return fail(SBM_EINVAL, "bad layout arguments");
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(gen_row_scan, dim3(n_experts), dim3(1024), 0, s, row_counts, rows, row_off);
-  hipLaunchKernelGGL(gen_desc, dim3(1), dim3(1024), 0, s, row_off, n_experts, rows, cols, desc, totals);
+  hipLaunchKernelGGL(gen_desc, dim3(1), dim3(1024), 0, s, row_off, n_experts, rows, cols, (uint32_t)dict_checksum,
+                     desc, totals);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "gen_layout launch: %s", hipGetErrorString(e));
   return SBM_OK;

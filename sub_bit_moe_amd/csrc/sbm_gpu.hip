@@ -87,7 +87,8 @@ constexpr uint32_t kMfmaWeight = 24;    // slice weight of one row of an MFMA it
 constexpr int kMaxRmax = 4096;    // rows per chunk
 constexpr int kEpiRegs = (kMaxRmax + 2 + kFThreads - 1) / kFThreads;   // epilogue slots per thread
 constexpr int kGroupInLds = 128;  // up to this many tokens are grouped inside the fused kernel
-constexpr uint32_t kErrBadDesc = 0x40000000u, kErrBadImage = 0x80000000u;
+constexpr uint32_t kErrDict = 0x20000000u, kErrBadDesc = 0x40000000u, kErrBadImage = 0x80000000u;
+constexpr uint32_t kErrCountMask = 0x1FFFFFFFu;   // bits 0-28: tokens with an expert id out of range
 struct WsLayout {
   uint64_t cnt, start, chunk, perm, items, bounds, total_words;
 };
@@ -130,6 +131,7 @@ struct FusedArgs {
   uint32_t lds_racc;    // byte offsets in LDS
   uint32_t lds_x;
   int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
+  uint32_t dict_tag;    // low 32 bits of the image's dictionary checksum (read by the kernel)
 };
 
 // ------------------------------------------------------------ wave helpers
@@ -261,10 +263,14 @@ __device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint
   return boundary_in_item(u, (uint64_t)w0 * R + (uint64_t)lo * F, lo, w1 > w0 ? w1 - w0 : 1u, F, R);
 }
 
-// A matrix descriptor the fused kernel can use for a call of this shape.
-__device__ __forceinline__ bool desc_ok(const sbm_matrix_desc& d, int32_t rows, int32_t cols, int32_t minmax) {
-  return (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols &&
-         (!minmax || (d.scale_base & 1u) == 0);     // (w_min, w_max) pairs are read as one dword
+// Why a matrix descriptor cannot be used for a call of this shape with this
+// decode image: kErrBadDesc (shape, alignment), kErrDict (its codes were
+// encoded with another dictionary, [M8.5] 0x08B), or 0.
+__device__ __forceinline__ uint32_t desc_err(const sbm_matrix_desc& d, int32_t rows, int32_t cols, int32_t minmax,
+                                             uint32_t dict_tag) {
+  const bool shape = (d.code_base % SBM_CODE_ALIGN) == 0 && d.rows == rows && d.cols == cols &&
+                     (!minmax || (d.scale_base & 1u) == 0);     // (w_min, w_max) pairs are read as one dword
+  return (shape ? 0u : kErrBadDesc) | (d.dict_tag == dict_tag ? 0u : kErrDict);
 }
 
 constexpr uint32_t kRowWeight1 = 4;   // slice weight of a one-token row
@@ -302,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
                                                          int32_t E, int32_t titem, int32_t rows, int32_t cols,
                                                          int32_t grid, uint32_t item_cost, int32_t mfma, int32_t minmax,
                                                          const sbm_matrix_desc* __restrict__ experts,
+                                                         const DictImage* __restrict__ image,
                                                          uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh_tot[kWaves + 1];
   const WsLayout L = ws_layout(E, T);
@@ -311,6 +318,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   uint32_t* chunk = ws + L.chunk;
   int32_t* perm = (int32_t*)(ws + L.perm);
   uint4* items = (uint4*)(ws + L.items);
+  const uint32_t dict_tag = (uint32_t)image->checksum;
   for (int i = threadIdx.x; i < (int)kWsHdr; i += kThreads) hdr[i] = 0;
   for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
   __syncthreads();
@@ -359,7 +367,10 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
       const uint32_t nt = ((n - k) < span ? (n - k) : span) | (heavy ? kItemMfma : 0u);
       items[q] = make_uint4((uint32_t)e, s0 + k, nt, item_weight(nt, minmax));
     }
-    if (n && !desc_ok(experts[e], rows, cols, minmax)) atomicOr(&hdr[0], kErrBadDesc);
+    if (n) {
+      const uint32_t err = desc_err(experts[e], rows, cols, minmax, dict_tag);
+      if (err) atomicOr(&hdr[0], err);
+    }
   }
   __syncthreads();
   // exclusive prefix of the per-row weights over items (.w), total in hdr[2]
@@ -487,7 +498,7 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   ch.nt = it.z & ~kItemMfma;
   ch.mfma = (it.z & kItemMfma) != 0;
   const sbm_matrix_desc d = a.experts[it.x];
-  ch.ok = desc_ok(d, a.rows, a.cols, a.minmax);
+  ch.ok = desc_err(d, a.rows, a.cols, a.minmax, a.dict_tag) == 0;
   ch.code_base = d.code_base;
   ch.n_codes = d.n_codes;
   ch.blk_base = d.blk_base;
@@ -1568,9 +1579,10 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols, a.minmax)) atomicOr(&s_ghdr[3], 1u);
+      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, a.dict_tag))
+        atomicOr(&s_ghdr[3], err);
     __syncthreads();
-    if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
+    if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
   }
 }
 
@@ -1666,9 +1678,10 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (!desc_ok(a.experts[s_items[q].x], a.rows, a.cols, a.minmax)) atomicOr(&s_ghdr[3], 1u);
+      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, a.dict_tag))
+        atomicOr(&s_ghdr[3], err);
     __syncthreads();
-    if (threadIdx.x == 0) a.ws[0] = ((uint32_t)T - s_ghdr[2]) | (s_ghdr[3] ? kErrBadDesc : 0u);
+    if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
   }
 }
 
@@ -1690,6 +1703,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
   const int32_t my_id = a.ids[tq];
   const uint4 hdr = *(const uint4*)a.image;       // magic, version, split, n_tab
+  a.dict_tag = (uint32_t)a.image->checksum;       // same scalar cache line as the header
   stage_tables_dma<NS>(a.image);
   // the table indexes stay below n_tab <= the table's capacity for every codeword
   const bool image_ok = hdr.x == kImageMagic && hdr.y == (NS == 3 ? kImageVersion : kImage4Version) &&
@@ -1703,7 +1717,9 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
     else group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
     if (!image_ok) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = kErrBadImage;   // after the grouping's write
+      // the same thread wrote the grouping's word: keep its id count and shape
+      // bit; the dictionary comparison was made against a damaged header
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
       return;               // (s_endpgm waits for the table copy still in flight, as on an empty slice)
     }
     g0 = s_slice[0];
@@ -1711,8 +1727,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     perm = s_perm;
     items = s_items;
   } else {
-    if (!image_ok) {
-      if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ws[0], kErrBadImage);
+    if (!image_ok) {   // group_kernel's word is complete (stream order); its dictionary bit is void
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
       return;
     }
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
@@ -1842,7 +1858,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
                                 const int32_t* expert_ids, int32_t n_tokens, void* y,
                                 uint32_t flags, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  if (n_tokens < 0 || n_experts <= 0 || n_experts > (1 << 24))
+  if (n_tokens < 0 || n_tokens > (int32_t)kErrCountMask || n_experts <= 0 || n_experts > (1 << 24))
     return fail(SBM_EINVAL, "bad n_tokens=%d or n_experts=%d", n_tokens, n_experts);
   if (rows <= 0 || rows > (1 << 24) || cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", rows, cols);
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
@@ -1914,6 +1930,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
   // dense MFMA tiles for heavy experts reuse the same dynamic LDS
   a.mfma_rows = 0;
+  a.dict_tag = 0;        // the kernel reads it from the image
   for (int R : {64, 32, 16})
     if ((flags & SBM_F_MFMA) && mfma_lds(R, cols).total <= lds) {
       a.mfma_rows = R;
@@ -1924,7 +1941,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   if (!a.group_in_lds) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
                        a.titem, rows, cols, (int32_t)grid, a.item_cost, (int32_t)(a.mfma_rows > 0), a.minmax, experts,
-                       (uint32_t*)workspace);
+                       (const DictImage*)dict_image, (uint32_t*)workspace);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
   }

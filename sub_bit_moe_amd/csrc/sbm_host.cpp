@@ -441,6 +441,7 @@ int encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int3
     return fail(SBM_ENOSPACE, "stack needs %llu codewords and %llu block starts",
                 (unsigned long long)total, (unsigned long long)blocks);
   std::copy(offs.begin(), offs.end(), row_off);
+  const uint32_t tag = (uint32_t)checksum(words);   // the descriptors name their dictionary
   for (int32_t i = 0; i < n_mats; ++i) {
     uint16_t* out = codes + base[i];
     const uint32_t* off = offs.data() + i * R1;
@@ -461,7 +462,7 @@ int encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, int3
     desc[i].n_codes = (uint32_t)nc[i];
     desc[i].rows = rows;
     desc[i].cols = cols;
-    desc[i].reserved = 0;
+    desc[i].dict_tag = tag;
   }
   return SBM_OK;
 }

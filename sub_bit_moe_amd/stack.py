@@ -79,13 +79,15 @@ class Stack:
 
 def build(cfg: StackConfig, device="cuda", log=None) -> Stack:
     import torch
-    words, _ = api.build_dictionary(cfg.dict_p0)
+    words, checksum = api.build_dictionary(cfg.dict_p0)
     st = Stack(cfg, api.device_image(words, device, cfg.image_slots))
     trie = torch.from_numpy(api.build_trie(words)).to(device)
     table = torch.from_numpy(synth.scale_table().view(np.int16)).to(device)
     for l in range(cfg.n_layers):
-        st.up.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 0, cfg.d_ff, cfg.d_model, cfg.p0, trie, table))
-        st.down.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 1, cfg.d_model, cfg.d_ff, cfg.p0, trie, table))
+        st.up.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 0, cfg.d_ff, cfg.d_model, cfg.p0, trie, table,
+                                           dict_checksum=checksum))
+        st.down.append(api.generate_stack(cfg.seed, l, cfg.n_experts, 1, cfg.d_model, cfg.d_ff, cfg.p0, trie, table,
+                                             dict_checksum=checksum))
         if log:
             log(f"layer {l + 1}/{cfg.n_layers} generated")
     routes = np.stack([synth.zipf_routing(np.random.default_rng(cfg.seed * 1000 + l), cfg.n_tokens,

@@ -61,7 +61,7 @@ def _run(lib_state, experts, rows, cols, x, ids, dev, odict, relu=False, out_f32
          mfma=False):
     api = lib_state["api"]
     mats = P.encode_all(experts, odict["words"], odict, check_every)
-    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     it = torch.from_numpy(np.asarray(ids, np.int32)).to(dev)
     ws = api.alloc_workspace(stack.n_experts, x.shape[0], dev)
@@ -97,7 +97,7 @@ def test_fused_input_rms(dev, lib_state, odict, rows, cols, T):
     api = lib_state["api"]
     E = 3
     ex = P.host_experts(E, rows, cols, 0.886, rows + 7)
-    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev)
+    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     rng = np.random.default_rng(cols)
     x = (rng.standard_normal((T, cols)) * rng.uniform(0.01, 40, (T, 1))).astype(np.float16)
     x[1] = 0
@@ -190,7 +190,7 @@ def test_fused_invalid_ids_are_skipped_and_counted(dev, lib_state, odict, T):
     E, rows, cols = 3, 64, 256
     ex = P.host_experts(E, rows, cols, 0.886, 5)
     mats = P.encode_all(ex, odict["words"])
-    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     x = np.random.default_rng(1).standard_normal((T, cols)).astype(np.float16)
     ids = np.random.default_rng(2).integers(0, E, T).astype(np.int32)
     ids[:4] = [0, -1, 7, 2]
@@ -216,7 +216,7 @@ def test_fused_bad_descriptor_is_flagged(dev, lib_state, odict, T):
     api = lib_state["api"]
     E, rows, cols = 3, 64, 256
     ex = P.host_experts(E, rows, cols, 0.886, 6)
-    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev)
+    stack = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     descs = list(stack.host_desc)
     descs[1].rows = rows + 1
     arr = (N.MatrixDesc * E)(*descs)
@@ -316,7 +316,7 @@ def test_fused_minmax_grid(dev, lib_state, odict, rows, cols, T, E):
     syms = [synth.ternary_symbols(rng, rows, cols, 0.886) for _ in range(E)]
     mms = [synth.row_minmax(rng, rows) for _ in range(E)]
     mats = P.encode_all(list(zip(syms, mms)), odict["words"], odict)
-    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     x = rng.standard_normal((T, cols)).astype(np.float16)
     ids = (np.arange(T) * 7 + T) % E
     ids = ids.astype(np.int32)
@@ -355,7 +355,7 @@ def test_fused_minmax_input_rms_and_symmetric_case(dev, lib_state, odict):
     for e in range(E):
         sel = np.nonzero(ids == e)[0]
         ref[sel] = P.oracle_matvec_minmax_from_codes(odict, syms[e], mms[e], xn[sel])
-    stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, mms)), odict["words"]), rows, cols, dev)
+    stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, mms)), odict["words"]), rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     xt, it = torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev)
     y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], xt, it, in_rms=True, out_f32=True, minmax=True)
     torch.cuda.synchronize()
@@ -364,9 +364,9 @@ def test_fused_minmax_input_rms_and_symmetric_case(dev, lib_state, odict):
     ss = [synth.row_scales(rng, rows) for _ in range(E)]
     mats1 = P.encode_all(list(zip(syms, ss)), odict["words"])
     mats2 = [(c, o, b, np.stack([-s, s], axis=1)) for (c, o, b, s) in mats1]
-    y1 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats1, rows, cols, dev), lib_state["image_t"],
+    y1 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats1, rows, cols, dev, dict_tag=api.dict_tag(odict["words"])), lib_state["image_t"],
                                      xt, it, out_f32=True)
-    y2 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats2, rows, cols, dev), lib_state["image_t"],
+    y2 = api.moe_fused_decode_matvec(api.ExpertStack.from_host(mats2, rows, cols, dev, dict_tag=api.dict_tag(odict["words"])), lib_state["image_t"],
                                      xt, it, out_f32=True, minmax=True)
     torch.cuda.synchronize()
     P.assert_close(y2.cpu().numpy().astype(np.float64), y1.cpu().numpy().astype(np.float64), 1e-5, 1e-4,
@@ -391,7 +391,7 @@ def test_fused_size_limits(dev, lib_state, odict):
     P.assert_close(y, P.oracle_matvec_from_symbols(ex[0][0], ex[0][1], x), what="cols=15000")
     # too wide for LDS: rejected before any launch
     wide = P.encode_all([(np.zeros((2, 16384), np.uint8), np.ones(2, np.float16))], odict["words"])
-    st = api.ExpertStack.from_host(wide, 2, 16384, dev)
+    st = api.ExpertStack.from_host(wide, 2, 16384, dev, dict_tag=api.dict_tag(odict["words"]))
     with pytest.raises(N.SbmError) as e:
         api.moe_fused_decode_matvec(st, lib_state["image_t"], torch.zeros((1, 16384), dtype=torch.float16, device=dev),
                                     torch.zeros(1, dtype=torch.int32, device=dev))
@@ -402,7 +402,7 @@ def test_fused_size_limits(dev, lib_state, odict):
     sym = synth.ternary_symbols(rng, rows, cols, 0.886)
     sc = synth.row_scales(rng, rows)
     codes, row_off, bstart = api.encode_matrix(sym, odict["words"])
-    st = api.ExpertStack.from_host([(codes, row_off, bstart, sc)], rows, cols, dev)
+    st = api.ExpertStack.from_host([(codes, row_off, bstart, sc)], rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
     x = rng.standard_normal((T, cols)).astype(np.float16)
     yt = api.moe_fused_decode_matvec(st, lib_state["image_t"], torch.from_numpy(x).to(dev),
                                      torch.zeros(T, dtype=torch.int32, device=dev), out_f32=True)
@@ -432,7 +432,7 @@ def test_fused_random_shapes(dev, lib_state, odict):
         print(f"case {case}: {rows}x{cols} E={E} T={T} p0={p0:.3f} minmax={minmax}", flush=True)
         syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
         scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
-        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), odict["words"]), rows, cols, dev)
+        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), odict["words"]), rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
         x = rng.standard_normal((T, cols)).astype(np.float16)
         ids = rng.integers(0, E, T).astype(np.int32)
         y = api.moe_fused_decode_matvec(stack, lib_state["image_t"], torch.from_numpy(x).to(dev),
@@ -474,7 +474,7 @@ def test_fused_image4_matched_dictionary(dev, lib_state, odict_for, p0, rows, co
     scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
     big = rows * cols > 500_000
     mats = P.encode_all(list(zip(syms, scs)), od["words"], od, check_every=E if big else 1)
-    stack = api.ExpertStack.from_host(mats, rows, cols, dev)
+    stack = api.ExpertStack.from_host(mats, rows, cols, dev, dict_tag=api.dict_tag(od["words"]))
     image4 = api.device_image(od["words"], dev, slots=4)
     x = synth.activations(rng, T, cols)
     ids = synth.zipf_routing(rng, T, E)
@@ -506,7 +506,7 @@ def test_fused_image_kind_mismatch_is_flagged(dev, lib_state, odict_for):
     api = lib_state["api"]
     od = odict_for(0.857)
     sym, sc = P.host_experts(1, 64, 256, 0.857, 9)[0]
-    stack = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"]), 64, 256, dev)
+    stack = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"]), 64, 256, dev, dict_tag=api.dict_tag(od["words"]))
     from sub_bit_moe_amd import synth
     from sub_bit_moe_amd import _native as N
     x = torch.from_numpy(synth.activations(np.random.default_rng(9), 3, 256)).to(dev)
@@ -537,7 +537,7 @@ def test_fused_image4_lds_limits(dev, lib_state, odict_for):
         print(f"image4 limit {rows}x{cols} minmax={minmax}", flush=True)
         sym = synth.ternary_symbols(rng, rows, cols, 0.857)
         sc = synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows)
-        st = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"], od), rows, cols, dev)
+        st = api.ExpertStack.from_host(P.encode_all([(sym, sc)], od["words"], od), rows, cols, dev, dict_tag=api.dict_tag(od["words"]))
         x = synth.activations(rng, T, cols)
         ws = api.alloc_workspace(1, T, dev)
         y = api.moe_fused_decode_matvec(st, image4, torch.from_numpy(x).to(dev),
@@ -549,7 +549,7 @@ def test_fused_image4_lds_limits(dev, lib_state, odict_for):
                else P.oracle_matvec_from_symbols(sym, sc, x))
         P.assert_close(y.cpu().numpy().astype(np.float64), ref, what=f"{rows}x{cols}")
     wide = P.encode_all([(np.zeros((2, 15000), np.uint8), np.ones(2, np.float16))], od["words"])
-    st = api.ExpertStack.from_host(wide, 2, 15000, dev)
+    st = api.ExpertStack.from_host(wide, 2, 15000, dev, dict_tag=api.dict_tag(od["words"]))
     with pytest.raises(N.SbmError) as e:
         api.moe_fused_decode_matvec(st, image4, torch.zeros((1, 15000), dtype=torch.float16, device=dev),
                                     torch.zeros(1, dtype=torch.int32, device=dev))
@@ -578,7 +578,7 @@ def test_fused_image4_random_shapes(dev, lib_state, odict_for):
         print(f"image4 case {case}: {rows}x{cols} E={E} T={T} p0={p0:.3f} minmax={minmax}", flush=True)
         syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
         scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
-        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), od["words"], od), rows, cols, dev)
+        stack = api.ExpertStack.from_host(P.encode_all(list(zip(syms, scs)), od["words"], od), rows, cols, dev, dict_tag=api.dict_tag(od["words"]))
         x = rng.standard_normal((T, cols)).astype(np.float16)
         ids = rng.integers(0, E, T).astype(np.int32)
         ws = api.alloc_workspace(E, T, dev)
@@ -614,7 +614,7 @@ def test_stack_from_native_encoder_matches(dev, lib_state, odict):
         scs = [synth.row_minmax(rng, rows) if minmax else synth.row_scales(rng, rows) for _ in range(E)]
         a = api.ExpertStack.from_symbols(syms, scs, odict["words"], dev)
         b = api.ExpertStack.from_host([api.encode_matrix(s, odict["words"]) + (sc,) for s, sc in zip(syms, scs)],
-                                      rows, cols, dev)
+                                      rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
         ya = api.moe_fused_decode_matvec(a, lib_state["image_t"], x, ids, minmax=minmax)
         yb = api.moe_fused_decode_matvec(b, lib_state["image_t"], x, ids, minmax=minmax)
         torch.cuda.synchronize()
@@ -658,3 +658,107 @@ def test_decode_dense_bit_exact(dev, lib_state, odict):
     out, bad = api.decode_dense(st, 0, bad_image, out=sentinel)
     torch.cuda.synchronize()
     assert int(bad.item()) == 1 and bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("T", [5, 90, 150])
+def test_fused_dictionary_mismatch_is_flagged(dev, lib_state, odict_for, T):
+    """[M8.5] 0x08B: codes are only meaningful with the dictionary they were
+    encoded under.  A stack encoded under the table built for P(0) = 0.857,
+    run with the page's static table (its 4-slot image, which the kernel can
+    otherwise execute, and its 3-slot image), is refused: error bit 29, no
+    output rows.  In a mixed stack only the mislabelled expert is refused."""
+    import ctypes
+    from sub_bit_moe_amd import _native as N
+    api = lib_state["api"]
+    od, os_ = odict_for(0.857), odict_for(0.885)
+    E, rows, cols = 3, 64, 256
+    ex = P.host_experts(E, rows, cols, 0.857, 12)
+    x = np.random.default_rng(13).standard_normal((T, cols)).astype(np.float16)
+    ids = (np.arange(T) % E).astype(np.int32)
+    xt, it = torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev)
+    st857 = api.ExpertStack.from_host(P.encode_all(ex, od["words"]), rows, cols, dev, dict_tag=api.dict_tag(od["words"]))
+    for image_t, image4 in ((api.device_image(os_["words"], dev, slots=4), True), (lib_state["image_t"], False)):
+        y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+        ws = api.alloc_workspace(E, T, dev)
+        api.moe_fused_decode_matvec(st857, image_t, xt, it, out_f32=True, workspace=ws, y=y, image4=image4)
+        torch.cuda.synchronize()
+        assert api.workspace_error(ws) == 0x20000000
+        assert bool(torch.isnan(y).all())
+    # the same table's image computes them exactly
+    y = api.moe_fused_decode_matvec(st857, api.device_image(od["words"], dev, slots=4), xt, it, out_f32=True)
+    torch.cuda.synchronize()
+    for t in range(min(T, 6)):
+        P.assert_close(y[t].cpu().numpy(), P.oracle_matvec_from_symbols(*ex[ids[t]], x[t:t + 1])[0])
+    # static-table stack with expert 1 labelled as encoded under the 0.857 table
+    ex2 = P.host_experts(E, rows, cols, 0.886, 14)
+    st = api.ExpertStack.from_host(P.encode_all(ex2, os_["words"]), rows, cols, dev, dict_tag=api.dict_tag(os_["words"]))
+    descs = list(st.host_desc)
+    descs[1].dict_tag = api.dict_tag(od["words"])
+    arr = (N.MatrixDesc * E)(*descs)
+    st.desc.copy_(torch.from_numpy(np.frombuffer(bytes(arr), np.uint8).copy()))
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+    ws = api.alloc_workspace(E, T, dev)
+    api.moe_fused_decode_matvec(st, lib_state["image_t"], xt, it, out_f32=True, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 0x20000000
+    yn = y.cpu().numpy()
+    assert np.isnan(yn[ids == 1]).all()
+    for t in np.flatnonzero(ids != 1)[:8]:
+        P.assert_close(yn[t], P.oracle_matvec_from_symbols(*ex2[ids[t]], x[t:t + 1])[0])
+    # the dense decoder refuses a matrix of another dictionary and writes nothing
+    sentinel = torch.full((rows, cols), 7.0, dtype=torch.float16, device=dev)
+    out, bad = api.decode_dense(st857, 0, lib_state["image_t"], out=sentinel)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 2 and bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("T", [9, 100, 140])
+def test_fused_bad_image_keeps_id_count(dev, lib_state, odict, T):
+    """A damaged image with out-of-range ids: the error word keeps the id
+    count (from whichever grouping path ran) and adds bit 31; no row is written."""
+    api = lib_state["api"]
+    E, rows, cols = 3, 64, 256
+    ex = P.host_experts(E, rows, cols, 0.886, 15)
+    st = api.ExpertStack.from_host(P.encode_all(ex, odict["words"]), rows, cols, dev, dict_tag=api.dict_tag(odict["words"]))
+    ids = (np.arange(T) % E).astype(np.int32)
+    ids[:3] = [-1, E, 1 << 20]
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+    ws = api.alloc_workspace(E, T, dev)
+    bad_image = torch.zeros_like(lib_state["image_t"])
+    x = torch.from_numpy(np.random.default_rng(16).standard_normal((T, cols)).astype(np.float16)).to(dev)
+    api.moe_fused_decode_matvec(st, bad_image, x, torch.from_numpy(ids).to(dev), out_f32=True, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == (0x80000000 | 3)
+    assert bool(torch.isnan(y).all())
+
+
+@pytest.mark.parametrize("T", [16, 44])
+def test_decompress_gemm_expert_matches_oracle(dev, lib_state, odict, T):
+    """The two-launch path for a heavy expert ([QMoE] "Limitations and
+    Trade-offs": decompress, then multiply on the matrix cores): one c2048 pair
+    (up 6144x2080, down 2080x6144, P(0)=0.886) decoded by sbm_decode_dense and
+    multiplied by library fp16 GEMMs, against the oracle's own encode +
+    reference decode + fp64 product; the down projection on the GPU's h."""
+    from sub_bit_moe_amd import hybrid, synth
+    api = lib_state["api"]
+    rng = np.random.default_rng(41 + T)
+    up = (synth.ternary_symbols(rng, 6144, 2080, 0.886), synth.row_scales(rng, 6144))
+    down = (synth.ternary_symbols(rng, 2080, 6144, 0.886), synth.row_scales(rng, 2080))
+    tag = api.dict_tag(odict["words"])
+    su = api.ExpertStack.from_symbols([up[0]], [up[1]], odict["words"], dev)
+    sd = api.ExpertStack.from_symbols([down[0]], [down[1]], odict["words"], dev)
+    assert su.host_desc[0].dict_tag == tag
+    x = synth.activations(np.random.default_rng(42 + T), T, 2080)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    y, h = hybrid.expert_ffn(su, sd, 0, lib_state["image_t"], torch.from_numpy(x).to(dev), bad=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    hn = h.float().cpu().numpy().astype(np.float64)
+    yn = y.float().cpu().numpy().astype(np.float64)
+    ref_h = np.maximum(P.oracle_matvec_from_codes(odict, up[0], up[1], x), 0)
+    ref_y = P.oracle_matvec_from_codes(odict, down[0], down[1], h.cpu().numpy())
+    P.assert_close(hn, ref_h, what="decompress-then-GEMM up")
+    P.assert_close(yn, ref_y, what="decompress-then-GEMM down")
+    for t in range(T):
+        P.assert_close(hn[t], ref_h[t], what=f"up t={t}")
+        P.assert_close(yn[t], ref_y[t], what=f"down t={t}")

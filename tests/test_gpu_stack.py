@@ -49,7 +49,8 @@ def test_generated_codes_bit_exact(dev, odict, gen_state, E, rows, cols, mat, la
     print(f"gen E={E} {rows}x{cols} mat={mat} layer={layer}", flush=True)
     api, trie, table = gen_state
     seed = 41
-    stg = api.generate_stack(seed, layer, E, mat, rows, cols, p0, trie, table)
+    stg = api.generate_stack(seed, layer, E, mat, rows, cols, p0, trie, table,
+                             dict_checksum=api.dictionary_checksum(odict["words"]))
     torch.cuda.synchronize()
     for e in range(E):
         key = synth.matrix_key(seed, layer, e, mat, E)
@@ -62,6 +63,7 @@ def test_generated_codes_bit_exact(dev, odict, gen_state, E, rows, cols, mat, la
         exp_sc = synth.scale_table()[synth.counter_scale_index(key, rows)]
         assert np.array_equal(scales.view(np.uint16), exp_sc.view(np.uint16)), f"expert {e}: scales"
         assert stg.host_desc[e].code_base % 8 == 0
+        assert stg.host_desc[e].dict_tag == api.dict_tag(odict["words"])
 
 
 def test_generated_codes_matched_dictionary(dev, odict_for):
@@ -73,7 +75,8 @@ def test_generated_codes_matched_dictionary(dev, odict_for):
     trie = torch.from_numpy(api.build_trie(od["words"])).to(dev)
     table = torch.from_numpy(synth.scale_table().view(np.int16)).to(dev)
     E, rows, cols, mat, layer, seed = 3, 96, 3072, 1, 2, 11
-    stg = api.generate_stack(seed, layer, E, mat, rows, cols, 0.857, trie, table)
+    stg = api.generate_stack(seed, layer, E, mat, rows, cols, 0.857, trie, table,
+                             dict_checksum=api.dictionary_checksum(od["words"]))
     torch.cuda.synchronize()
     for e in range(E):
         sym = synth.counter_symbols(synth.matrix_key(seed, layer, e, mat, E), rows, cols, 0.857)

@@ -14,12 +14,26 @@ from sub_bit_moe_amd import api, synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _fnv1a64(words):
+def _fnv1a64_bytes(data: bytes) -> int:
+    """FNV-1a 64 from its published definition (offset basis, prime)."""
     h = 0xCBF29CE484222325
-    for b in np.asarray(words, np.uint32).astype("<u4").tobytes():
+    for b in data:
         h ^= b
         h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
     return h
+
+
+def _fnv1a64(words):
+    return _fnv1a64_bytes(np.asarray(words, np.uint32).astype("<u4").tobytes())
+
+
+def test_fnv1a64_published_vectors():
+    """The checker's FNV-1a 64 against the test vectors of the FNV authors'
+    reference suite, so the library's dictionary checksum is pinned to the
+    published function and not to a copy of itself."""
+    assert _fnv1a64_bytes(b"") == 0xCBF29CE484222325
+    assert _fnv1a64_bytes(b"a") == 0xAF63DC4C8601EC8C
+    assert _fnv1a64_bytes(b"foobar") == 0x85944171F73967E8
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,10 +50,6 @@ def test_dictionary_bit_exact_with_oracle(odict):
     words, cs = api.build_dictionary(0.885)
     assert np.array_equal(words, odict["words"])
     assert cs == api.dictionary_checksum(words)
-    # FNV-1a 64 over the little-endian bytes (published definition), on a slice
-    part = words[:4096]
-    h = _fnv1a64(part)
-    assert isinstance(h, int)
     w2, _ = api.build_dictionary(0.886)
     assert np.array_equal(w2, words)
 
@@ -271,11 +281,11 @@ def test_fused_argument_errors_without_gpu():
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 3, z, 0, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 1 << 23, 6144, z, z, z, 1, z, 0, z, 0, z) == -5
     assert L.sbm_decode_ref(z, z, 3, 5, z, z, z, z) == -2
-    assert L.sbm_decode_dense(z, 10, z, 3, 5, z, z, z, z) == -2          # odd width
-    assert L.sbm_decode_dense(z, 0, z, 0, 4, z, z, z, z) == 0            # no rows: nothing to do
-    assert L.sbm_decode_dense(z, 0, z, 3, 4, z, z, z, z) == -1           # rows without codewords
-    assert L.sbm_decode_dense(z, 10, z, 1 << 20, 1 << 12, z, z, z, z) == -5   # positions beyond 32 bits
-    assert L.sbm_decode_dense(z, 10, z, 3, 4, z, z, z, z) == -1          # null pointers
+    assert L.sbm_decode_dense(z, 10, z, 3, 5, z, 0, z, z, z) == -2          # odd width
+    assert L.sbm_decode_dense(z, 0, z, 0, 4, z, 0, z, z, z) == 0            # no rows: nothing to do
+    assert L.sbm_decode_dense(z, 0, z, 3, 4, z, 0, z, z, z) == -1           # rows without codewords
+    assert L.sbm_decode_dense(z, 10, z, 1 << 20, 1 << 12, z, 0, z, z, z) == -5   # positions beyond 32 bits
+    assert L.sbm_decode_dense(z, 10, z, 3, 4, z, 0, z, z, z) == -1          # null pointers
     assert L.sbm_decode_ref(z, z, 0, 4, z, z, z, z) == 0
     assert L.sbm_workspace_bytes(10, 5) >= 4 * (16 + 10 + 11 + 11 + 5)
 
@@ -293,9 +303,12 @@ def test_encode_experts_layout(odict_for, E, rows, cols, p0, dict_p0):
     syms = [synth.ternary_symbols(rng, rows, cols, p0) for _ in range(E)]
     scs = [synth.row_scales(rng, rows) for _ in range(E)]
     codes, row_off, bstart, descs = api.encode_experts(syms, w)
-    ref = api.ExpertStack.assemble([api.encode_matrix(s, w) + (sc,) for s, sc in zip(syms, scs)], rows, cols)
+    tag = api.dict_tag(w)
+    ref = api.ExpertStack.assemble([api.encode_matrix(s, w) + (sc,) for s, sc in zip(syms, scs)], rows, cols, tag)
     assert np.array_equal(codes, ref[1]) and np.array_equal(row_off, ref[2]) and np.array_equal(bstart, ref[3])
     assert [bytes(a) for a in descs] == [bytes(b) for b in ref[0]]
+    # every descriptor names its dictionary: the low half of the FNV-1a 64 checksum of the packed table
+    assert all(d.dict_tag == (_fnv1a64(w) & 0xFFFFFFFF) for d in descs)
     assert all(d.code_base % N.SBM_CODE_ALIGN == 0 for d in descs)
     if rows:
         rc, ro = OC.encode_matrix(syms[0], od["child"])
