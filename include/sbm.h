@@ -250,6 +250,25 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
                                 void* y, uint32_t flags, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * fused call with no workspace argument.  The kernels use a static device
+ * array of 256 KiB (one copy per GPU the library runs on, held until the
+ * process ends) in place of the workspace; calls whose
+ * sbm_workspace_bytes(n_experts, n_tokens) exceeds it return SBM_ERANGE and
+ * launch nothing.  The call allocates nothing and leaves no state that a
+ * later call relies on.  Calls that overlap on one GPU (other streams, other
+ * host threads) share that array and race: serialise them.  error_word:
+ * device uint32 that receives the error word described at
+ * sbm_workspace_error (may be NULL).  Every other argument as for
+ * sbm_moe_fused_decode_matvec. */
+int sbm_moe_fused_decode_matvec_noalloc(const uint16_t* codes, const uint32_t* row_off,
+                                        const uint32_t* bstart, const uint16_t* scales,
+                                        const sbm_matrix_desc* experts, int32_t n_experts,
+                                        int32_t rows, int32_t cols, const void* dict_image,
+                                        const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens,
+                                        void* y, uint32_t flags, uint32_t* error_word, void* stream);
+
 /* ------------------------------------------- synthetic stack generation */
 /* The QMoE page's c2048 stack (1.6T parameters, under 160 GB at ~0.8 bit per
  * parameter, ~88.6% zeros; Executive Summary and "Natural sparsity") cannot be

@@ -132,6 +132,7 @@ struct FusedArgs {
   uint32_t lds_x;
   int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
   uint32_t dict_tag;    // low 32 bits of the image's dictionary checksum (read by the kernel)
+  uint32_t* err_out;    // if set, workgroup 0 copies the finished error word here
 };
 
 // ------------------------------------------------------------ wave helpers
@@ -1719,18 +1720,26 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     if (!image_ok) {
       // the same thread wrote the grouping's word: keep its id count and shape
       // bit; the dictionary comparison was made against a damaged header
-      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
+        if (a.err_out) *a.err_out = a.ws[0];
+      }
       return;               // (s_endpgm waits for the table copy still in flight, as on an empty slice)
     }
+    if (a.err_out && blockIdx.x == 0 && threadIdx.x == 0) *a.err_out = a.ws[0];   // this thread wrote it
     g0 = s_slice[0];
     g1 = s_slice[1];
     perm = s_perm;
     items = s_items;
   } else {
     if (!image_ok) {   // group_kernel's word is complete (stream order); its dictionary bit is void
-      if (blockIdx.x == 0 && threadIdx.x == 0) a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.ws[0] = (a.ws[0] & ~kErrDict) | kErrBadImage;
+        if (a.err_out) *a.err_out = a.ws[0];
+      }
       return;
     }
+    if (a.err_out && blockIdx.x == 0 && threadIdx.x == 0) *a.err_out = a.ws[0];
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
     g0 = bounds[blockIdx.x];
@@ -1751,9 +1760,17 @@ struct DevInfo {
   // the instances one call may launch (0-2: 3-slot image, 3-4: 4-slot image)
   int static_lds[2] = {};
   bool attr_set = false;
+  void* scratch = nullptr;   // device address of this device's copy of `scratch`
 };
 static std::mutex g_mu;
 static DevInfo g_dev[64];
+
+// Workspace of the allocation-free entry point: one copy per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in;
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device (DevInfo::scratch), never the array's name.
+constexpr size_t kScratchBytes = 256u << 10;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
 
 static const void* fused_instance(int mode) {
   switch (mode) {
@@ -1765,7 +1782,7 @@ static const void* fused_instance(int mode) {
   }
 }
 
-static int dev_info(DevInfo** out) {
+static int dev_info(DevInfo** out, bool want_scratch = false) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(SBM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -1796,6 +1813,12 @@ static int dev_info(DevInfo** out) {
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
     di.attr_set = true;
+  }
+  if (want_scratch && !di.scratch) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess || !ptr)
+      return fail(SBM_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    di.scratch = ptr;
   }
   *out = &di;
   return SBM_OK;
@@ -1851,13 +1874,15 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
   return (size_t)ws_layout(n_experts, n_tokens).total_words * 4u;
 }
 
-int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
-                                const uint32_t* bstart, const uint16_t* scales,
-                                const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
-                                int32_t cols, const void* dict_image, const uint16_t* x,
-                                const int32_t* expert_ids, int32_t n_tokens, void* y,
-                                uint32_t flags, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+}  // extern "C"
+
+// The fused call on a given workspace (the caller's, or this device's static
+// scratch); err_out, if set, receives a copy of the error word.
+static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint32_t* bstart,
+                      const uint16_t* scales, const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
+                      int32_t cols, const void* dict_image, const uint16_t* x, const int32_t* expert_ids,
+                      int32_t n_tokens, void* y, uint32_t flags, void* workspace, size_t workspace_bytes,
+                      uint32_t* err_out, bool use_scratch, void* stream) {
   if (n_tokens < 0 || n_tokens > (int32_t)kErrCountMask || n_experts <= 0 || n_experts > (1 << 24))
     return fail(SBM_EINVAL, "bad n_tokens=%d or n_experts=%d", n_tokens, n_experts);
   if (rows <= 0 || rows > (1 << 24) || cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", rows, cols);
@@ -1872,14 +1897,15 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
     return fail(SBM_EINVAL, "SBM_F_IMAGE4 and SBM_F_MFMA cannot be combined");
   if (n_tokens == 0) return SBM_OK;
   if (!codes || !row_off || !bstart || !scales || !experts || !dict_image || !x || !expert_ids || !y ||
-      !workspace)
+      (!workspace && !use_scratch))
     return fail(SBM_EINVAL, "null pointer");
   if (workspace_bytes < sbm_workspace_bytes(n_experts, n_tokens))
     return fail(SBM_ENOSPACE, "workspace %zu < %zu bytes", workspace_bytes,
                 sbm_workspace_bytes(n_experts, n_tokens));
   DevInfo* di = nullptr;
-  int st = dev_info(&di);
+  int st = dev_info(&di, use_scratch);
   if (st) return st;
+  if (use_scratch) workspace = di->scratch;
   const bool minmax = (flags & SBM_F_MINMAX) != 0;
   const int mode = (flags & SBM_F_MFMA) ? 1 : ((flags & SBM_F_IMAGE4) ? (minmax ? 4 : 3) : (minmax ? 2 : 0));
   Plan plan;
@@ -1931,6 +1957,7 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   // dense MFMA tiles for heavy experts reuse the same dynamic LDS
   a.mfma_rows = 0;
   a.dict_tag = 0;        // the kernel reads it from the image
+  a.err_out = err_out;
   for (int R : {64, 32, 16})
     if ((flags & SBM_F_MFMA) && mfma_lds(R, cols).total <= lds) {
       a.mfma_rows = R;
@@ -1953,6 +1980,33 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "fused launch: %s", hipGetErrorString(e));
   return SBM_OK;
+}
+
+extern "C" {
+
+int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
+                                const uint32_t* bstart, const uint16_t* scales,
+                                const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
+                                int32_t cols, const void* dict_image, const uint16_t* x,
+                                const int32_t* expert_ids, int32_t n_tokens, void* y,
+                                uint32_t flags, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return fused_call(codes, row_off, bstart, scales, experts, n_experts, rows, cols, dict_image, x, expert_ids,
+                    n_tokens, y, flags, workspace, workspace_bytes, nullptr, false, stream);
+}
+
+int sbm_moe_fused_decode_matvec_noalloc(const uint16_t* codes, const uint32_t* row_off,
+                                        const uint32_t* bstart, const uint16_t* scales,
+                                        const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
+                                        int32_t cols, const void* dict_image, const uint16_t* x,
+                                        const int32_t* expert_ids, int32_t n_tokens, void* y,
+                                        uint32_t flags, uint32_t* error_word, void* stream) {
+  if (n_tokens > 0 && n_experts > 0 && sbm_workspace_bytes(n_experts, n_tokens) > kScratchBytes)
+    return fail(SBM_ERANGE, "%d experts x %d tokens need %zu bytes of workspace; the allocation-free call "
+                "holds %zu (use sbm_moe_fused_decode_matvec with a workspace)", n_experts, n_tokens,
+                sbm_workspace_bytes(n_experts, n_tokens), kScratchBytes);
+  return fused_call(codes, row_off, bstart, scales, experts, n_experts, rows, cols, dict_image, x, expert_ids,
+                    n_tokens, y, flags, nullptr, kScratchBytes, error_word, true, stream);
 }
 
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream) {
