@@ -250,6 +250,49 @@ int sbm_moe_fused_decode_matvec(const uint16_t* codes, const uint32_t* row_off,
                                 void* y, uint32_t flags, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* One projection (all experts' matrices of one shape) of an MoE layer, as
+ * the layer call reads it: the arrays and descriptor table described at
+ * sbm_moe_fused_decode_matvec. */
+typedef struct {
+  const uint16_t* codes;
+  const uint32_t* row_off;
+  const uint32_t* bstart;
+  const uint16_t* scales;
+  const sbm_matrix_desc* experts;  /* device, [n_experts] */
+  int32_t n_experts;
+  int32_t rows;
+  int32_t cols;
+} sbm_projection;
+
+/* Workspace bytes of sbm_moe_fused_ffn. */
+size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens);
+
+/* [QMoE] "The GPU Decoding Kernel" for a whole expert FFN in one launch: for
+ * every token t with e = expert_ids[t],
+ *   h[t, :] = relu( W_up_e x[t, :] )          (fp16, up: rows = f, cols = d)
+ *   y[t, :] = W_down_e h[t, :]                (down: rows = d', cols = f)
+ * on the per-row ternary grid (codes 1, 2 -> -s_r, +s_r), both projections
+ * decoded on the fly as in sbm_moe_fused_decode_matvec.  The down rows of a
+ * token start once all of its up rows are written (per-token counts in the
+ * workspace; h is written and read coherently at device scope), so a layer
+ * takes one launch instead of two.  up, down: host structs of device arrays
+ * with the same experts; up->rows == down->cols; both cols even and >= 512
+ * (narrower rows: two sbm_moe_fused_decode_matvec calls).  x: device fp16
+ * [n_tokens x up->cols]; h: device fp16 [n_tokens x up->rows] (written);
+ * y: device [n_tokens x down->rows], fp16 or fp32 (SBM_F_OUT_F32); x, h and y
+ * must not overlap (workgroups still reading x run beside others writing y).  flags:
+ * SBM_F_IN_RMS, SBM_F_OUT_F32 only (symmetric grid, 3-slot image).
+ * workspace: device, 16-byte aligned, sbm_ffn_workspace_bytes(n_experts,
+ * n_tokens) bytes, ZEROED by the caller before its first use with a call;
+ * every call leaves it ready for the next (calls sharing a workspace must not
+ * overlap).  Its first word is the call's error word (sbm_workspace_error),
+ * as for sbm_moe_fused_decode_matvec, plus bit 28: the down phase gave up
+ * waiting for up rows (about 20 ms, e.g. when not every workgroup could be
+ * resident, or the workspace was not zeroed): those tokens' y is invalid. */
+int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, const void* dict_image,
+                      const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens, uint16_t* h, void* y,
+                      uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * fused call with no workspace argument.  The kernels use a static device
@@ -313,7 +356,8 @@ int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
 int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint16_t* x_out, void* stream);
 
 /* Workspace error word of the last fused call (device read; synchronises the
- * stream).  Bits 0-28: number of tokens whose expert id was out of range;
+ * stream).  Bits 0-27: number of tokens whose expert id was out of range;
+ * bit 28: (layer calls) the down phase gave up waiting for up rows;
  * bit 29: a touched expert's dict_tag differs from the image's dictionary
  * checksum (its tokens get no output); bit 30: a touched expert's descriptor
  * disagrees with the call's shape or alignment (its tokens get no output);

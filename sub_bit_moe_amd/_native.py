@@ -34,6 +34,11 @@ class MatrixDesc(C.Structure):
                 ("cols", C.c_int32), ("dict_tag", C.c_uint32)]
 
 
+class Projection(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("row_off", C.c_void_p), ("bstart", C.c_void_p), ("scales", C.c_void_p),
+                ("experts", C.c_void_p), ("n_experts", C.c_int32), ("rows", C.c_int32), ("cols", C.c_int32)]
+
+
 P = C.c_void_p
 _SIGS = {
     "sbm_last_error": (C.c_char_p, []),
@@ -57,6 +62,8 @@ _SIGS = {
                                               P, P, C.c_int32, P, C.c_uint32, P, C.c_size_t, P]),
     "sbm_moe_fused_decode_matvec_noalloc": (C.c_int, [P, P, P, P, P, C.c_int32, C.c_int32, C.c_int32, P,
                                                       P, P, C.c_int32, P, C.c_uint32, P, P]),
+    "sbm_ffn_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
+    "sbm_moe_fused_ffn": (C.c_int, [P, P, P, P, P, C.c_int32, P, P, C.c_uint32, P, C.c_size_t, P]),
     "sbm_workspace_error": (C.c_int, [P, P, P]),
     "sbm_rms_glue": (C.c_int, [P, C.c_int32, C.c_int32, P, P]),
     "sbm_trie_words": (C.c_size_t, []),

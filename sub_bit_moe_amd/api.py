@@ -289,6 +289,43 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
     return y
 
 
+def ffn_workspace_bytes(n_experts: int, n_tokens: int) -> int:
+    return int(lib().sbm_ffn_workspace_bytes(n_experts, n_tokens))
+
+
+def alloc_ffn_workspace(n_experts: int, n_tokens: int, device="cuda"):
+    """Zeroed workspace of the layer call (it must start zeroed; every call
+    leaves it ready for the next)."""
+    import torch
+    return torch.zeros(max(ffn_workspace_bytes(n_experts, n_tokens), 64), dtype=torch.uint8, device=device)
+
+
+def _projection(st: ExpertStack):
+    return N.Projection(codes=_ptr(st.codes), row_off=_ptr(st.row_off), bstart=_ptr(st.bstart),
+                        scales=_ptr(st.scales), experts=_ptr(st.desc), n_experts=st.n_experts, rows=st.rows,
+                        cols=st.cols)
+
+
+def moe_fused_ffn(up: ExpertStack, down: ExpertStack, image_t, x, expert_ids, h=None, y=None, workspace=None,
+                  in_rms: bool = False, out_f32: bool = False, stream=None):
+    """One MoE expert FFN in one launch (sbm_moe_fused_ffn): h = relu(W_up x),
+    y = W_down h for every token's expert.  Returns (y, h)."""
+    import torch
+    T = int(x.shape[0])
+    dev = up.codes.device
+    if h is None:
+        h = torch.empty((T, up.rows), dtype=torch.float16, device=dev)
+    if y is None:
+        y = torch.empty((T, down.rows), dtype=torch.float32 if out_f32 else torch.float16, device=dev)
+    if workspace is None:
+        workspace = alloc_ffn_workspace(up.n_experts, T, dev)
+    flags = (N.SBM_F_IN_RMS if in_rms else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0)
+    pu, pd = _projection(up), _projection(down)
+    check(lib().sbm_moe_fused_ffn(C.addressof(pu), C.addressof(pd), _ptr(image_t), _ptr(x), _ptr(expert_ids), T,
+                                  _ptr(h), _ptr(y), flags, _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return y, h
+
+
 def workspace_error(workspace, stream=None) -> int:
     v = C.c_uint32()
     check(lib().sbm_workspace_error(_ptr(workspace), C.addressof(v), _stream(stream)))

@@ -87,8 +87,9 @@ constexpr uint32_t kMfmaWeight = 24;    // slice weight of one row of an MFMA it
 constexpr int kMaxRmax = 4096;    // rows per chunk
 constexpr int kEpiRegs = (kMaxRmax + 2 + kFThreads - 1) / kFThreads;   // epilogue slots per thread
 constexpr int kGroupInLds = 128;  // up to this many tokens are grouped inside the fused kernel
-constexpr uint32_t kErrDict = 0x20000000u, kErrBadDesc = 0x40000000u, kErrBadImage = 0x80000000u;
-constexpr uint32_t kErrCountMask = 0x1FFFFFFFu;   // bits 0-28: tokens with an expert id out of range
+constexpr uint32_t kErrLayerWait = 0x10000000u, kErrDict = 0x20000000u, kErrBadDesc = 0x40000000u,
+                   kErrBadImage = 0x80000000u;
+constexpr uint32_t kErrCountMask = 0x0FFFFFFFu;   // bits 0-27: tokens with an expert id out of range
 struct WsLayout {
   uint64_t cnt, start, chunk, perm, items, bounds, total_words;
 };
@@ -131,9 +132,23 @@ struct FusedArgs {
   uint32_t lds_racc;    // byte offsets in LDS
   uint32_t lds_x;
   int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
-  uint32_t dict_tag;    // low 32 bits of the image's dictionary checksum (read by the kernel)
   uint32_t* err_out;    // if set, workgroup 0 copies the finished error word here
+  // layer calls (up, ReLU, down in one launch): per-token counts of up rows
+  // written, the count a token needs before its down rows start, and the
+  // bytes of x (the down phase reads h through a range-checked resource)
+  uint32_t* tok_done;
+  uint32_t tok_expect;
+  uint32_t x_bytes;
+  uint32_t* sync_err;   // the layer call's error accumulator (device-scope atomics only)
 };
+
+// Layer mode of the staging and epilogue code: 0 a single projection; 1 the
+// up phase of a layer call (h stored coherently at device scope, per-token
+// row counts raised after each chunk); 2 its down phase (a token's rows of h
+// are waited for, then read coherently at device scope).
+constexpr int kCpolSc1 = 16;                     // buffer-load cache policy: device-scope coherent
+
+constexpr uint64_t kLayerWaitTicks = 2000000;    // 20 ms of the 100 MHz real-time counter
 
 // ------------------------------------------------------------ wave helpers
 // Inclusive scan over the 64 lanes of a wave (DPP row shifts, then the row
@@ -263,6 +278,9 @@ __device__ uint64_t weighted_boundary(const uint4* items, uint32_t n_items, uint
   const uint32_t w1 = lo + 1 < n_items ? items[lo + 1].w : wtot;
   return boundary_in_item(u, (uint64_t)w0 * R + (uint64_t)lo * F, lo, w1 > w0 ? w1 - w0 : 1u, F, R);
 }
+
+// The dictionary tag of the decode image: the low 32 bits of its checksum.
+__device__ __forceinline__ uint32_t image_tag(const FusedArgs& a) { return (uint32_t)a.image->checksum; }
 
 // Why a matrix descriptor cannot be used for a call of this shape with this
 // decode image: kErrBadDesc (shape, alignment), kErrDict (its codes were
@@ -499,7 +517,7 @@ __device__ __forceinline__ Chunk chunk_at(const FusedArgs& a, const uint4* items
   ch.nt = it.z & ~kItemMfma;
   ch.mfma = (it.z & kItemMfma) != 0;
   const sbm_matrix_desc d = a.experts[it.x];
-  ch.ok = desc_err(d, a.rows, a.cols, a.minmax, a.dict_tag) == 0;
+  ch.ok = desc_err(d, a.rows, a.cols, a.minmax, image_tag(a)) == 0;
   ch.code_base = d.code_base;
   ch.n_codes = d.n_codes;
   ch.blk_base = d.blk_base;
@@ -748,24 +766,69 @@ __device__ __forceinline__ int32_t x_src(const FusedArgs& a, int32_t c, bool wra
   return (wrap && c >= a.cols) ? c - a.cols : c;
 }
 
+// Activation loads: plain, or (LM 2: h written by other workgroups of the
+// same launch) device-scope coherent through a range-checked resource.
+template <int LM>
+__device__ __forceinline__ uint4 ld_x16(const FusedArgs& a, int64_t idx) {
+  if constexpr (LM == 2) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufferFlags);
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)idx * 2u, 0, kCpolSc1);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+  } else {
+    return *(const uint4*)(a.x + idx);
+  }
+}
+template <int LM>
+__device__ __forceinline__ uint32_t ld_x2(const FusedArgs& a, int64_t idx) {
+  if constexpr (LM == 2) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufferFlags);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)idx * 2u, 0, kCpolSc1);
+  } else {
+    return a.x[idx];
+  }
+}
+
+// LM 2: wait until the up phase has written all rows of h for tokens
+// perm[tb .. tb+nt) (each wave polls the nt counters; bounded by the real-time
+// counter: on expiry the layer error bit is raised and the wave goes on, so
+// the kernel always ends).  Lanes past nt and other modes return at once.
+template <int LM>
+__device__ __forceinline__ void wait_tokens(const FusedArgs& a, const int32_t* perm, uint32_t tb, uint32_t nt) {
+  if constexpr (LM == 2) {
+    const uint32_t lane = threadIdx.x & 63;
+    const bool mine = lane < nt;
+    const uint32_t* p = a.tok_done + (mine ? (uint32_t)perm[tb + lane] : 0u);
+    const uint64_t t0 = wall_clock64();
+    while (true) {
+      const uint32_t v = mine ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.tok_expect;
+      if (__all(v >= a.tok_expect)) break;
+      if (wall_clock64() - t0 > kLayerWaitTicks) {
+        if (lane == 0) __hip_atomic_fetch_or(a.sync_err, kErrLayerWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
 // fp16 pairs of staged columns c0 .. c0+7 of TC token rows (zero past the
 // staged content or for tok < 0).
-template <int TC>
+template <int TC, int LM = 0>
 __device__ __forceinline__ void load_x_group(const FusedArgs& a, const int32_t (&tok)[TC], int32_t c0, bool vec,
                                              bool wrap, uint32_t (&p)[TC][4]) {
   const int32_t s0 = x_src(a, c0, wrap);
 #pragma unroll
   for (int t = 0; t < TC; ++t) {
     if (tok[t] >= 0 && s0 + 8 <= a.cols && vec) {
-      const uint4 v = *(const uint4*)(a.x + (int64_t)tok[t] * a.cols + s0);
+      const uint4 v = ld_x16<LM>(a, (int64_t)tok[t] * a.cols + s0);
       p[t][0] = v.x; p[t][1] = v.y; p[t][2] = v.z; p[t][3] = v.w;
     } else {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int32_t sl = x_src(a, c0 + 2 * m, wrap), sh = x_src(a, c0 + 2 * m + 1, wrap);
         uint32_t lo = 0, hi = 0;
-        if (tok[t] >= 0 && sl < a.cols) lo = a.x[(int64_t)tok[t] * a.cols + sl];
-        if (tok[t] >= 0 && sh < a.cols) hi = a.x[(int64_t)tok[t] * a.cols + sh];
+        if (tok[t] >= 0 && sl < a.cols) lo = ld_x2<LM>(a, (int64_t)tok[t] * a.cols + sl);
+        if (tok[t] >= 0 && sh < a.cols) hi = ld_x2<LM>(a, (int64_t)tok[t] * a.cols + sh);
         p[t][m] = lo | (hi << 16);
       }
     }
@@ -819,7 +882,7 @@ __device__ __forceinline__ bool x_prefetchable(const FusedArgs& a, int tc) {
   return x_vec(a) && a.xcols / 8 <= kFThreads * (4 / tc);
 }
 
-template <int TC>
+template <int TC, int LM = 0>
 __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* perm, uint32_t tb, uint32_t nt,
                                           XPre& r) {
   const int32_t n8 = a.xcols / 8;
@@ -832,7 +895,7 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
       const uint32_t u = x_row_token(a, t);
       const int32_t tok = u < nt ? perm[tb + u] : -1;
       r.v[j * TC + t] = (tok >= 0 && s0 + 8 <= a.cols && c0 < 8 * n8)
-                            ? *(const uint4*)(a.x + (int64_t)tok * a.cols + s0) : make_uint4(0, 0, 0, 0);
+                            ? ld_x16<LM>(a, (int64_t)tok * a.cols + s0) : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -877,13 +940,14 @@ __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* sm
   }
 }
 
-template <int TC>
+template <int TC, int LM = 0>
 __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem, const int32_t* perm, uint32_t tb,
                         uint32_t nt) {
+  wait_tokens<LM>(a, perm, tb, nt);
   if (x_prefetchable(a, TC)) {
     // one round trip: the rows stay in registers for the RMS scale
     XPre r;
-    xpre_load<TC>(a, perm, tb, nt, r);
+    xpre_load<TC, LM>(a, perm, tb, nt, r);
     xpre_store<TC>(a, smem, r);
     return;
   }
@@ -900,7 +964,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
     for (int t = 0; t < TC; ++t) ss[t] = 0.f;
     for (int32_t i = threadIdx.x; 8 * i < a.cols; i += kFThreads) {     // the row itself, not its wrap copy
       uint32_t p[TC][4];
-      load_x_group<TC>(a, tok, 8 * i, vec, false, p);
+      load_x_group<TC, LM>(a, tok, 8 * i, vec, false, p);
 #pragma unroll
       for (int t = 0; t < TC; ++t)
 #pragma unroll
@@ -910,7 +974,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
   }
   for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
     uint32_t p[TC][4];
-    load_x_group<TC>(a, tok, 8 * i, vec, x_wrap(a), p);
+    load_x_group<TC, LM>(a, tok, 8 * i, vec, x_wrap(a), p);
     if (rms) {
 #pragma unroll
       for (int t = 0; t < TC; ++t)
@@ -1305,7 +1369,7 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 
 // MFMA: the kernel instance that runs dense-tile items (SBM_F_MFMA); the
 // default instance has no call in its loop, which keeps its registers unspilled.
-template <bool SMALL, bool MFMA, int NS>
+template <bool SMALL, bool MFMA, int NS, int LM = 0>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1, uint32_t split7) {
   float* racc = (float*)(smem + a.lds_racc);
@@ -1343,9 +1407,9 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       }
       const int tc = tc_rows(a, ch.nt);
       if (ch.q != cur_q) {
-        if (tc == 1) stage_x<1>(a, smem, perm, ch.tb, ch.nt);
-        else if (tc == 2) stage_x<2>(a, smem, perm, ch.tb, ch.nt);
-        else stage_x<4>(a, smem, perm, ch.tb, ch.nt);
+        if (tc == 1) stage_x<1, LM>(a, smem, perm, ch.tb, ch.nt);
+        else if (tc == 2) stage_x<2, LM>(a, smem, perm, ch.tb, ch.nt);
+        else stage_x<4, LM>(a, smem, perm, ch.tb, ch.nt);
         cur_q = ch.q;
         wait_vmem_all();      // this wave's part of the image has landed
         __syncthreads();
@@ -1390,9 +1454,10 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         const int ntc = tc_rows(a, nx.nt);
         if (next_new && x_prefetchable(a, ntc)) {
           next_pre = true;
-          if (ntc == 1) xpre_load<1>(a, perm, nx.tb, nx.nt, xp);
-          else if (ntc == 2) xpre_load<2>(a, perm, nx.tb, nx.nt, xp);
-          else xpre_load<4>(a, perm, nx.tb, nx.nt, xp);
+          wait_tokens<LM>(a, perm, nx.tb, nx.nt);
+          if (ntc == 1) xpre_load<1, LM>(a, perm, nx.tb, nx.nt, xp);
+          else if (ntc == 2) xpre_load<2, LM>(a, perm, nx.tb, nx.nt, xp);
+          else xpre_load<4, LM>(a, perm, nx.tb, nx.nt, xp);
         }
       }
       __syncthreads();
@@ -1429,8 +1494,14 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
               v *= s;
               if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
               const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + i - 1;
-              if (a.flags & SBM_F_OUT_F32) ((float*)a.y)[o] = v;
-              else ((_Float16*)a.y)[o] = (_Float16)v;
+              if constexpr (LM == 1) {   // h for the down phase: written through to device scope
+                __hip_atomic_store((uint16_t*)a.y + o, __builtin_bit_cast(uint16_t, (_Float16)v), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+              } else if (a.flags & SBM_F_OUT_F32) {
+                ((float*)a.y)[o] = v;
+              } else {
+                ((_Float16*)a.y)[o] = (_Float16)v;
+              }
             }
           }
         }
@@ -1442,13 +1513,21 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
           else if (ntc == 2) xpre_store<2>(a, smem, xp);
           else xpre_store<4>(a, smem, xp);
         } else {
-          if (ntc == 1) stage_x<1>(a, smem, perm, nx.tb, nx.nt);
-          else if (ntc == 2) stage_x<2>(a, smem, perm, nx.tb, nx.nt);
-          else stage_x<4>(a, smem, perm, nx.tb, nx.nt);
+          if (ntc == 1) stage_x<1, LM>(a, smem, perm, nx.tb, nx.nt);
+          else if (ntc == 2) stage_x<2, LM>(a, smem, perm, nx.tb, nx.nt);
+          else stage_x<4, LM>(a, smem, perm, nx.tb, nx.nt);
         }
         cur_q = nx.q;
       }
+      if constexpr (LM == 1) wait_vmem_all();   // this thread's rows of h have reached device scope
       __syncthreads();
+      if constexpr (LM == 1) {
+        // every row of the chunk is written: raise its tokens' counts (also
+        // for a refused expert, whose rows stay unwritten, so no wait hangs)
+        if (threadIdx.x < ch.nt)
+          __hip_atomic_fetch_add(a.tok_done + perm[ch.tb + threadIdx.x], (uint32_t)(ch.rb - ch.ra), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     const uint64_t gn = s_gnext;
     __syncthreads();      // every wave has read the table before it is rebuilt
@@ -1580,7 +1659,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, a.dict_tag))
+      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, image_tag(a)))
         atomicOr(&s_ghdr[3], err);
     __syncthreads();
     if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
@@ -1679,7 +1758,7 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
     for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
-      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, a.dict_tag))
+      if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, image_tag(a)))
         atomicOr(&s_ghdr[3], err);
     __syncthreads();
     if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
@@ -1704,7 +1783,6 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   const int32_t tq = (int32_t)threadIdx.x < a.n_tokens ? (int32_t)threadIdx.x : a.n_tokens - 1;
   const int32_t my_id = a.ids[tq];
   const uint4 hdr = *(const uint4*)a.image;       // magic, version, split, n_tab
-  a.dict_tag = (uint32_t)a.image->checksum;       // same scalar cache line as the header
   stage_tables_dma<NS>(a.image);
   // the table indexes stay below n_tab <= the table's capacity for every codeword
   const bool image_ok = hdr.x == kImageMagic && hdr.y == (NS == 3 ? kImageVersion : kImage4Version) &&
@@ -1752,6 +1830,88 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
   else run_slice<false, MFMA, NS>(a, smem, perm, items, g0, g1, split7);
 }
 
+// ------------------------------------------------------------ layer calls
+// Up projection, ReLU and down projection of the same routed tokens in one
+// launch ([QMoE] "The GPU Decoding Kernel": the experts are FFNs whose two
+// matrices are multiplied in turn; doing both here saves the second launch,
+// its prologue and the first phase's tail).  Every workgroup runs its up
+// slice, then its down slice; the down phase stages a token's h only once all
+// up rows of that token are written (per-token counts raised by the up
+// chunks, h written and read coherently at device scope, so no cache-wide
+// writeback or invalidation is needed).  All workgroups are resident (one
+// per CU, at most the CU count), and every wait is bounded.
+// Sync area at the start of the layer workspace (uint32 words): [0] the
+// finished call's error word, [1] the running error word, [2] workgroups
+// done, [16 ..) one count per token.  The last workgroup to finish publishes
+// the error word and clears the rest, so a call leaves the area ready for
+// the next one (the caller zeroes it once, before the first call).
+constexpr uint32_t kSyncHdr = 16;
+__shared__ uint32_t s_last;
+
+// One phase of a layer call: LM 1 the up projection, LM 2 the down projection.
+template <int LM>
+__device__ __forceinline__ void ffn_phase(const FusedArgs& a, unsigned char* smem, int32_t my_id, bool image_ok,
+                                          uint32_t split7, uint32_t* sync) {
+  const int32_t* perm;
+  const uint4* items;
+  uint64_t g0, g1;
+  if (a.group_in_lds) {
+    if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
+    else group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
+    g0 = s_slice[0];
+    g1 = s_slice[1];
+    perm = s_perm;
+    items = s_items;
+  } else {
+    const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
+    const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
+    g0 = bounds[blockIdx.x];
+    g1 = bounds[blockIdx.x + 1];
+    perm = (const int32_t*)(a.ws + L.perm);
+    items = (const uint4*)(a.ws + L.items);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // this thread wrote (or the grouping kernel before this launch wrote) the
+    // phase's word: the id count once, the flag bits of both phases
+    uint32_t w = a.ws[0];
+    if (LM == 2) w &= ~kErrCountMask;
+    if (!image_ok) w = (w & ~kErrDict) | kErrBadImage;
+    if (w) __hip_atomic_fetch_or(sync + 1, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (image_ok && g0 < g1) run_slice<false, false, 3, LM>(a, smem, perm, items, g0, g1, split7);
+  __syncthreads();      // the grouping's LDS is rebuilt by the next phase
+}
+
+template <int DUMMY>
+__global__ __launch_bounds__(kFThreads) void ffn_kernel(const FusedArgs up, const FusedArgs dn, uint32_t* sync) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int32_t tq = (int32_t)threadIdx.x < up.n_tokens ? (int32_t)threadIdx.x : up.n_tokens - 1;
+  const int32_t my_id = up.ids[tq];
+  const uint4 hdr = *(const uint4*)up.image;
+  stage_tables_dma<3>(up.image);
+  const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
+                        hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
+  const uint32_t split7 = 7u * hdr.z;
+  ffn_phase<1>(up, smem, my_id, image_ok, split7, sync);
+  ffn_phase<2>(dn, smem, my_id, image_ok, split7, sync);
+  wait_vmem_all();        // every store and count of this workgroup is complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (s_last) {
+    // the other workgroups are done: publish the error word, clear the counts
+    for (int32_t t = threadIdx.x; t < up.n_tokens; t += kFThreads)
+      __hip_atomic_store(sync + kSyncHdr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      const uint32_t err = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ------------------------------------------------------------ host entries
 struct DevInfo {
   int cus = 0;
@@ -1759,6 +1919,7 @@ struct DevInfo {
   // static LDS of the fused-kernel instances, per image kind: the largest over
   // the instances one call may launch (0-2: 3-slot image, 3-4: 4-slot image)
   int static_lds[2] = {};
+  int ffn_static_lds = 0;
   bool attr_set = false;
   void* scratch = nullptr;   // device address of this device's copy of `scratch`
 };
@@ -1810,6 +1971,15 @@ static int dev_info(DevInfo** out, bool want_scratch = false) {
     for (int m = 0; m < kModes; ++m) {
       e = hipFuncSetAttribute(fused_instance(m), hipFuncAttributeMaxDynamicSharedMemorySize,
                               di.max_lds - di.static_lds[m >= 3 ? 1 : 0]);
+      if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    }
+    {
+      hipFuncAttributes fa;
+      if ((e = hipFuncGetAttributes(&fa, (const void*)ffn_kernel<0>)) != hipSuccess)
+        return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
+      di.ffn_static_lds = (int)fa.sharedSizeBytes;
+      e = hipFuncSetAttribute((const void*)ffn_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              di.max_lds - di.ffn_static_lds);
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
     di.attr_set = true;
@@ -1876,6 +2046,57 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
 
 }  // extern "C"
 
+// Kernel arguments of one projection call (the kernels read the dictionary
+// tag from the image; MFMA tiles and layer fields are set by the callers).
+static void fill_args(FusedArgs& a, const uint16_t* codes, const uint32_t* row_off, const uint32_t* bstart,
+                      const uint16_t* scales, const sbm_matrix_desc* experts, int32_t n_experts, int32_t rows,
+                      int32_t cols, const void* dict_image, const uint16_t* x, const int32_t* expert_ids,
+                      int32_t n_tokens, void* y, uint32_t flags, void* workspace, const Plan& plan, int32_t grid) {
+  const bool minmax = (flags & SBM_F_MINMAX) != 0;
+  a = FusedArgs{};
+  a.codes = codes;
+  a.row_off = row_off;
+  a.bstart = bstart;
+  a.scales = scales;
+  a.experts = experts;
+  a.image = (const DictImage*)dict_image;
+  a.x = x;
+  a.ids = expert_ids;
+  a.y = y;
+  a.ws = (uint32_t*)workspace;
+  a.rows = rows;
+  a.cols = cols;
+  a.n_experts = n_experts;
+  a.n_tokens = n_tokens;
+  a.flags = flags;
+  a.colsB = 6u * (uint32_t)cols;
+  div_magic(a.colsB, &a.magic_m, &a.magic_s);
+  a.rmax = plan.rmax;
+  a.tcmax = plan.tcmax;
+  a.minmax = minmax ? 1 : 0;
+  a.titem = minmax ? plan.tcmax / 2 : plan.tcmax;
+  a.xcols = plan.xcols;
+  a.lds_racc = plan.lds_racc;
+  a.lds_x = plan.lds_x;
+  a.grid = grid;
+  // an item change costs about as much as kItemChangeBlocks blocks of one-token
+  // rows (activation restaging, drain, epilogue); a one-token row of cols
+  // columns is about cols / 22 codewords and weighs 4
+  a.item_cost = (uint32_t)std::min<int64_t>((int64_t)kRowWeight1 * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
+  a.mfma_rows = 0;
+  a.err_out = nullptr;
+  a.group_in_lds = n_tokens <= kGroupInLds && n_experts < (1 << 24);
+}
+
+// The grouping kernel for calls of more than kGroupInLds tokens.
+static int launch_group(const FusedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, a.ids, a.n_tokens, a.n_experts, a.titem, a.rows,
+                     a.cols, a.grid, a.item_cost, (int32_t)(a.mfma_rows > 0), a.minmax, a.experts, a.image, a.ws);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
+  return SBM_OK;
+}
+
 // The fused call on a given workspace (the caller's, or this device's static
 // scratch); err_out, if set, receives a copy of the error word.
 static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint32_t* bstart,
@@ -1916,62 +2137,26 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   if (minmax && ((uintptr_t)scales & 3u))
     return fail(SBM_EINVAL, "SBM_F_MINMAX: scales must be 4-byte aligned");
   FusedArgs a;
-  a.codes = codes;
-  a.row_off = row_off;
-  a.bstart = bstart;
-  a.scales = scales;
-  a.experts = experts;
-  a.image = (const DictImage*)dict_image;
-  a.x = x;
-  a.ids = expert_ids;
-  a.y = y;
-  a.ws = (uint32_t*)workspace;
-  a.rows = rows;
-  a.cols = cols;
-  a.n_experts = n_experts;
-  a.n_tokens = n_tokens;
-  a.flags = flags;
-  a.colsB = 6u * (uint32_t)cols;
-  div_magic(a.colsB, &a.magic_m, &a.magic_s);
-  a.rmax = plan.rmax;
-  a.tcmax = plan.tcmax;
-  a.minmax = minmax ? 1 : 0;
-  a.titem = minmax ? plan.tcmax / 2 : plan.tcmax;
-  a.xcols = plan.xcols;
-  a.lds_racc = plan.lds_racc;
-  a.lds_x = plan.lds_x;
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / a.titem + 1;
+  const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / (minmax ? plan.tcmax / 2 : plan.tcmax) + 1;
   const int64_t n_upper = max_items * rows;
   int64_t grid = (n_upper + 63) / 64;
   if (grid > di->cus) grid = di->cus;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
-  a.grid = (int32_t)grid;
-  // an item change costs about as much as kItemChangeBlocks blocks of one-token
-  // rows (activation restaging, drain, epilogue); a one-token row of cols
-  // columns is about cols / 22 codewords and weighs 4
-  a.item_cost = (uint32_t)std::min<int64_t>((int64_t)kRowWeight1 * kItemChangeBlocks * 22 * SBM_BLOCK / cols, 1 << 20);
+  fill_args(a, codes, row_off, bstart, scales, experts, n_experts, rows, cols, dict_image, x, expert_ids, n_tokens,
+            y, flags, workspace, plan, (int32_t)grid);
+  a.err_out = err_out;
+  hipStream_t s = (hipStream_t)stream;
   // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
   const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
   // dense MFMA tiles for heavy experts reuse the same dynamic LDS
-  a.mfma_rows = 0;
-  a.dict_tag = 0;        // the kernel reads it from the image
-  a.err_out = err_out;
   for (int R : {64, 32, 16})
     if ((flags & SBM_F_MFMA) && mfma_lds(R, cols).total <= lds) {
       a.mfma_rows = R;
       break;
     }
-  a.group_in_lds = n_tokens <= kGroupInLds && n_experts < (1 << 24);
   hipError_t e;
-  if (!a.group_in_lds) {
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kThreads), 0, s, expert_ids, n_tokens, n_experts,
-                       a.titem, rows, cols, (int32_t)grid, a.item_cost, (int32_t)(a.mfma_rows > 0), a.minmax, experts,
-                       (const DictImage*)dict_image, (uint32_t*)workspace);
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail(SBM_EHIP, "group launch: %s", hipGetErrorString(e));
-  }
+  if (!a.group_in_lds && (st = launch_group(a, s))) return st;
   if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<1>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (mode == 3) hipLaunchKernelGGL(fused_kernel<3>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (mode == 4) hipLaunchKernelGGL(fused_kernel<4>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
@@ -2007,6 +2192,72 @@ int sbm_moe_fused_decode_matvec_noalloc(const uint16_t* codes, const uint32_t* r
                 sbm_workspace_bytes(n_experts, n_tokens), kScratchBytes);
   return fused_call(codes, row_off, bstart, scales, experts, n_experts, rows, cols, dict_image, x, expert_ids,
                     n_tokens, y, flags, nullptr, kScratchBytes, error_word, true, stream);
+}
+
+static size_t align16(size_t b) { return (b + 15u) & ~(size_t)15u; }
+
+size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
+  if (n_experts < 0 || n_tokens < 0) return 0;
+  return align16(((size_t)kSyncHdr + (size_t)n_tokens) * 4u) + 2u * align16(sbm_workspace_bytes(n_experts, n_tokens));
+}
+
+int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, const void* dict_image,
+                      const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens, uint16_t* h, void* y,
+                      uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!up || !down) return fail(SBM_EINVAL, "null projection");
+  if (n_tokens < 0 || n_tokens > (int32_t)kErrCountMask) return fail(SBM_EINVAL, "bad n_tokens=%d", n_tokens);
+  if (up->n_experts <= 0 || up->n_experts > (1 << 24) || up->n_experts != down->n_experts)
+    return fail(SBM_EINVAL, "the projections must hold the same experts (%d, %d)", up->n_experts, down->n_experts);
+  for (const sbm_projection* p : {up, down}) {
+    if (p->rows <= 0 || p->rows > (1 << 24) || p->cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", p->rows, p->cols);
+    if (p->cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", p->cols);
+    if (p->cols < kSmallCols)
+      return fail(SBM_EINVAL, "cols=%d: the layer call needs rows of at least %d columns (use two "
+                  "sbm_moe_fused_decode_matvec calls)", p->cols, kSmallCols);
+    if ((uint64_t)p->rows * (uint64_t)p->cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
+      return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
+  }
+  if (up->rows != down->cols)
+    return fail(SBM_EINVAL, "up rows (%d) must equal down cols (%d): h is their common width", up->rows, down->cols);
+  if (flags & ~(SBM_F_OUT_F32 | SBM_F_IN_RMS)) return fail(SBM_EINVAL, "unknown or unsupported flags 0x%x", flags);
+  if ((uint64_t)n_tokens * (uint64_t)down->cols * 2u >= (1ull << 31)) return fail(SBM_ERANGE, "h too large");
+  if (n_tokens == 0) return SBM_OK;
+  for (const sbm_projection* p : {up, down})
+    if (!p->codes || !p->row_off || !p->bstart || !p->scales || !p->experts) return fail(SBM_EINVAL, "null pointer");
+  if (!dict_image || !x || !expert_ids || !h || !y || !workspace) return fail(SBM_EINVAL, "null pointer");
+  if ((uintptr_t)workspace & 15u) return fail(SBM_EINVAL, "workspace must be 16-byte aligned");
+  const size_t need = sbm_ffn_workspace_bytes(up->n_experts, n_tokens);
+  if (workspace_bytes < need) return fail(SBM_ENOSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  DevInfo* di = nullptr;
+  int st = dev_info(&di);
+  if (st) return st;
+  Plan pu, pd;
+  if (!make_plan(up->cols, di->max_lds, di->ffn_static_lds, &pu) ||
+      !make_plan(down->cols, di->max_lds, di->ffn_static_lds, &pd))
+    return fail(SBM_ERANGE, "a token row does not fit in %d bytes of LDS", di->max_lds);
+  const int32_t grid = std::min(di->cus, kMaxGrid);
+  uint32_t* sync = (uint32_t*)workspace;
+  unsigned char* wsu = (unsigned char*)workspace + align16(((size_t)kSyncHdr + (size_t)n_tokens) * 4u);
+  unsigned char* wsd = wsu + align16(sbm_workspace_bytes(up->n_experts, n_tokens));
+  FusedArgs ua, da;
+  fill_args(ua, up->codes, up->row_off, up->bstart, up->scales, up->experts, up->n_experts, up->rows, up->cols,
+            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & SBM_F_IN_RMS), wsu, pu, grid);
+  fill_args(da, down->codes, down->row_off, down->bstart, down->scales, down->experts, down->n_experts, down->rows,
+            down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, wsd, pd, grid);
+  ua.tok_done = da.tok_done = sync + kSyncHdr;
+  ua.sync_err = da.sync_err = sync + 1;
+  da.tok_expect = (uint32_t)up->rows;
+  da.x_bytes = (uint32_t)((uint64_t)n_tokens * (uint64_t)down->cols * 2u);
+  hipStream_t s = (hipStream_t)stream;
+  if (!ua.group_in_lds) {
+    if ((st = launch_group(ua, s))) return st;
+    if ((st = launch_group(da, s))) return st;
+  }
+  const uint32_t lds = std::max<uint32_t>(std::max(pu.lds_total, pd.lds_total), kGroupScratch);
+  hipLaunchKernelGGL(ffn_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, ua, da, sync);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SBM_EHIP, "layer launch: %s", hipGetErrorString(e));
+  return SBM_OK;
 }
 
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream) {

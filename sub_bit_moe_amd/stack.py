@@ -135,12 +135,16 @@ class Runner:
     """Preallocated buffers for repeated passes (minmax: the stack's scales
     are (w_min, w_max) pairs)."""
 
-    def __init__(self, st: Stack, minmax: bool = False):
+    def __init__(self, st: Stack, minmax: bool = False, layer: bool = False):
         import torch
         c = st.cfg
         dev = st.x0.device
         self.st = st
         self.minmax = minmax
+        self.layer = layer and not minmax     # one launch per layer (sbm_moe_fused_ffn)
+        self.ws_ffn = api.alloc_ffn_workspace(c.n_experts, c.n_tokens, dev) if self.layer else None
+        # a layer call reads x while other workgroups already write y: consecutive layers alternate buffers
+        self.y2 = [torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev) for _ in range(2)]
         self.ws_up = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
         self.ws_down = api.alloc_workspace(c.n_experts, c.n_tokens, dev)
         self.h = torch.empty(c.n_tokens, c.d_ff, dtype=torch.float16, device=dev)
@@ -153,15 +157,24 @@ class Runner:
         for checking; from layer 1 on the input is the previous y, which the up
         projection scales to unit RMS itself (the glue fused into its
         activation staging)."""
-        self.run_layers(keep)
-        return api.rms_glue(self.y, out=self.x[0])
+        y = self.run_layers(keep)
+        return api.rms_glue(y, out=self.x[0])
 
     def run_layers(self, keep=None):
-        """The fused launches of one pass (2 per layer), nothing else."""
+        """The fused launches of one pass (1 per layer with layer=True, else 2),
+        nothing else."""
         st = self.st
         x = st.x0
         for l in range(st.cfg.n_layers):
             ids = st.routes[l]
+            if self.layer:
+                y = self.y2[l & 1]
+                api.moe_fused_ffn(st.up[l], st.down[l], st.image, x, ids, h=self.h, y=y, workspace=self.ws_ffn,
+                                  in_rms=l > 0)
+                if keep is not None:
+                    keep[l] = (x.clone(), self.h.clone(), y.clone())
+                x = y
+                continue
             api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h,
                                         in_rms=l > 0, minmax=self.minmax)
             if keep is not None:
@@ -171,4 +184,4 @@ class Runner:
             if keep is not None:
                 keep[l] = keep[l] + (self.y.clone(),)
             x = self.y
-        return self.y
+        return x
