@@ -119,41 +119,39 @@ def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
 
 def fusion_baselines(st, run, reps: int = 5):
     """The touched experts of layer 0 three ways, same inputs: the fused
-    decode + matvec (two launches), the unfused path (GPU reference decode of
-    each matrix to symbols, dequantised to bf16, then a bf16 GEMM), and dense
-    bf16 GEMMs on uncompressed weights (decoded once, untimed).  The GEMMs are
-    the library's (hipBLASLt / rocBLAS through torch.matmul); these are
-    comparators for the fusion argument, not the product path."""
+    decode + matvec (two launches), the unfused path the cache-amplification
+    page argues against (each expert's matrices decompressed to dense fp16 by
+    the library's block-parallel decoder, sbm_decode_dense, then library fp16
+    GEMMs with the scales and ReLU applied to their outputs), and dense bf16
+    GEMMs on uncompressed weights (decoded once, untimed).  The GEMMs are the
+    platform's (hipBLASLt / rocBLAS through torch); these are comparators for
+    the fusion argument, not the product path.  The HBM floors price the
+    dense paths at 8 TB/s: bf16 weights read once (dense), fp16 weights
+    written, read back and the codes read (unfused)."""
     import numpy as np
     import torch
-    from sub_bit_moe_amd import api
+    from sub_bit_moe_amd import api, hybrid
     c = st.cfg
     dev = st.x0.device
-    words, _ = api.build_dictionary(c.dict_p0)
-    words_t = torch.from_numpy(words.view(np.int32)).to(dev)
     ids_h = st.routes_host[0]
     experts = [int(e) for e in np.unique(ids_h)]
     tok = {e: torch.from_numpy(np.flatnonzero(ids_h == e)).to(dev) for e in experts}
     x = st.x0
-    stacks = (st.up[0], st.down[0])
-    sym_buf = [torch.empty((s.rows, s.cols), dtype=torch.uint8, device=dev) for s in stacks]
+    up, down = st.up[0], st.down[0]
+    wu = torch.empty(up.rows, up.cols, dtype=torch.float16, device=dev)
+    wd = torch.empty(down.rows, down.cols, dtype=torch.float16, device=dev)
     bad = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def views(s, e):
-        d = s.host_desc[e]
-        return (s.codes[d.code_base:d.code_base + d.n_codes], s.row_off[d.off_base:d.off_base + s.rows + 1],
-                s.scales[d.scale_base:d.scale_base + s.rows])
+    def dense_bf16(s_, e):
+        w, _ = api.decode_dense(s_, e, st.image)
+        d = s_.host_desc[e]
+        sc = s_.scales[d.scale_base:d.scale_base + s_.rows].float()
+        return (w.float() * sc[:, None]).to(torch.bfloat16).t().contiguous()      # [cols, rows]
 
-    def dequant(s, e, buf):
-        codes, off, sc = views(s, e)
-        api.decode_ref(codes, off, s.rows, s.cols, words_t, out=buf, bad=bad)
-        w = (buf == 2).to(torch.bfloat16) - (buf == 1).to(torch.bfloat16)
-        return (w * sc.to(torch.bfloat16)[:, None]).t().contiguous()      # [cols, rows]
-
-    dense = {e: [dequant(s, e, sym_buf[m]) for m, s in enumerate(stacks)] for e in experts}
+    dense = {e: (dense_bf16(up, e), dense_bf16(down, e)) for e in experts}
     torch.cuda.synchronize()
-    assert int(bad.item()) == 0
     xb = x.to(torch.bfloat16)
+    yu = torch.empty_like(run.y)
 
     def run_dense():
         out = {}
@@ -164,13 +162,13 @@ def fusion_baselines(st, run, reps: int = 5):
 
     def run_unfused():
         for e in experts:
-            h = torch.relu(xb[tok[e]] @ dequant(stacks[0], e, sym_buf[0]))
-            h @ dequant(stacks[1], e, sym_buf[1])
+            ye, _ = hybrid.expert_ffn(up, down, e, st.image, x.index_select(0, tok[e]), wu=wu, wd=wd, bad=bad)
+            yu.index_copy_(0, tok[e], ye)
 
     def run_fused():
         ids = st.routes[0]
-        api.moe_fused_decode_matvec(st.up[0], st.image, x, ids, relu=True, workspace=run.ws_up, y=run.h)
-        api.moe_fused_decode_matvec(st.down[0], st.image, run.h, ids, workspace=run.ws_down, y=run.y)
+        api.moe_fused_decode_matvec(up, st.image, x, ids, relu=True, workspace=run.ws_up, y=run.h)
+        api.moe_fused_decode_matvec(down, st.image, run.h, ids, workspace=run.ws_down, y=run.y)
 
     def timed(fn):
         # each path captured in a graph, so launch overheads are the graph's
@@ -192,26 +190,30 @@ def fusion_baselines(st, run, reps: int = 5):
 
     t_fused, t_dense, t_unfused = timed(run_fused), timed(run_dense), timed(run_unfused)
     yd = run_dense()
+    run_fused()
     torch.cuda.synchronize()
     yf = run.y.float()
     num = sum(float(((yd[e].float() - yf[tok[e]]) ** 2).sum()) for e in experts)
     den = sum(float((yf[tok[e]] ** 2).sum()) for e in experts)
-    comp = sum(s.matrix_bytes(e) for e in experts for s in stacks)
-    dense_bytes = sum(2 * s.rows * s.cols for e in experts for s in stacks)
+    rel_unfused = float((yu.float() - yf).norm() / yf.norm())
+    comp = sum(s_.matrix_bytes(e) for e in experts for s_ in (up, down))
+    dense_bytes = sum(2 * s_.rows * s_.cols for e in experts for s_ in (up, down))
     return {"layer": 0, "experts": len(experts), "tokens": int(c.n_tokens),
-            "fused_us": round(t_fused, 1), "unfused_decode_bf16_gemm_us": round(t_unfused, 1),
+            "fused_us": round(t_fused, 1), "unfused_decode_dense_gemm_us": round(t_unfused, 1),
             "dense_bf16_gemm_us": round(t_dense, 1),
-            "dense_over_fused": round(t_dense / t_fused, 2), "unfused_over_fused": round(t_unfused / t_fused, 2),
+            "unfused_over_fused": round(t_unfused / t_fused, 2),
             "fused_compressed_GBps": round(comp / t_fused / 1e3, 1),
-            "dense_bf16_GBps": round(dense_bytes / t_dense / 1e3, 1),
             "dense_bf16_hbm_floor_us": round(dense_bytes / (HBM_PEAK_GBPS * 1e3), 1),
-            "unfused_hbm_floor_us": round(3 * dense_bytes / (HBM_PEAK_GBPS * 1e3), 1),
-            "dense_vs_fused_rel_l2": round((num / den) ** 0.5, 4),
-            "note": "each path graph-captured; fused = two launches of the library; unfused = reference "
-                    "decode kernel (one thread per row) + torch dequantise + bf16 GEMM per matrix; dense = "
-                    "bf16 GEMMs per expert on weights decoded beforehand (bf16 scales, hence the rel-L2 "
-                    "against the fused output); floors = bf16 weight bytes read once (dense) or written, "
-                    "read back and read again (unfused) at 8 TB/s"}
+            "dense_floor_over_fused": round(dense_bytes / (HBM_PEAK_GBPS * 1e3) / t_fused, 2),
+            "unfused_hbm_floor_us": round((2 * dense_bytes + comp) / (HBM_PEAK_GBPS * 1e3), 1),
+            "unfused_floor_over_fused": round((2 * dense_bytes + comp) / (HBM_PEAK_GBPS * 1e3) / t_fused, 2),
+            "unfused_vs_fused_rel_l2": round(rel_unfused, 5), "dense_vs_fused_rel_l2": round((num / den) ** 0.5, 4),
+            "bad_image": int(bad.item()),
+            "note": "each path graph-captured; fused = the library's two launches; unfused = per touched expert, "
+                    "sbm_decode_dense of up and down to fp16 {-1,0,+1} + library fp16 GEMMs (scales, ReLU on the "
+                    "outputs); dense = bf16 GEMMs per expert on weights decoded beforehand (one small GEMM per "
+                    "expert, so it is launch-bound: compare the floors); floors at 8 TB/s: bf16 weights read once "
+                    "(dense), fp16 weights written + read back + codes read (unfused)"}
 
 
 def minmax_pass(st, steps, warmup, sym_launch_us):
@@ -392,6 +394,155 @@ def decompress_hybrid(steps, warmup, thresholds=(16, 32)):
     return out
 
 
+def measured_peaks(gib: int = 4, reps: int = 10):
+    """Practical bandwidth of this GPU, as the cache-amplification page's host
+    roofline measures a "GPU device copy": a device-to-device copy of `gib`
+    GiB (torch copy_; bytes copied per second, each byte read and written)
+    and a streaming read of the same buffer (the library's probe,
+    sbm_stream_read: 16-byte loads, bytes read per second)."""
+    import torch
+    from sub_bit_moe_amd import api
+    n = gib << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fn in (("device_copy", lambda: b.copy_(a)), ("stream_read", lambda: api.stream_read(a, sink))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = round(n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.synchronize()
+    return out
+
+
+def _graph_time_us(fn, n_calls, warmup=2):
+    """Average time of fn(i) over i = 0 .. n_calls-1, captured in one graph."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            fn(i)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return 1e3 * e0.elapsed_time(e1) / n_calls
+
+
+def per_matrix_table(n_calls: int = 200, gb: float = 1.1):
+    """The QMoE page's per-layer kernel comparison (Figure 5, left) on MI355X:
+    for each Switch matrix shape, one token through the fused decode + matvec
+    of one compressed matrix against the library's bf16 GEMV on the same
+    shape uncompressed, as relative time.  Each side rotates over distinct
+    matrices totalling >= `gb` GB (beyond the 256 MB Infinity Cache), so
+    every call reads its weights from HBM.  Compressed matrices: generated on
+    the GPU at P(0) = 0.886, the page's static table; dense: random bf16."""
+    import math
+    import numpy as np
+    import torch
+    from sub_bit_moe_amd import api, synth
+    dev = torch.device("cuda:0")
+    words, checksum = api.build_dictionary(0.885)
+    image = api.device_image(words, dev)
+    trie = torch.from_numpy(api.build_trie(words)).to(dev)
+    table = torch.from_numpy(synth.scale_table().view(np.int16)).to(dev)
+    rows_out = []
+    for rows, cols in ((768, 3072), (3072, 768), (1024, 4096), (4096, 1024), (2080, 6144), (6144, 2080)):
+        est = rows * cols * 0.74 / 8 + 6 * rows
+        n_comp = int(math.ceil(gb * 1e9 / est))
+        stk = api.generate_stack(51, 0, n_comp, 0, rows, cols, 0.886, trie, table, dict_checksum=checksum)
+        comp_bytes = float(np.mean([stk.matrix_bytes(e) for e in range(0, n_comp, max(1, n_comp // 64))]))
+        x = torch.from_numpy(synth.activations(np.random.default_rng(rows), 1, cols)).to(dev)
+        order = [(i * 7919) % n_comp for i in range(n_calls)]
+        ids = [torch.full((1,), e, dtype=torch.int32, device=dev) for e in order]
+        ws = api.alloc_workspace(n_comp, 1, dev)
+        y = torch.empty(1, rows, dtype=torch.float16, device=dev)
+        t_fused = _graph_time_us(lambda i: api.moe_fused_decode_matvec(stk, image, x, ids[i], workspace=ws, y=y),
+                                 n_calls)
+        del stk, ids, ws
+        torch.cuda.synchronize()
+        n_dense = int(math.ceil(gb * 1e9 / (2 * rows * cols)))
+        W = [torch.randn(rows, cols, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(n_dense)]
+        xv = x[0].to(torch.bfloat16)
+        yb = torch.empty(rows, dtype=torch.bfloat16, device=dev)
+        t_bf16 = _graph_time_us(lambda i: torch.mv(W[i % n_dense], xv, out=yb), n_calls)
+        del W
+        torch.cuda.synchronize()
+        rows_out.append({"shape": f"{rows}x{cols}", "fused_us": round(t_fused, 2), "bf16_gemv_us": round(t_bf16, 2),
+                         "fused_over_bf16": round(t_fused / t_bf16, 3),
+                         "fused_compressed_GBps": round(comp_bytes / t_fused / 1e3, 1),
+                         "bf16_GBps": round(2 * rows * cols / t_bf16 / 1e3, 1),
+                         "compressed_matrices": n_comp, "dense_matrices": n_dense})
+        log(f"  {rows}x{cols}: fused {t_fused:.2f} us, bf16 GEMV {t_bf16:.2f} us")
+    return {"rows": rows_out,
+            "note": "one token per call (the page's Figure 5 setting); relative time = fused / bf16 (the page's "
+                    "metric: ~0.70-0.98 on an A6000, ~0.60-0.95 on an RTX 3090, context only); each side "
+                    f"rotates over >= {gb} GB of distinct matrices, {n_calls} calls per graph"}
+
+
+def c3_pair(n_pairs: int = 480, n_calls: int = 200):
+    """One c2048 expert pair (up 6144x2080 + down 2080x6144, P(0) = 0.886)
+    with T = 1, 8 and 32 tokens all routed to it, rotating over `n_pairs`
+    distinct pairs (~1.1 GB): the fused sparse path (two launches), the layer
+    call (one launch), the dense-tile MFMA instance (a6), and decompress-then-
+    GEMM (sbm_decode_dense + library fp16 GEMMs).  Time per pair."""
+    import numpy as np
+    import torch
+    from sub_bit_moe_amd import api, hybrid, stack as S, synth
+    cfg = S.StackConfig(n_layers=1, n_experts=n_pairs, n_tokens=32, seed=21)
+    st = S.build(cfg, torch.device("cuda:0"))
+    up, down = st.up[0], st.down[0]
+    dev = st.x0.device
+    pair_bytes = float(np.mean([up.matrix_bytes(e) + down.matrix_bytes(e) for e in range(n_pairs)]))
+    out = {"workload": f"c2048 pair (up 6144x2080 + down 2080x6144, P(0)=0.886), {n_pairs} distinct pairs "
+                       f"({n_pairs * pair_bytes / 1e9:.2f} GB) in rotation, {n_calls} calls per graph",
+           "pair_compressed_MB": round(pair_bytes / 1e6, 3)}
+    wu = torch.empty(up.rows, up.cols, dtype=torch.float16, device=dev)
+    wd = torch.empty(down.rows, down.cols, dtype=torch.float16, device=dev)
+    for T in (1, 8, 32):
+        x = torch.from_numpy(synth.activations(np.random.default_rng(T), T, cfg.d_model)).to(dev)
+        order = [(i * 7) % n_pairs for i in range(n_calls)]
+        ids = [torch.full((T,), e, dtype=torch.int32, device=dev) for e in order]
+        h = torch.empty(T, cfg.d_ff, dtype=torch.float16, device=dev)
+        y = torch.empty(T, cfg.d_model, dtype=torch.float16, device=dev)
+        wsu, wsd = api.alloc_workspace(n_pairs, T, dev), api.alloc_workspace(n_pairs, T, dev)
+        wsf = api.alloc_ffn_workspace(n_pairs, T, dev)
+
+        def two(i, mfma=False):
+            api.moe_fused_decode_matvec(up, st.image, x, ids[i], relu=True, workspace=wsu, y=h, mfma=mfma)
+            api.moe_fused_decode_matvec(down, st.image, h, ids[i], workspace=wsd, y=y, mfma=mfma)
+
+        res = {"sparse_two_launches_us": _graph_time_us(two, n_calls),
+               "layer_call_us": _graph_time_us(
+                   lambda i: api.moe_fused_ffn(up, down, st.image, x, ids[i], h=h, y=y, workspace=wsf), n_calls),
+               "mfma_a6_us": _graph_time_us(lambda i: two(i, True), n_calls),
+               "decompress_gemm_us": _graph_time_us(
+                   lambda i: hybrid.expert_ffn(up, down, order[i], st.image, x, wu=wu, wd=wd), n_calls // 4)}
+        res = {k: round(v, 2) for k, v in res.items()}
+        res["sparse_compressed_GBps"] = round(pair_bytes / res["sparse_two_launches_us"] / 1e3, 1)
+        out[f"T{T}"] = res
+        log(f"  C3 T={T}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
+    out["note"] = ("the dense-tile MFMA instance handles experts with 16 or more tokens; at T = 1 and 8 it runs "
+                   "the sparse path inside its own instance")
+    del st
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +559,10 @@ def main():
                     help="skip the table-built-for-the-data comparison (base128-shaped stack at P(0)=0.857)")
     ap.add_argument("--no-hybrid", action="store_true",
                     help="skip the decompress-then-GEMM comparison for heavy experts (one c2048 layer, 256 tokens)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured device-copy / streaming-read bandwidth")
+    ap.add_argument("--no-per-matrix", action="store_true",
+                    help="skip the per-matrix fused vs bf16 GEMV table (six Switch shapes, one token)")
+    ap.add_argument("--no-c3", action="store_true", help="skip the c2048 pair at T = 1, 8, 32 on every path")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one device copy of this many MiB (a known-size kernel for scaling "
                          "hardware byte counters)")
@@ -516,8 +671,20 @@ def main():
     if not args.no_fusion_baselines:
         log("fusion baselines (layer 0: unfused decode -> bf16 -> GEMM, dense bf16 GEMM) ...")
         fusion = fusion_baselines(st, run)
-        log(f"layer 0: fused {fusion['fused_us']} us, unfused {fusion['unfused_decode_bf16_gemm_us']} us, "
+        log(f"layer 0: fused {fusion['fused_us']} us, unfused {fusion['unfused_decode_dense_gemm_us']} us, "
             f"dense bf16 {fusion['dense_bf16_gemm_us']} us")
+    permat = None
+    if not args.no_per_matrix:
+        log("per-matrix fused vs bf16 GEMV, one token, six Switch shapes ...")
+        permat = per_matrix_table()
+    c3 = None
+    if not args.no_c3:
+        log("c2048 pair at T = 1, 8, 32 ...")
+        c3 = c3_pair()
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        log(f"measured peaks: {peaks}")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -545,12 +712,17 @@ def main():
                    "pass_compressed_MB": round(comp / 1e6, 1), "seed": cfg.seed},
         "bf16_equiv_GBps": round(bf16 / (ms * 1e-3) / 1e9, 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "pct_of_measured_read": round(100 * value / peaks["stream_read_GBps"], 2) if peaks else None,
+        "pct_of_measured_copy": round(100 * value / peaks["device_copy_GBps"], 2) if peaks else None,
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fusion_baselines": fusion,
         "minmax_grid": minmax,
         "dictionary_match": dmatch,
         "decompress_hybrid": hybrid,
+        "per_matrix_fig5": permat,
+        "c3_pair": c3,
     }
     print(json.dumps(out), flush=True)
 

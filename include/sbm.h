@@ -355,6 +355,14 @@ int sbm_gen_write(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, 
  * [n_tokens x d]; they may not alias. */
 int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint16_t* x_out, void* stream);
 
+/* Bandwidth probe (not part of the method): the cache-amplification page
+ * measures a GPU device copy as the practical ceiling of its host roofline
+ * ("Results", host roofline).  Streams `bytes` (a multiple of 16, buf 16-byte
+ * aligned) of device memory through 16-byte loads in a grid of at most
+ * sink_words workgroups, each writing one folded word to device sink[]; time
+ * the call on `stream` to get the read bandwidth. */
+int sbm_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t sink_words, void* stream);
+
 /* Workspace error word of the last fused call (device read; synchronises the
  * stream).  Bits 0-27: number of tokens whose expert id was out of range;
  * bit 28: (layer calls) the down phase gave up waiting for up rows;

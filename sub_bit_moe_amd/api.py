@@ -369,6 +369,12 @@ def generate_stack(seed: int, layer: int, n_experts: int, mat: int, rows: int, c
     return ExpertStack(rows, cols, n_experts, codes, row_off, bstart, scales, desc, host_desc, used)
 
 
+def stream_read(buf, sink, stream=None) -> None:
+    """Bandwidth probe: read every byte of the device tensor buf (sbm_stream_read)."""
+    check(lib().sbm_stream_read(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink), int(sink.numel()),
+                                _stream(stream)))
+
+
 def rms_glue(y, out=None, stream=None):
     """Stack glue (not the method): x_next = y / rms(y) per token, fp16."""
     import torch

@@ -323,3 +323,47 @@ extern "C" int sbm_rms_glue(const uint16_t* y, int32_t n_tokens, int32_t d, uint
   if (e != hipSuccess) return sbm::fail(SBM_EHIP, "rms_glue launch: %s", hipGetErrorString(e));
   return SBM_OK;
 }
+
+// ------------------------------------------------------------ bandwidth probe
+// The practical read bandwidth of the device, the denominator the
+// cache-amplification page uses for its host roofline ("Results", host
+// roofline table: a measured GPU device copy next to the nominal figure):
+// a grid-stride stream of 16-byte loads over the buffer, folded into one
+// word per workgroup so the loads cannot be dropped.
+namespace sbm {
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ p, uint64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < n16; i += 4 * stride) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = i + k * stride < n16 ? __builtin_nontemporal_load(p + i + k * stride)
+                                                           : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  __shared__ uint32_t s[256];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < 256; ++i) r ^= s[i];
+    sink[blockIdx.x] = r;
+  }
+}
+}  // namespace sbm
+
+extern "C" int sbm_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t sink_words, void* stream) {
+  if (!buf || !sink || sink_words == 0) return sbm::fail(SBM_EINVAL, "null pointer or empty sink");
+  if (((uintptr_t)buf & 15u) || (bytes & 15u)) return sbm::fail(SBM_EINVAL, "buffer and size must be multiples of 16");
+  if (bytes == 0) return SBM_OK;
+  const uint64_t n16 = bytes / 16u;
+  const unsigned grid = (unsigned)std::min<uint64_t>(sink_words, std::max<uint64_t>(1, n16 / 1024));
+  hipLaunchKernelGGL(sbm::stream_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const sbm::u32x4_t*)buf, n16,
+                     sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sbm::fail(SBM_EHIP, "stream_read launch: %s", hipGetErrorString(e));
+  return SBM_OK;
+}
