@@ -208,17 +208,6 @@ using namespace sbm;
 
 extern "C" {
 
-size_t sbm_trie_words(void) { return (size_t)(SBM_DICT_ENTRIES + 1) * 9; }
-
-int sbm_build_trie(const uint32_t* words, int32_t* out_child) {
-  if (!words || !out_child) return fail(SBM_EINVAL, "null pointer");
-  std::vector<int32_t> child;
-  const int st = build_trie(words, child);
-  if (st) return st;
-  std::copy(child.begin(), child.end(), out_child);
-  return SBM_OK;
-}
-
 int sbm_gen_count(uint64_t seed, int32_t layer, int32_t n_experts, int32_t mat, int32_t rows, int32_t cols,
                   uint32_t zero_threshold16, const int32_t* trie, uint32_t* row_counts, void* stream) {
   int st = check_gen(layer, n_experts, mat, rows, cols);

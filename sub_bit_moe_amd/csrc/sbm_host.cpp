@@ -547,6 +547,17 @@ int sbm_dict_image(const uint32_t* words, void* out_image, size_t image_bytes) {
   return sbm::dict_image(words, out_image, image_bytes);
 }
 
+size_t sbm_trie_words(void) { return (size_t)(SBM_DICT_ENTRIES + 1) * 9; }
+
+int sbm_build_trie(const uint32_t* words, int32_t* out_child) {
+  if (!words || !out_child) return sbm::fail(SBM_EINVAL, "null pointer");
+  std::vector<int32_t> child;
+  const int st = sbm::build_trie(words, child);
+  if (st) return st;
+  std::copy(child.begin(), child.end(), out_child);
+  return SBM_OK;
+}
+
 int sbm_encode_size(const uint8_t* sym, int32_t rows, int32_t cols, const uint32_t* words,
                     uint64_t* n_codes) {
   return sbm::encode_size(sym, rows, cols, words, n_codes);
