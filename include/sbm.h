@@ -89,6 +89,15 @@ typedef enum {
                              gathers 4 activation slots per codeword instead of 3, from a 65.5 KB
                              LDS table, which leaves less LDS for activation rows.  dict_image
                              must then hold sbm_dict_image4_bytes() bytes.  Not with SBM_F_MFMA. */
+#define SBM_F_DETERMINISTIC 64u  /* bit-reproducible outputs: the row accumulators are 64-bit
+                             integers in units of 2^-S (S = 34 - ceil(log2(3 (cols/1024 + 2))),
+                             29 for 6144 columns) instead of fp32 LDS atomics, so each fp32
+                             partial sum is rounded once to that grid and the sums do not depend
+                             on the order in which waves add them.  The same call on the same
+                             device then returns the same bits every time.  The pages leave the
+                             summation order open.  Costs LDS (8-byte accumulators: shorter row
+                             chunks) and a few conversions per block.  Activations must be finite.
+                             Not with SBM_F_MFMA; not a flag of the layer call. */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);

@@ -259,12 +259,14 @@ def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
 
 def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
                             out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False,
-                            mfma: bool = False, minmax: bool = False, image4=None):
+                            mfma: bool = False, minmax: bool = False, image4=None,
+                            deterministic: bool = False):
     """y[t] = act(W_{expert_ids[t]} x[t]) for one projection of an MoE layer
     (in_rms: x[t] is first scaled to unit RMS, as rms_glue does; mfma=True
     sends experts with 16 or more tokens to the dense-tile MFMA path; minmax:
     the stack's scales are (w_min, w_max) per row, the page's grid; image4:
-    image_t is a 4-slot image, by default told from its byte size)."""
+    image_t is a 4-slot image, by default told from its byte size;
+    deterministic: fixed-point row accumulators, bit-reproducible outputs)."""
     import torch
     T = int(x.shape[0]) if x is not None else 0
     if y is None:
@@ -275,6 +277,7 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
     flags = (N.SBM_F_RELU if relu else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0) | (N.SBM_F_IN_RMS if in_rms else 0)
     flags |= N.SBM_F_MFMA if mfma else 0
     flags |= N.SBM_F_MINMAX if minmax else 0
+    flags |= N.SBM_F_DETERMINISTIC if deterministic else 0
     n4 = int(lib().sbm_dict_image4_bytes())
     if image4 is None:
         image4 = int(image_t.numel()) == n4

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 #include <mutex>
 
@@ -132,6 +133,7 @@ struct FusedArgs {
   uint32_t lds_racc;    // byte offsets in LDS
   uint32_t lds_x;
   int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
+  int32_t det_shift;    // SBM_F_DETERMINISTIC: accumulator terms are rounded to multiples of 2^-det_shift
   uint32_t* err_out;    // if set, workgroup 0 copies the finished error word here
   // layer calls (up, ReLU, down in one launch): per-token counts of up rows
   // written, the count a token needs before its down rows start, and the
@@ -616,8 +618,55 @@ __device__ __forceinline__ void decode_block(const BlockCodes& raw, uint32_t spl
   d.pl = 6u * raw.bst + wave_incl_scan(tot) - tot;
 }
 
+// Row accumulators.  By default fp32 with LDS float atomics: the order in
+// which waves add their partial sums varies from run to run, and so do the
+// last bits of a row sum.  With SBM_F_DETERMINISTIC they are 64-bit integers
+// in units of 2^-det_shift: each fp32 partial sum is rounded once to that
+// grid and the integer sums are exact, so the result does not depend on the
+// order of the additions.  The host picks det_shift so that no accumulator
+// can overflow (every partial sum is below 2^28 for fp16 activations, and a
+// row accumulator receives at most 3 per block touching the row).
+__device__ __forceinline__ unsigned long long to_fixed(float v, int sh) {
+  return (unsigned long long)(long long)rint(ldexp((double)v, sh));
+}
+__device__ __forceinline__ float from_fixed(unsigned long long q, int sh) {
+  return (float)ldexp((double)(long long)q, -sh);
+}
+template <bool DET>
+constexpr uint32_t acc_bytes() { return DET ? 8u : 4u; }
+// Accumulator slot idx of activation row t.
+template <bool DET>
+__device__ __forceinline__ void racc_add(const FusedArgs& a, unsigned char* smem, int t, int32_t idx, float v) {
+  unsigned char* base = smem + a.lds_racc + (uint32_t)t * (uint32_t)(a.rmax + 2) * acc_bytes<DET>();
+  if constexpr (DET) atomicAdd((unsigned long long*)base + idx, to_fixed(v, a.det_shift));
+  else atomicAdd((float*)base + idx, v);
+}
+// Read and clear.
+template <bool DET>
+__device__ __forceinline__ float racc_take(const FusedArgs& a, unsigned char* smem, int t, int32_t idx) {
+  unsigned char* base = smem + a.lds_racc + (uint32_t)t * (uint32_t)(a.rmax + 2) * acc_bytes<DET>();
+  if constexpr (DET) {
+    unsigned long long* p = (unsigned long long*)base + idx;
+    const unsigned long long q = *p;
+    *p = 0ull;
+    return from_fixed(q, a.det_shift);
+  } else {
+    float* p = (float*)base + idx;
+    const float v = *p;
+    *p = 0.f;
+    return v;
+  }
+}
+// Zero the accumulators of every activation row.
+template <bool DET>
+__device__ __forceinline__ void racc_clear(const FusedArgs& a, unsigned char* smem) {
+  const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) * acc_bytes<DET>() + 15u) / 16u;   // 16B-aligned
+  uint4* r = (uint4*)(smem + a.lds_racc);
+  for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) r[i] = make_uint4(0, 0, 0, 0);
+}
+
 // Multiply-accumulate of one decoded block into the row accumulators.
-template <int TC, bool SMALL, int NS>
+template <int TC, bool SMALL, int NS, bool DET>
 __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, unsigned char* smem, const DecBlock& d) {
   const int lane = threadIdx.x & 63;
   const uint32_t tot = d.tot, pl = d.pl;
@@ -625,7 +674,6 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
   ls[0] = 0;
 #pragma unroll
   for (int j = 1; j < kK; ++j) ls[j] = ls[j - 1] + run_b<NS>(d.s[j - 1]);
-  float* racc = (float*)(smem + a.lds_racc);
   const int32_t R = ch.rb - ch.ra;
   if constexpr (!SMALL) {
     const uint32_t rl = div_magic_dev(pl, a.magic_m, a.magic_s);
@@ -678,13 +726,12 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
       const float S = wave_incl_scan_f(acc[t]);
-      float* rt = racc + t * (a.rmax + 2);
       if (closes) {
         const float Ev = S - (acc[t] - snap[t]);
-        atomicAdd(rt + ia, Ev);
-        atomicAdd(rt + ib, -Ev);
+        racc_add<DET>(a, smem, t, ia, Ev);
+        racc_add<DET>(a, smem, t, ib, -Ev);
       }
-      if (lane == 63) atomicAdd(rt + (closes ? ib : ia), S);
+      if (lane == 63) racc_add<DET>(a, smem, t, closes ? ib : ia, S);
     }
   } else {
     // narrow rows: a lane may span several rows; locate every codeword's row
@@ -705,7 +752,7 @@ __device__ __forceinline__ void accumulate(const FusedArgs& a, const Chunk& ch, 
       const int32_t i0 = (int32_t)r - ch.ra + 1;
       const int32_t ii = i0 < 0 ? 0 : (i0 > R + 1 ? R + 1 : i0);
 #pragma unroll
-      for (int t = 0; t < TC; ++t) atomicAdd(racc + t * (a.rmax + 2) + ii, v[t]);
+      for (int t = 0; t < TC; ++t) racc_add<DET>(a, smem, t, ii, v[t]);
     }
   }
 }
@@ -989,12 +1036,12 @@ __device__ __forceinline__ int tc_of(uint32_t nt) { return nt <= 1 ? 1 : (nt <= 
 // Interleaved activation rows of an item of nt tokens.
 __device__ __forceinline__ int tc_rows(const FusedArgs& a, uint32_t nt) { return tc_of(a.minmax ? 2 * nt : nt); }
 
-template <bool SMALL, int NS>
+template <bool SMALL, int NS, bool DET>
 __device__ __forceinline__ void process_dispatch(int tc, const FusedArgs& a, const Chunk& ch, unsigned char* smem,
                                                  const DecBlock& d) {
-  if (tc == 1) accumulate<1, SMALL, NS>(a, ch, smem, d);
-  else if (tc == 2) accumulate<2, SMALL, NS>(a, ch, smem, d);
-  else accumulate<4, SMALL, NS>(a, ch, smem, d);
+  if (tc == 1) accumulate<1, SMALL, NS, DET>(a, ch, smem, d);
+  else if (tc == 2) accumulate<2, SMALL, NS, DET>(a, ch, smem, d);
+  else accumulate<4, SMALL, NS, DET>(a, ch, smem, d);
 }
 
 // ------------------------------------------------------------ dense-tile MFMA path
@@ -1369,17 +1416,13 @@ __device__ __forceinline__ Slot grab(const FusedArgs& a, uint32_t nseq, uint32_t
 
 // MFMA: the kernel instance that runs dense-tile items (SBM_F_MFMA); the
 // default instance has no call in its loop, which keeps its registers unspilled.
-template <bool SMALL, bool MFMA, int NS, int LM = 0>
+template <bool SMALL, bool MFMA, int NS, int LM = 0, bool DET = false>
 __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* smem, const int32_t* perm, const uint4* items,
                           uint64_t g0, uint64_t g1, uint32_t split7) {
-  float* racc = (float*)(smem + a.lds_racc);
   // the image copy issued at kernel entry is waited for just before the
   // barrier that follows the first activation staging (or inside the first
   // dense tile), so the chunk table and first blocks are fetched meanwhile
-  {
-    const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;   // lds_racc region is 16B-aligned
-    for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
-  }
+  racc_clear<DET>(a, smem);
   build_chunks(a, items, g0, g1);
   uint32_t cur_q = 0xFFFFFFFFu;
   while (true) {
@@ -1399,8 +1442,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
           if (x_vec(a)) mfma_chunk<true>(a, smem, perm, ch, split7);
           else mfma_chunk<false>(a, smem, perm, ch, split7);
         }
-        const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) + 3u) / 4u;
-        for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) ((uint4*)racc)[i] = make_uint4(0, 0, 0, 0);
+        racc_clear<DET>(a, smem);
         cur_q = 0xFFFFFFFFu;
         __syncthreads();
         continue;
@@ -1420,7 +1462,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         DecBlock d;
         decode_block<NS>(sl.v, split7, d);
         sl = grab(a, nseq, nch, -1, &ch, seq_end);
-        process_dispatch<SMALL, NS>(tc, a, ch, smem, d);
+        process_dispatch<SMALL, NS, DET>(tc, a, ch, smem, d);
         return true;
       };
       while (step(A)) {
@@ -1471,11 +1513,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
           const float wmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc[k] & 0xFFFFu));
           const float wmax = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc[k] >> 16));
           for (int u = 0; 2 * u < tc; ++u) {
-            float* pa = racc + (2 * u) * (a.rmax + 2) + i;
-            float* pb = pa + (a.rmax + 2);
-            const float A = *pa, B = *pb;
-            *pa = 0.f;
-            *pb = 0.f;
+            const float A = racc_take<DET>(a, smem, 2 * u, i), B = racc_take<DET>(a, smem, 2 * u + 1, i);
             if (ch.ok && i >= 1 && i <= R && (uint32_t)u < ch.nt) {
               float v = 0.5f * ((wmax - wmin) * A + (wmax + wmin) * B);
               if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
@@ -1487,9 +1525,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         } else if (i < R + 2) {
           const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[k]);
           for (int t = 0; t < tc; ++t) {
-            float* p = racc + t * (a.rmax + 2) + i;
-            float v = *p;
-            *p = 0.f;
+            float v = racc_take<DET>(a, smem, t, i);
             if (ch.ok && i >= 1 && i <= R && (uint32_t)t < ch.nt) {
               v *= s;
               if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
@@ -1766,15 +1802,20 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
 }
 
 // Instances: MODE 0 the sparse path, 1 with dense-tile MFMA items, 2 with the
-// per-row min/max grid; 3 and 4 are 0 and 2 with the 4-slot decode image.
-// The grid flag is made a constant of each instance, so the default instance
-// carries none of its code.
-constexpr int kModes = 5;
+// per-row min/max grid; 3 and 4 are 0 and 2 with the 4-slot decode image;
+// 5 to 8 are 0, 2, 3 and 4 with fixed-point row accumulators
+// (SBM_F_DETERMINISTIC).  The grid flag is made a constant of each instance,
+// so the default instance carries none of its code.
+constexpr int kModes = 9;
+__host__ __device__ constexpr int mode_base(int m) { return m == 5 ? 0 : m == 6 ? 2 : m == 7 ? 3 : m == 8 ? 4 : m; }
+__host__ __device__ constexpr int mode_slots(int m) { return mode_base(m) >= 3 ? 4 : 3; }
 template <int MODE>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
-  constexpr bool MFMA = MODE == 1;
-  constexpr int NS = MODE >= 3 ? 4 : 3;
-  a.minmax = (MODE == 2 || MODE == 4) ? 1 : 0;
+  constexpr int BASE = mode_base(MODE);
+  constexpr bool DET = MODE >= 5;
+  constexpr bool MFMA = BASE == 1;
+  constexpr int NS = mode_slots(MODE);
+  a.minmax = (BASE == 2 || BASE == 4) ? 1 : 0;
   extern __shared__ __align__(16) unsigned char smem[];
   // Requests in order of need: token ids (every thread, no branch, so the
   // request goes out with the first argument loads), the image header in one
@@ -1826,8 +1867,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     items = (const uint4*)(a.ws + L.items);
   }
   if (g0 >= g1) return;
-  if (a.cols < kSmallCols) run_slice<true, MFMA, NS>(a, smem, perm, items, g0, g1, split7);
-  else run_slice<false, MFMA, NS>(a, smem, perm, items, g0, g1, split7);
+  if (a.cols < kSmallCols) run_slice<true, MFMA, NS, 0, DET>(a, smem, perm, items, g0, g1, split7);
+  else run_slice<false, MFMA, NS, 0, DET>(a, smem, perm, items, g0, g1, split7);
 }
 
 // ------------------------------------------------------------ layer calls
@@ -1917,7 +1958,7 @@ struct DevInfo {
   int cus = 0;
   int max_lds = 0;        // LDS per workgroup
   // static LDS of the fused-kernel instances, per image kind: the largest over
-  // the instances one call may launch (0-2: 3-slot image, 3-4: 4-slot image)
+  // the instances one call may launch (3-slot or 4-slot image)
   int static_lds[2] = {};
   int ffn_static_lds = 0;
   bool attr_set = false;
@@ -1939,6 +1980,10 @@ static const void* fused_instance(int mode) {
     case 2: return (const void*)fused_kernel<2>;
     case 3: return (const void*)fused_kernel<3>;
     case 4: return (const void*)fused_kernel<4>;
+    case 5: return (const void*)fused_kernel<5>;
+    case 6: return (const void*)fused_kernel<6>;
+    case 7: return (const void*)fused_kernel<7>;
+    case 8: return (const void*)fused_kernel<8>;
     default: return (const void*)fused_kernel<0>;
   }
 }
@@ -1965,12 +2010,12 @@ static int dev_info(DevInfo** out, bool want_scratch = false) {
       hipFuncAttributes fa;
       if ((e = hipFuncGetAttributes(&fa, fused_instance(m))) != hipSuccess)
         return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
-      int& st = di.static_lds[m >= 3 ? 1 : 0];
+      int& st = di.static_lds[mode_slots(m) == 4 ? 1 : 0];
       st = std::max(st, (int)fa.sharedSizeBytes);
     }
     for (int m = 0; m < kModes; ++m) {
       e = hipFuncSetAttribute(fused_instance(m), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              di.max_lds - di.static_lds[m >= 3 ? 1 : 0]);
+                              di.max_lds - di.static_lds[mode_slots(m) == 4 ? 1 : 0]);
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
     {
@@ -1999,19 +2044,20 @@ struct Plan {
   int tcmax, rmax, xcols;
   uint32_t lds_racc, lds_x, lds_total;
 };
-static bool make_plan(int cols, int max_lds, int static_lds, Plan* p) {
+static bool make_plan(int cols, int max_lds, int static_lds, Plan* p, bool det = false) {
   p->xcols = (cols + (cols >= kSmallCols ? kXWrap : kXPad) + 7) / 8 * 8;
+  const int ab = det ? 8 : 4;    // bytes per row accumulator
   // prefer more tokens per item, then the longest row chunks that fit
   for (int tc : {4, 2, 1}) {
     const uint32_t xbytes = (uint32_t)(p->xcols * 6 * tc);
     const int64_t room = (int64_t)max_lds - static_lds - xbytes - 32;
-    int64_t rmax = room / (4 * tc) - 2;
+    int64_t rmax = room / (ab * tc) - 2;
     if (rmax > kMaxRmax) rmax = kMaxRmax;
     if (rmax < (tc > 1 ? 256 : 64)) continue;
     p->tcmax = tc;
     p->rmax = (int)rmax;
     p->lds_racc = 0;
-    p->lds_x = ((uint32_t)(tc * (rmax + 2) * 4) + 15u) & ~15u;
+    p->lds_x = ((uint32_t)(tc * (rmax + 2) * ab) + 15u) & ~15u;
     p->lds_total = (p->lds_x + xbytes + 15u) & ~15u;
     return true;
   }
@@ -2110,8 +2156,11 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   if (cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", cols);
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
-  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX | SBM_F_IMAGE4))
+  if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX | SBM_F_IMAGE4 |
+                SBM_F_DETERMINISTIC))
     return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & SBM_F_DETERMINISTIC) && (flags & SBM_F_MFMA))
+    return fail(SBM_EINVAL, "SBM_F_DETERMINISTIC and SBM_F_MFMA cannot be combined");
   if ((flags & SBM_F_MINMAX) && (flags & SBM_F_MFMA))
     return fail(SBM_EINVAL, "SBM_F_MINMAX and SBM_F_MFMA cannot be combined");
   if ((flags & SBM_F_IMAGE4) && (flags & SBM_F_MFMA))
@@ -2128,9 +2177,11 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   if (st) return st;
   if (use_scratch) workspace = di->scratch;
   const bool minmax = (flags & SBM_F_MINMAX) != 0;
-  const int mode = (flags & SBM_F_MFMA) ? 1 : ((flags & SBM_F_IMAGE4) ? (minmax ? 4 : 3) : (minmax ? 2 : 0));
+  const bool det = (flags & SBM_F_DETERMINISTIC) != 0;
+  int mode = (flags & SBM_F_MFMA) ? 1 : ((flags & SBM_F_IMAGE4) ? (minmax ? 4 : 3) : (minmax ? 2 : 0));
+  if (det) mode = mode == 0 ? 5 : (mode == 2 ? 6 : (mode == 3 ? 7 : 8));
   Plan plan;
-  if (!make_plan(cols, di->max_lds, di->static_lds[mode >= 3 ? 1 : 0], &plan))
+  if (!make_plan(cols, di->max_lds, di->static_lds[mode_slots(mode) == 4 ? 1 : 0], &plan, det))
     return fail(SBM_ERANGE, "cols=%d: one token row does not fit in %d bytes of LDS", cols, di->max_lds);
   if (minmax && plan.tcmax < 2)
     return fail(SBM_ERANGE, "cols=%d: the min/max grid needs two activation rows per token in LDS", cols);
@@ -2146,6 +2197,14 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   fill_args(a, codes, row_off, bstart, scales, experts, n_experts, rows, cols, dict_image, x, expert_ids, n_tokens,
             y, flags, workspace, plan, (int32_t)grid);
   a.err_out = err_out;
+  if (det) {
+    // Every partial sum added to a row accumulator is below 2^28 (a block of
+    // 1024 codewords, at most 4 nonzeros each, |x| <= 65504 < 2^16), and a row
+    // accumulator receives at most 3 of them per block that touches its row,
+    // at most cols / SBM_BLOCK + 2 blocks; 2^62 bounds the integer sums.
+    const double terms = 3.0 * ((double)cols / SBM_BLOCK + 2.0);
+    a.det_shift = 62 - 28 - (int)std::ceil(std::log2(terms));
+  }
   hipStream_t s = (hipStream_t)stream;
   // the in-kernel grouping keeps its sort keys at the start of dynamic LDS
   const uint32_t lds = std::max<uint32_t>(plan.lds_total, kGroupScratch);
@@ -2158,6 +2217,10 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   hipError_t e;
   if (!a.group_in_lds && (st = launch_group(a, s))) return st;
   if (a.mfma_rows > 0) hipLaunchKernelGGL(fused_kernel<1>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 5) hipLaunchKernelGGL(fused_kernel<5>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 6) hipLaunchKernelGGL(fused_kernel<6>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 7) hipLaunchKernelGGL(fused_kernel<7>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
+  else if (mode == 8) hipLaunchKernelGGL(fused_kernel<8>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (mode == 3) hipLaunchKernelGGL(fused_kernel<3>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (mode == 4) hipLaunchKernelGGL(fused_kernel<4>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
   else if (a.minmax) hipLaunchKernelGGL(fused_kernel<2>, dim3((unsigned)grid), dim3(kFThreads), lds, s, a);
