@@ -253,6 +253,44 @@ def minmax_pass(st, steps, warmup, sym_launch_us):
     return out
 
 
+def deterministic_pass(st, steps, warmup, sym_launch_us):
+    """The main pass with SBM_F_DETERMINISTIC (64-bit fixed-point row
+    accumulators): graph-captured and timed like the main pass, and two
+    replays compared bit for bit."""
+    import torch
+    from sub_bit_moe_amd import stack as S
+    run = S.Runner(st, deterministic=True)
+    run.run_layers()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = run.run_layers()
+    g.replay()
+    torch.cuda.synchronize()
+    first = out.clone()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, first))
+    stream = torch.cuda.current_stream()
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    same = same and bool(torch.equal(out, first))
+    n_launch = 2 * st.cfg.n_layers
+    us = 1e3 * k0.elapsed_time(k1) / (steps * n_launch)
+    comp, _ = st.pass_bytes()
+    res = {"avg_launch_us": round(us, 2), "GBps": round(comp / n_launch / (us * 1e-6) / 1e9, 1),
+           "launch_time_vs_default": round(us / sym_launch_us, 3), "replays_bit_identical": same}
+    del g, run
+    torch.cuda.synchronize()
+    return res
+
+
 def dictionary_match(steps, warmup):
     """A table built for the data against the page's static one ([QMoE]
     "Limitations and Trade-offs" and Table 7: the static table is tuned to
@@ -555,6 +593,7 @@ def main():
                     help="skip the unfused and dense bf16 comparators on layer 0")
     ap.add_argument("--no-minmax", action="store_true",
                     help="skip the pass on the page's per-row (w_min, w_max) grid")
+    ap.add_argument("--no-det", action="store_true", help="skip the pass with fixed-point row accumulators")
     ap.add_argument("--no-dict-match", action="store_true",
                     help="skip the table-built-for-the-data comparison (base128-shaped stack at P(0)=0.857)")
     ap.add_argument("--no-hybrid", action="store_true",
@@ -654,6 +693,11 @@ def main():
         log("pass on the per-row (w_min, w_max) grid ...")
         minmax = minmax_pass(st, args.steps, args.warmup, launch_us)
         log(f"min/max grid: {minmax['avg_launch_us']} us per launch, {minmax['GBps']} GB/s")
+    det = None
+    if not args.no_det:
+        log("pass with fixed-point row accumulators (SBM_F_DETERMINISTIC) ...")
+        det = deterministic_pass(st, args.steps, args.warmup, launch_us)
+        log(f"deterministic: {det['avg_launch_us']} us per launch, bit-identical replays: {det['replays_bit_identical']}")
     dmatch = None
     if not args.no_dict_match:
         log("dictionary built for the data vs the static table (base128-shaped stack) ...")
@@ -719,6 +763,7 @@ def main():
         "cpu_baseline": cpu,
         "fusion_baselines": fusion,
         "minmax_grid": minmax,
+        "deterministic": det,
         "dictionary_match": dmatch,
         "decompress_hybrid": hybrid,
         "per_matrix_fig5": permat,

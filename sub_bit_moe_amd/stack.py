@@ -133,15 +133,16 @@ def with_minmax(st: Stack, seed: int = 7) -> Stack:
 
 class Runner:
     """Preallocated buffers for repeated passes (minmax: the stack's scales
-    are (w_min, w_max) pairs)."""
+    are (w_min, w_max) pairs; deterministic: fixed-point row accumulators)."""
 
-    def __init__(self, st: Stack, minmax: bool = False, layer: bool = False):
+    def __init__(self, st: Stack, minmax: bool = False, layer: bool = False, deterministic: bool = False):
         import torch
         c = st.cfg
         dev = st.x0.device
         self.st = st
         self.minmax = minmax
-        self.layer = layer and not minmax     # one launch per layer (sbm_moe_fused_ffn)
+        self.det = deterministic
+        self.layer = layer and not minmax and not deterministic   # one launch per layer (sbm_moe_fused_ffn)
         self.ws_ffn = api.alloc_ffn_workspace(c.n_experts, c.n_tokens, dev) if self.layer else None
         # a layer call reads x while other workgroups already write y: consecutive layers alternate buffers
         self.y2 = [torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev) for _ in range(2)]
@@ -176,11 +177,11 @@ class Runner:
                 x = y
                 continue
             api.moe_fused_decode_matvec(st.up[l], st.image, x, ids, relu=True, workspace=self.ws_up, y=self.h,
-                                        in_rms=l > 0, minmax=self.minmax)
+                                        in_rms=l > 0, minmax=self.minmax, deterministic=self.det)
             if keep is not None:
                 keep[l] = (x.clone(), self.h.clone())
             api.moe_fused_decode_matvec(st.down[l], st.image, self.h, ids, workspace=self.ws_down, y=self.y,
-                                        minmax=self.minmax)
+                                        minmax=self.minmax, deterministic=self.det)
             if keep is not None:
                 keep[l] = keep[l] + (self.y.clone(),)
             x = self.y
