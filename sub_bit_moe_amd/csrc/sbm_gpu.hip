@@ -78,6 +78,9 @@ __shared__ LdsTables4 g_tab4;
 // workspace layout (uint32 words)
 constexpr uint32_t kWsHdr = 16;   // [0] error count, [1] n_items, [2] total item weight
 constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed slices
+// Workgroups of a call: one per kRowsPerGroup output rows an upper bound of the
+// items could hold, at most one per CU.
+constexpr int64_t kRowsPerGroup = 16;
 constexpr int kItemChangeBlocks = 20;   // measured: a chunk change costs ~16 one-token blocks
 // Heavy experts (at least kMfmaMinTokens tokens) take the dense-tile MFMA path:
 // items of up to kMfmaMaxTokens tokens, flagged in the item's token-count word.
@@ -1904,10 +1907,13 @@ __device__ __forceinline__ void ffn_phase(const FusedArgs& a, unsigned char* sme
     perm = s_perm;
     items = s_items;
   } else {
+    // the grouping launch cut the phase into a.grid slices; the layer launch
+    // may hold more workgroups (the other phase's count)
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
-    g0 = bounds[blockIdx.x];
-    g1 = bounds[blockIdx.x + 1];
+    const bool mine = (int32_t)blockIdx.x < a.grid;
+    g0 = mine ? bounds[blockIdx.x] : 0;
+    g1 = mine ? bounds[blockIdx.x + 1] : 0;
     perm = (const int32_t*)(a.ws + L.perm);
     items = (const uint4*)(a.ws + L.items);
   }
@@ -2190,7 +2196,7 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   FusedArgs a;
   const int64_t max_items = (int64_t)std::min(n_experts, n_tokens) + n_tokens / (minmax ? plan.tcmax / 2 : plan.tcmax) + 1;
   const int64_t n_upper = max_items * rows;
-  int64_t grid = (n_upper + 63) / 64;
+  int64_t grid = (n_upper + kRowsPerGroup - 1) / kRowsPerGroup;
   if (grid > di->cus) grid = di->cus;
   if (grid > kMaxGrid) grid = kMaxGrid;
   if (grid < 1) grid = 1;
@@ -2298,15 +2304,23 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
   if (!make_plan(up->cols, di->max_lds, di->ffn_static_lds, &pu) ||
       !make_plan(down->cols, di->max_lds, di->ffn_static_lds, &pd))
     return fail(SBM_ERANGE, "a token row does not fit in %d bytes of LDS", di->max_lds);
-  const int32_t grid = std::min(di->cus, kMaxGrid);
+  // Each phase is cut into as many slices as its rows fill at 64 rows per
+  // workgroup (as a projection call is), at most one per CU; the launch holds
+  // the larger count, and workgroups past a phase's count skip that phase.
+  auto phase_grid = [&](const sbm_projection* p, const Plan& pl) {
+    const int64_t max_items = (int64_t)std::min(p->n_experts, n_tokens) + n_tokens / pl.tcmax + 1;
+    const int64_t g = (max_items * p->rows + kRowsPerGroup - 1) / kRowsPerGroup;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(g, std::min(di->cus, kMaxGrid)));
+  };
+  const int32_t grid_u = phase_grid(up, pu), grid_d = phase_grid(down, pd), grid = std::max(grid_u, grid_d);
   uint32_t* sync = (uint32_t*)workspace;
   unsigned char* wsu = (unsigned char*)workspace + align16(((size_t)kSyncHdr + (size_t)n_tokens) * 4u);
   unsigned char* wsd = wsu + align16(sbm_workspace_bytes(up->n_experts, n_tokens));
   FusedArgs ua, da;
   fill_args(ua, up->codes, up->row_off, up->bstart, up->scales, up->experts, up->n_experts, up->rows, up->cols,
-            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & SBM_F_IN_RMS), wsu, pu, grid);
+            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & SBM_F_IN_RMS), wsu, pu, grid_u);
   fill_args(da, down->codes, down->row_off, down->bstart, down->scales, down->experts, down->n_experts, down->rows,
-            down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, wsd, pd, grid);
+            down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, wsd, pd, grid_d);
   ua.tok_done = da.tok_done = sync + kSyncHdr;
   ua.sync_err = da.sync_err = sync + 1;
   da.tok_expect = (uint32_t)up->rows;
