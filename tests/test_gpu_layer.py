@@ -144,3 +144,39 @@ def test_layer_call_argument_errors(dev, c2048):
                                             api.build_dictionary(0.885)[0], dev)
     with pytest.raises(N.SbmError):          # rows narrower than 512 columns
         api.moe_fused_ffn(small, small_dn, st.image, torch.zeros((4, 256), dtype=torch.float16, device=dev), ids)
+
+
+@pytest.mark.parametrize("T", [1, 3, 7])
+def test_layer_call_phases_of_different_widths(dev, odict, T):
+    """d_model 512, d_ff 2048: the up phase is cut into more workgroup slices
+    than the down phase, so workgroups past the down phase's count skip it.
+    Both outputs against two single-projection calls and the oracle."""
+    from sub_bit_moe_amd import api
+    E, d, f = 3, 512, 2048
+    words = odict["words"]
+    tag = api.dict_tag(words)
+    ups = P.host_experts(E, f, d, 0.886, 60 + T)
+    downs = P.host_experts(E, d, f, 0.886, 70 + T)
+    up = api.ExpertStack.from_host(P.encode_all(ups, words), f, d, dev, dict_tag=tag)
+    down = api.ExpertStack.from_host(P.encode_all(downs, words), d, f, dev, dict_tag=tag)
+    image = api.device_image(words, dev)
+    rng = np.random.default_rng(T)
+    x = synth.activations(rng, T, d)
+    ids_h = rng.integers(0, E, T).astype(np.int32)
+    xt, ids = torch.from_numpy(x).to(dev), torch.from_numpy(ids_h).to(dev)
+    print(f"layer call phases T={T}", flush=True)
+    ws = api.alloc_ffn_workspace(E, T, dev)
+    y, h = api.moe_fused_ffn(up, down, image, xt, ids, workspace=ws, out_f32=True)
+    torch.cuda.synchronize()
+    assert api.workspace_error(ws) == 0
+    h2 = api.moe_fused_decode_matvec(up, image, xt, ids, relu=True)
+    y2 = api.moe_fused_decode_matvec(down, image, h2, ids, out_f32=True)
+    torch.cuda.synchronize()
+    hn, yn = h.float().cpu().numpy(), y.cpu().numpy().astype(np.float64)
+    P.assert_close(hn, h2.float().cpu().numpy(), what="h vs two calls")
+    P.assert_close(yn, y2.cpu().numpy().astype(np.float64), what="y vs two calls")
+    for t in range(T):
+        e = int(ids_h[t])
+        P.assert_close(hn[t], np.maximum(P.oracle_matvec_from_symbols(*ups[e], x[t:t + 1])[0], 0), what=f"h {t}")
+        P.assert_close(yn[t], P.oracle_matvec_from_symbols(*downs[e], hn[t:t + 1].astype(np.float16))[0],
+                       what=f"y {t}")
