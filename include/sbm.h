@@ -28,7 +28,8 @@
  *     bstart  uint32  ceil(n_codes/SBM_BLOCK) entries: the linear symbol
  *                     position row*cols+col where codeword b*SBM_BLOCK starts
  *     scales  fp16    one per row (stored as uint16 bit patterns)
- *   Operator contract ([M8.5] 0x08A/0x08B): input fp16; decoded operand
+ *   Operator contract ([M8.5] 0x08A/0x08B): input fp16 (bf16 with
+ *   SBM_F_IN_BF16); decoded operand
  *   ternary; fp32 accumulation; scale applied in fp32 in the epilogue; output
  *   fp16 or fp32.
  *
@@ -98,6 +99,12 @@ typedef enum {
                              summation order open.  Costs LDS (8-byte accumulators: shorter row
                              chunks) and a few conversions per block.  Activations must be finite.
                              Not with SBM_F_MFMA; not a flag of the layer call. */
+#define SBM_F_IN_BF16 128u  /* x holds bf16 activations (the page's kernel reads bf16 x) instead of
+                             fp16.  They are converted to fp16 as they are staged in LDS, which is
+                             exact for magnitudes from 2^-14 to 65504 (smaller ones round to fp16
+                             subnormals); |x| must stay below 65504.  With SBM_F_IN_RMS the RMS is
+                             taken of the converted values.  Not with SBM_F_MFMA.  In the layer call
+                             it applies to x (h stays fp16). */
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* sbm_last_error(void);
@@ -246,7 +253,7 @@ size_t sbm_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  *   experts:    device sbm_matrix_desc[n_experts] (dict_tag = the image's dictionary)
  *   dict_image: device copy of sbm_dict_image() output (sbm_dict_image4() with SBM_F_IMAGE4);
  *               an image of the other kind, or a damaged one, sets the workspace error word
- *   x:          device fp16 [n_tokens x cols];  expert_ids: device int32 [n_tokens]
+ *   x:          device fp16 (bf16 with SBM_F_IN_BF16) [n_tokens x cols];  expert_ids: device int32 [n_tokens]
  *   y:          device [n_tokens x rows], fp16 (or fp32 with SBM_F_OUT_F32)
  *   workspace:  device, at least sbm_workspace_bytes(n_experts, n_tokens)
  * n_tokens may be 0 (nothing is launched).  cols must be even, 2..65536;
@@ -287,10 +294,12 @@ size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  * takes one launch instead of two.  up, down: host structs of device arrays
  * with the same experts; up->rows == down->cols; both cols even and >= 512
  * (narrower rows: two sbm_moe_fused_decode_matvec calls).  x: device fp16
- * [n_tokens x up->cols]; h: device fp16 [n_tokens x up->rows] (written);
+ * (bf16 with SBM_F_IN_BF16) [n_tokens x up->cols]; h: device fp16
+ * [n_tokens x up->rows] (written);
  * y: device [n_tokens x down->rows], fp16 or fp32 (SBM_F_OUT_F32); x, h and y
  * must not overlap (workgroups still reading x run beside others writing y).  flags:
- * SBM_F_IN_RMS, SBM_F_OUT_F32 only (symmetric grid, 3-slot image).
+ * SBM_F_IN_RMS, SBM_F_OUT_F32, SBM_F_IN_BF16 only (symmetric grid, 3-slot
+ * image).
  * workspace: device, 16-byte aligned, sbm_ffn_workspace_bytes(n_experts,
  * n_tokens) bytes, ZEROED by the caller before its first use with a call;
  * every call leaves it ready for the next (calls sharing a workspace must not

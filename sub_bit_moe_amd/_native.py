@@ -18,6 +18,7 @@ SBM_F_MFMA = 8
 SBM_F_MINMAX = 16
 SBM_F_IMAGE4 = 32
 SBM_F_DETERMINISTIC = 64
+SBM_F_IN_BF16 = 128
 
 STATUS = {0: "SBM_OK", -1: "SBM_EINVAL", -2: "SBM_EODD_WIDTH", -3: "SBM_ECORRUPT",
           -4: "SBM_EDICT", -5: "SBM_ERANGE", -6: "SBM_ENOSPACE", -7: "SBM_EHIP"}

@@ -257,6 +257,16 @@ def alloc_workspace(n_experts: int, n_tokens: int, device="cuda"):
     return torch.empty(max(workspace_bytes(n_experts, n_tokens), 16), dtype=torch.uint8, device=device)
 
 
+def _x_flag(x) -> int:
+    """Activation dtype flag: fp16 (none) or bf16 (SBM_F_IN_BF16)."""
+    import torch
+    if x is None or x.dtype == torch.float16:
+        return 0
+    if x.dtype == torch.bfloat16:
+        return N.SBM_F_IN_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, not {x.dtype}")
+
+
 def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bool = False,
                             out_f32: bool = False, workspace=None, y=None, stream=None, in_rms: bool = False,
                             mfma: bool = False, minmax: bool = False, image4=None,
@@ -278,6 +288,7 @@ def moe_fused_decode_matvec(stack: ExpertStack, image_t, x, expert_ids, relu: bo
     flags |= N.SBM_F_MFMA if mfma else 0
     flags |= N.SBM_F_MINMAX if minmax else 0
     flags |= N.SBM_F_DETERMINISTIC if deterministic else 0
+    flags |= _x_flag(x)
     n4 = int(lib().sbm_dict_image4_bytes())
     if image4 is None:
         image4 = int(image_t.numel()) == n4
@@ -322,7 +333,7 @@ def moe_fused_ffn(up: ExpertStack, down: ExpertStack, image_t, x, expert_ids, h=
         y = torch.empty((T, down.rows), dtype=torch.float32 if out_f32 else torch.float16, device=dev)
     if workspace is None:
         workspace = alloc_ffn_workspace(up.n_experts, T, dev)
-    flags = (N.SBM_F_IN_RMS if in_rms else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0)
+    flags = (N.SBM_F_IN_RMS if in_rms else 0) | (N.SBM_F_OUT_F32 if out_f32 else 0) | _x_flag(x)
     pu, pd = _projection(up), _projection(down)
     check(lib().sbm_moe_fused_ffn(C.addressof(pu), C.addressof(pd), _ptr(image_t), _ptr(x), _ptr(expert_ids), T,
                                   _ptr(h), _ptr(y), flags, _ptr(workspace), int(workspace.numel()), _stream(stream)))

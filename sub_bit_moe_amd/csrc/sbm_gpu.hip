@@ -861,8 +861,17 @@ __device__ __forceinline__ void wait_tokens(const FusedArgs& a, const int32_t* p
   }
 }
 
+// SBM_F_IN_BF16: two bf16 activations in a dword as the same two values in
+// fp16 (exact for magnitudes in fp16's normal range, 2^-14 .. 65504; smaller
+// ones round to fp16 subnormals).  The staged triples stay fp16, so the
+// gathers and v_fma_mix accumulation are those of fp16 activations.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const _Float16 lo = (_Float16)__uint_as_float(w << 16), hi = (_Float16)__uint_as_float(w & 0xFFFF0000u);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
 // fp16 pairs of staged columns c0 .. c0+7 of TC token rows (zero past the
-// staged content or for tok < 0).
+// staged content or for tok < 0); bf16 activations are converted here.
 template <int TC, int LM = 0>
 __device__ __forceinline__ void load_x_group(const FusedArgs& a, const int32_t (&tok)[TC], int32_t c0, bool vec,
                                              bool wrap, uint32_t (&p)[TC][4]) {
@@ -882,6 +891,12 @@ __device__ __forceinline__ void load_x_group(const FusedArgs& a, const int32_t (
         p[t][m] = lo | (hi << 16);
       }
     }
+  }
+  if (a.flags & SBM_F_IN_BF16) {
+#pragma unroll
+    for (int t = 0; t < TC; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) p[t][m] = bf16x2_to_f16x2(p[t][m]);
   }
 }
 
@@ -951,8 +966,14 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
 }
 
 template <int TC>
-__device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* smem, const XPre& r) {
+__device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* smem, XPre& r) {
   const int32_t n8 = a.xcols / 8;
+  if (a.flags & SBM_F_IN_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r.v[j] = make_uint4(bf16x2_to_f16x2(r.v[j].x), bf16x2_to_f16x2(r.v[j].y), bf16x2_to_f16x2(r.v[j].z),
+                          bf16x2_to_f16x2(r.v[j].w));
+  }
   float inv[TC];
   const bool rms = (a.flags & SBM_F_IN_RMS) != 0;
   if (rms) {
@@ -2163,8 +2184,10 @@ static int fused_call(const uint16_t* codes, const uint32_t* row_off, const uint
   if ((uint64_t)rows * (uint64_t)cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
     return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
   if (flags & ~(SBM_F_RELU | SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_MFMA | SBM_F_MINMAX | SBM_F_IMAGE4 |
-                SBM_F_DETERMINISTIC))
+                SBM_F_DETERMINISTIC | SBM_F_IN_BF16))
     return fail(SBM_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & SBM_F_IN_BF16) && (flags & SBM_F_MFMA))
+    return fail(SBM_EINVAL, "SBM_F_IN_BF16 and SBM_F_MFMA cannot be combined");
   if ((flags & SBM_F_DETERMINISTIC) && (flags & SBM_F_MFMA))
     return fail(SBM_EINVAL, "SBM_F_DETERMINISTIC and SBM_F_MFMA cannot be combined");
   if ((flags & SBM_F_MINMAX) && (flags & SBM_F_MFMA))
@@ -2288,7 +2311,8 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
   }
   if (up->rows != down->cols)
     return fail(SBM_EINVAL, "up rows (%d) must equal down cols (%d): h is their common width", up->rows, down->cols);
-  if (flags & ~(SBM_F_OUT_F32 | SBM_F_IN_RMS)) return fail(SBM_EINVAL, "unknown or unsupported flags 0x%x", flags);
+  if (flags & ~(SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_IN_BF16))
+    return fail(SBM_EINVAL, "unknown or unsupported flags 0x%x", flags);
   if ((uint64_t)n_tokens * (uint64_t)down->cols * 2u >= (1ull << 31)) return fail(SBM_ERANGE, "h too large");
   if (n_tokens == 0) return SBM_OK;
   for (const sbm_projection* p : {up, down})
@@ -2318,7 +2342,8 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
   unsigned char* wsd = wsu + align16(sbm_workspace_bytes(up->n_experts, n_tokens));
   FusedArgs ua, da;
   fill_args(ua, up->codes, up->row_off, up->bstart, up->scales, up->experts, up->n_experts, up->rows, up->cols,
-            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & SBM_F_IN_RMS), wsu, pu, grid_u);
+            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & (SBM_F_IN_RMS | SBM_F_IN_BF16)), wsu, pu,
+            grid_u);
   fill_args(da, down->codes, down->row_off, down->bstart, down->scales, down->experts, down->n_experts, down->rows,
             down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, wsd, pd, grid_d);
   ua.tok_done = da.tok_done = sync + kSyncHdr;

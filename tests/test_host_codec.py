@@ -273,8 +273,10 @@ def test_fused_argument_errors_without_gpu():
     z = None
     # odd width, bad flags, bad shape are rejected before any device call
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 7, z, z, z, 1, z, 0, z, 0, z) == -2
-    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 128, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 256, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 64 | 8, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 128 | 8, z, 0, z) == -1
+    assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 128, z, 0, z) == -1   # null pointers
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 64, z, 0, z) == -1   # null pointers
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 16 | 8, z, 0, z) == -1
     assert L.sbm_moe_fused_decode_matvec(z, z, z, z, z, 1, 4, 8, z, z, z, 1, z, 32 | 8, z, 0, z) == -1
