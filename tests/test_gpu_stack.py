@@ -283,3 +283,33 @@ def test_full_bench_stack_sampled(dev):
         prev_y = y
     del st, run, keep
     torch.cuda.empty_cache()
+
+
+def test_full_bench_stack_deterministic(dev):
+    """The benchmark workload with fixed-point row accumulators: two passes
+    return the same bits at every layer, and sampled rows of every layer
+    match the oracle on the GPU's own inputs."""
+    from oracle import matvec as OMv
+    from sub_bit_moe_amd import stack as S
+    torch.cuda.empty_cache()
+    cfg = S.StackConfig()
+    st = S.build(cfg, dev)
+    run = S.Runner(st, deterministic=True)
+    keep, keep2 = {}, {}
+    run.run(keep)
+    run.run(keep2)
+    torch.cuda.synchronize()
+    assert api_error(run.ws_up) == 0 and api_error(run.ws_down) == 0
+    for l in range(cfg.n_layers):
+        for a, b in zip(keep[l], keep2[l]):
+            assert torch.equal(a, b), f"layer {l}: two deterministic passes differ"
+    rng = np.random.default_rng(43)
+    prev_y = None
+    for l in range(cfg.n_layers):
+        xraw, h, y = (t.float().cpu().numpy() for t in keep[l])
+        xin = xraw if l == 0 else OMv.rms_glue(prev_y).astype(np.float64)
+        ids = st.routes_host[l]
+        _check_sampled(cfg, l, xin, h, y, ids, _sample_experts(ids, 1, rng), 2, 16, rng)
+        prev_y = y
+    del st, run, keep, keep2
+    torch.cuda.empty_cache()
