@@ -69,3 +69,29 @@ def test_noalloc_matches_workspace_entry(dev, odict):
     z = C.c_void_p(0)
     st = N.lib().sbm_moe_fused_decode_matvec_noalloc(z, z, z, z, z, big_e, rows, cols, z, z, z, 64, z, 0, z, z)
     assert st == -5 and b"allocation-free" in N.lib().sbm_last_error()
+
+
+def test_noalloc_deterministic_bf16(dev, odict):
+    """The allocation-free call with fixed-point accumulators and bf16
+    activations returns the workspace entry point's bits, twice in a row
+    (the second call smaller)."""
+    from sub_bit_moe_amd import _native as N
+    from sub_bit_moe_amd import api
+    words = odict["words"]
+    image_t = api.device_image(words, dev)
+    E, rows, cols = 12, 300, 2080
+    ex = P.host_experts(E, rows, cols, 0.886, 91)
+    stack = api.ExpertStack.from_host(P.encode_all(ex, words), rows, cols, dev, dict_tag=api.dict_tag(words))
+    flags = N.SBM_F_OUT_F32 | N.SBM_F_DETERMINISTIC | N.SBM_F_IN_BF16
+    for T, seed in ((150, 92), (9, 93)):
+        print(f"noalloc deterministic bf16: T={T}", flush=True)
+        rng = np.random.default_rng(seed)
+        x = torch.from_numpy(rng.standard_normal((T, cols)).astype(np.float32)).to(torch.bfloat16).to(dev)
+        ids = torch.from_numpy(rng.integers(0, E, T).astype(np.int32)).to(dev)
+        y0 = api.moe_fused_decode_matvec(stack, image_t, x, ids, out_f32=True, deterministic=True)
+        y1 = torch.full((T, rows), float("nan"), dtype=torch.float32, device=dev)
+        err = torch.full((1,), -1, dtype=torch.int32, device=dev)
+        assert _noalloc(stack, image_t, x, ids, y1, err, flags) == 0
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(y0, y1)
