@@ -51,6 +51,27 @@ def measured_traffic():
     return None, None
 
 
+def measured_lds():
+    """LDS and VALU occupancy of the fused kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    import glob
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "sub_bit_moe_amd", "csrc", "sbm_gpu.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "fused_kernel_lds_*.md"))):
+        text = open(f).read()
+        if f"sha256[:16] = {sha}" not in text:
+            continue
+        m = re.search(r"([\d.]+) LDS-busy cycles per LDS instruction, (\d+)% of them bank-conflict cycles", text)
+        b = re.search(r"LDS busy (\d+)% and VALU (\d+)% of the whole launch", text)
+        if m and b:
+            return {"lds_busy_cycles_per_instr": float(m.group(1)), "bank_conflict_frac": int(m.group(2)) / 100,
+                    "lds_busy_frac_of_launch": int(b.group(1)) / 100, "valu_busy_frac_of_launch": int(b.group(2)) / 100,
+                    "source": os.path.basename(f)}
+    return None
+
+
 def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
     """The oracle (pure Python/numpy, fp64) decoding and multiplying a bounded
     sample of the same workload: the first n_mats touched matrices of layer 0,
@@ -687,7 +708,9 @@ def main():
                 "traffic_source": traffic_src,
                 "kernel": "sbm::fused_kernel (token grouping inside; 2 launches per layer)",
                 "avg_launch_us": round(launch_us, 2),
-                "bytes_per_launch": int(bytes_per_launch)}
+                "bytes_per_launch": int(bytes_per_launch),
+                "binding_unit": "LDS gathers (64 random per 1024 codewords), not HBM",
+                "lds_counters": measured_lds()}
     minmax = None
     if not args.no_minmax:
         log("pass on the per-row (w_min, w_max) grid ...")
