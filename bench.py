@@ -595,8 +595,28 @@ def c3_pair(n_pairs: int = 480, n_calls: int = 200):
         res["sparse_compressed_GBps"] = round(pair_bytes / res["sparse_two_launches_us"] / 1e3, 1)
         out[f"T{T}"] = res
         log(f"  C3 T={T}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
+    # beyond the config's batch sizes: where decompress-then-GEMM overtakes the sparse path
+    for T in (128, 512):
+        x = torch.from_numpy(synth.activations(np.random.default_rng(T), T, cfg.d_model)).to(dev)
+        order = [(i * 7) % n_pairs for i in range(n_calls)]
+        ids = [torch.full((T,), e, dtype=torch.int32, device=dev) for e in order]
+        h = torch.empty(T, cfg.d_ff, dtype=torch.float16, device=dev)
+        y = torch.empty(T, cfg.d_model, dtype=torch.float16, device=dev)
+        wsu, wsd = api.alloc_workspace(n_pairs, T, dev), api.alloc_workspace(n_pairs, T, dev)
+
+        def two_big(i):
+            api.moe_fused_decode_matvec(up, st.image, x, ids[i], relu=True, workspace=wsu, y=h)
+            api.moe_fused_decode_matvec(down, st.image, h, ids[i], workspace=wsd, y=y)
+
+        res = {"sparse_two_launches_us": _graph_time_us(two_big, n_calls // 4),
+               "decompress_gemm_us": _graph_time_us(
+                   lambda i: hybrid.expert_ffn(up, down, order[i], st.image, x, wu=wu, wd=wd), n_calls // 4)}
+        res = {k: round(v, 2) for k, v in res.items()}
+        out[f"T{T}"] = res
+        log(f"  C3 T={T}: " + ", ".join(f"{k} {v}" for k, v in res.items()))
     out["note"] = ("the dense-tile MFMA instance handles experts with 16 or more tokens; at T = 1 and 8 it runs "
-                   "the sparse path inside its own instance")
+                   "the sparse path inside its own instance; T = 128 and 512 go beyond the config's batch sizes "
+                   "(sparse against decompress-then-GEMM only)")
     del st
     torch.cuda.synchronize()
     return out

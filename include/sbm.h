@@ -221,7 +221,9 @@ int sbm_encode_experts(int32_t n_mats, const uint8_t* const* sym, int32_t rows, 
  * dict_tag (the matrix descriptor's dictionary tag) differs from the low 32
  * bits of the image's dictionary checksum (nothing is written either).
  * rows * cols < 2^32, cols even.  One wave per 1024-codeword block: coalesced
- * zero-fill of the block's element span, then a store per nonzero. */
+ * zero-fill of the block's element span (16-byte stores where out is 16-byte
+ * aligned), the block's codewords (16-byte loads when codes is 16-byte
+ * aligned) looked up in the image's table, then a store per nonzero. */
 int sbm_decode_dense(const uint16_t* codes, uint64_t n_codes, const uint32_t* bstart, int32_t rows,
                      int32_t cols, const void* dict_image, uint32_t dict_tag, uint16_t* out_fp16, uint32_t* bad,
                      void* stream);

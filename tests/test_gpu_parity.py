@@ -660,6 +660,30 @@ def test_decode_dense_bit_exact(dev, lib_state, odict):
     assert int(bad.item()) == 1 and bool((out == 7.0).all())
 
 
+def test_decode_dense_unaligned_output(dev, lib_state, odict):
+    """sbm_decode_dense into outputs that start 4, 8 or 12 bytes past a
+    16-byte boundary: every element right, nothing written outside the
+    matrix (the zero fill uses 16-byte stores on the aligned part only)."""
+    from sub_bit_moe_amd import synth
+    api = lib_state["api"]
+    rng = np.random.default_rng(37)
+    to_f16 = np.array([0.0, -1.0, 1.0], np.float16)
+    for rows, cols in ((37, 30), (129, 2080), (3, 2)):
+        syms = [synth.ternary_symbols(rng, rows, cols, 0.886)]
+        st = api.ExpertStack.from_symbols(syms, [synth.row_scales(rng, rows)], odict["words"], dev)
+        for off in (2, 4, 6):
+            print(f"decode_dense {rows}x{cols} output offset {2 * off} bytes", flush=True)
+            buf = torch.full((rows * cols + 16,), 7.0, dtype=torch.float16, device=dev)
+            out = buf[off:off + rows * cols].view(rows, cols)
+            _, bad = api.decode_dense(st, 0, lib_state["image_t"], out=out)
+            torch.cuda.synchronize()
+            assert int(bad.item()) == 0
+            b = buf.cpu().numpy()
+            assert np.all(b[:off] == 7.0) and np.all(b[off + rows * cols:] == 7.0)
+            assert np.array_equal(b[off:off + rows * cols].view(np.uint16),
+                                  to_f16[syms[0]].reshape(-1).view(np.uint16))
+
+
 @pytest.mark.parametrize("T", [5, 90, 150])
 def test_fused_dictionary_mismatch_is_flagged(dev, lib_state, odict_for, T):
     """[M8.5] 0x08B: codes are only meaningful with the dictionary they were
