@@ -313,6 +313,40 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
                       const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens, uint16_t* h, void* y,
                       uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of sbm_moe_fused_layers. */
+size_t sbm_layers_workspace_bytes(int32_t n_layers, int32_t n_experts, int32_t n_tokens);
+
+/* [QMoE] "The GPU Decoding Kernel" for n_layers MoE layers in one launch: for
+ * l = 0 .. n_layers-1 and every token t with e = expert_ids[l * n_tokens + t],
+ *   x_0 = x,  x_l = y_{l-1} / rms(y_{l-1}) per token for l >= 1
+ *   h[t, :]   = relu( W_up_{l,e} x_l[t, :] )
+ *   y_l[t, :] = W_down_{l,e} h[t, :]
+ * as sbm_moe_fused_ffn computes each layer (the RMS scaling between layers is
+ * the one SBM_F_IN_RMS applies; with the flag, layer 0's input is scaled too).
+ * Every layer's routing is an input.  A workgroup prepares each projection
+ * (token grouping, chunk table, first code blocks) while the previous one is
+ * still finishing elsewhere, and starts a token's rows as soon as that
+ * token's input rows are all written.  up, down: arrays of n_layers host
+ * structs (1 <= n_layers <= 32; longer stacks: one call per 32 layers), all
+ * layers of layer 0's shapes, up->rows == down->cols and down->rows ==
+ * up->cols when n_layers > 1, cols even and >= 512.  expert_ids: device int32
+ * [n_layers x n_tokens].  x: device fp16 (bf16 with SBM_F_IN_BF16, layer 0
+ * only) [n_tokens x up->cols]; h: device fp16 [n_layers x n_tokens x
+ * up->rows] (written: every layer's h); y: device fp16 [n_layers x n_tokens x
+ * down->rows] (written: every layer's output, the last layer's last).  x, h
+ * and y must not overlap.  flags: SBM_F_IN_RMS, SBM_F_IN_BF16 (SBM_F_OUT_F32 with
+ * n_layers = 1 only).  workspace: device, 16-byte aligned,
+ * sbm_layers_workspace_bytes(n_layers, n_experts, n_tokens) bytes, ZEROED by
+ * the caller before its first use with a call; every call leaves it ready for
+ * the next (calls sharing a workspace must not overlap).  Its first word is
+ * the call's error word as for sbm_moe_fused_ffn (invalid ids counted once
+ * per layer; bit 28: a projection gave up waiting for its input rows).  With
+ * n_layers = 1 this is sbm_moe_fused_ffn. */
+int sbm_moe_fused_layers(const sbm_projection* up, const sbm_projection* down, int32_t n_layers,
+                         const void* dict_image, const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens,
+                         uint16_t* h, uint16_t* y, uint32_t flags, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * fused call with no workspace argument.  The kernels use a static device

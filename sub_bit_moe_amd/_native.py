@@ -66,6 +66,8 @@ _SIGS = {
                                                       P, P, C.c_int32, P, C.c_uint32, P, P]),
     "sbm_ffn_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32]),
     "sbm_moe_fused_ffn": (C.c_int, [P, P, P, P, P, C.c_int32, P, P, C.c_uint32, P, C.c_size_t, P]),
+    "sbm_layers_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int32, C.c_int32]),
+    "sbm_moe_fused_layers": (C.c_int, [P, P, C.c_int32, P, P, P, C.c_int32, P, P, C.c_uint32, P, C.c_size_t, P]),
     "sbm_stream_read": (C.c_int, [P, C.c_uint64, P, C.c_uint32, P]),
     "sbm_workspace_error": (C.c_int, [P, P, P]),
     "sbm_rms_glue": (C.c_int, [P, C.c_int32, C.c_int32, P, P]),

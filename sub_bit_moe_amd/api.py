@@ -340,6 +340,45 @@ def moe_fused_ffn(up: ExpertStack, down: ExpertStack, image_t, x, expert_ids, h=
     return y, h
 
 
+def layers_workspace_bytes(n_layers: int, n_experts: int, n_tokens: int) -> int:
+    return int(lib().sbm_layers_workspace_bytes(n_layers, n_experts, n_tokens))
+
+
+def alloc_layers_workspace(n_layers: int, n_experts: int, n_tokens: int, device="cuda"):
+    """Zeroed workspace of the multi-layer call (it must start zeroed; every
+    call leaves it ready for the next)."""
+    import torch
+    return torch.zeros(max(layers_workspace_bytes(n_layers, n_experts, n_tokens), 64), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_fused_layers(ups, downs, image_t, x, expert_ids, h=None, y=None, workspace=None, in_rms: bool = False,
+                     stream=None):
+    """len(ups) MoE layers in one launch (sbm_moe_fused_layers): per layer l,
+    h_l = relu(W_up x_l), y_l = W_down h_l with x_0 = x and x_l = y_{l-1}
+    scaled to unit RMS per token; expert_ids: int32 [n_layers, T].  Returns
+    (y, h): every layer's outputs, fp16 [n_layers, T, width]."""
+    import torch
+    L = len(ups)
+    assert L == len(downs) and L >= 1
+    T = int(x.shape[0])
+    dev = ups[0].codes.device
+    if h is None:
+        h = torch.empty((L, T, ups[0].rows), dtype=torch.float16, device=dev)
+    if y is None:
+        y = torch.empty((L, T, downs[0].rows), dtype=torch.float16, device=dev)
+    assert h.numel() >= L * T * ups[0].rows and y.numel() >= L * T * downs[0].rows
+    if workspace is None:
+        workspace = alloc_layers_workspace(L, ups[0].n_experts, T, dev)
+    flags = (N.SBM_F_IN_RMS if in_rms else 0) | _x_flag(x)
+    pu = (N.Projection * L)(*[_projection(u) for u in ups])
+    pd = (N.Projection * L)(*[_projection(d) for d in downs])
+    check(lib().sbm_moe_fused_layers(C.addressof(pu), C.addressof(pd), L, _ptr(image_t), _ptr(x), _ptr(expert_ids),
+                                     T, _ptr(h), _ptr(y), flags, _ptr(workspace), int(workspace.numel()),
+                                     _stream(stream)))
+    return y, h
+
+
 def workspace_error(workspace, stream=None) -> int:
     v = C.c_uint32()
     check(lib().sbm_workspace_error(_ptr(workspace), C.addressof(v), _stream(stream)))

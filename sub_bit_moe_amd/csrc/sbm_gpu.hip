@@ -37,6 +37,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstddef>
+#include <cstring>
 #include <mutex>
 
 #include "sbm_internal.h"
@@ -138,23 +139,45 @@ struct FusedArgs {
   int32_t mfma_rows;    // rows per dense MFMA tile (16, 32 or 64); 0: heavy experts stay sparse
   int32_t det_shift;    // SBM_F_DETERMINISTIC: accumulator terms are rounded to multiples of 2^-det_shift
   uint32_t* err_out;    // if set, workgroup 0 copies the finished error word here
-  // layer calls (up, ReLU, down in one launch): per-token counts of up rows
-  // written, the count a token needs before its down rows start, and the
-  // bytes of x (the down phase reads h through a range-checked resource)
+  // layer calls (several projections in one launch): lm bit 0, this phase's
+  // output rows are written coherently at device scope and counted per token
+  // in tok_done; bit 1, its input rows were written by the previous phase of
+  // the same launch and are waited for (tok_wait reaching tok_expect) and
+  // read coherently through a range-checked resource of x_bytes
+  uint32_t lm;
   uint32_t* tok_done;
+  const uint32_t* tok_wait;
   uint32_t tok_expect;
   uint32_t x_bytes;
   uint32_t* sync_err;   // the layer call's error accumulator (device-scope atomics only)
 };
 
-// Layer mode of the staging and epilogue code: 0 a single projection; 1 the
-// up phase of a layer call (h stored coherently at device scope, per-token
-// row counts raised after each chunk); 2 its down phase (a token's rows of h
-// are waited for, then read coherently at device scope).
+// Layer mode of the staging and epilogue code (template LM): 0 a single
+// projection, no coherence; 3 a phase of a layer call, with the bits of a.lm
+// deciding at run time whether its outputs are published (bit 0: stored
+// coherently at device scope, per-token row counts raised after each chunk)
+// and whether its inputs are waited for and read coherently (bit 1).
 constexpr int kCpolSc1 = 16;                     // buffer-load cache policy: device-scope coherent
+template <int LM>
+__device__ __forceinline__ bool lm_out(const FusedArgs& a) {
+  if constexpr (LM == 3) return (a.lm & 1u) != 0;
+  else return false;
+}
+template <int LM>
+__device__ __forceinline__ bool lm_in(const FusedArgs& a) {
+  if constexpr (LM == 3) return (a.lm & 2u) != 0;
+  else return false;
+}
 
 constexpr uint64_t kLayerWaitTicks = 2000000;    // 20 ms of the 100 MHz real-time counter
 
+// Thread index through a volatile move: values derived from it are computed
+// where they are used instead of being hoisted out of the phase loop.
+__device__ __forceinline__ uint32_t tid_v() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"((uint32_t)threadIdx.x));
+  return r;
+}
 // ------------------------------------------------------------ wave helpers
 // Inclusive scan over the 64 lanes of a wave (DPP row shifts, then the row
 // broadcasts of lane 15 and lane 31).
@@ -665,7 +688,7 @@ template <bool DET>
 __device__ __forceinline__ void racc_clear(const FusedArgs& a, unsigned char* smem) {
   const uint32_t n4 = ((uint32_t)a.tcmax * (uint32_t)(a.rmax + 2) * acc_bytes<DET>() + 15u) / 16u;   // 16B-aligned
   uint4* r = (uint4*)(smem + a.lds_racc);
-  for (uint32_t i = threadIdx.x; i < n4; i += kFThreads) r[i] = make_uint4(0, 0, 0, 0);
+  for (uint32_t i = tid_v(); i < n4; i += kFThreads) r[i] = make_uint4(0, 0, 0, 0);
 }
 
 // Multiply-accumulate of one decoded block into the row accumulators.
@@ -816,11 +839,11 @@ __device__ __forceinline__ int32_t x_src(const FusedArgs& a, int32_t c, bool wra
   return (wrap && c >= a.cols) ? c - a.cols : c;
 }
 
-// Activation loads: plain, or (LM 2: h written by other workgroups of the
+// Activation loads: plain, or (inputs written by other workgroups of the
 // same launch) device-scope coherent through a range-checked resource.
 template <int LM>
 __device__ __forceinline__ uint4 ld_x16(const FusedArgs& a, int64_t idx) {
-  if constexpr (LM == 2) {
+  if (lm_in<LM>(a)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufferFlags);
     const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)idx * 2u, 0, kCpolSc1);
     return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
@@ -830,7 +853,7 @@ __device__ __forceinline__ uint4 ld_x16(const FusedArgs& a, int64_t idx) {
 }
 template <int LM>
 __device__ __forceinline__ uint32_t ld_x2(const FusedArgs& a, int64_t idx) {
-  if constexpr (LM == 2) {
+  if (lm_in<LM>(a)) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)a.x_bytes, kBufferFlags);
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)idx * 2u, 0, kCpolSc1);
   } else {
@@ -838,16 +861,16 @@ __device__ __forceinline__ uint32_t ld_x2(const FusedArgs& a, int64_t idx) {
   }
 }
 
-// LM 2: wait until the up phase has written all rows of h for tokens
-// perm[tb .. tb+nt) (each wave polls the nt counters; bounded by the real-time
-// counter: on expiry the layer error bit is raised and the wave goes on, so
-// the kernel always ends).  Lanes past nt and other modes return at once.
+// Inputs from the previous phase: wait until it has written all input rows of
+// tokens perm[tb .. tb+nt) (each wave polls the nt counters; bounded by the
+// real-time counter: on expiry the layer error bit is raised and the wave
+// goes on, so the kernel always ends).  Other modes return at once.
 template <int LM>
 __device__ __forceinline__ void wait_tokens(const FusedArgs& a, const int32_t* perm, uint32_t tb, uint32_t nt) {
-  if constexpr (LM == 2) {
-    const uint32_t lane = threadIdx.x & 63;
+  if (lm_in<LM>(a)) {
+    const uint32_t lane = tid_v() & 63;
     const bool mine = lane < nt;
-    const uint32_t* p = a.tok_done + (mine ? (uint32_t)perm[tb + lane] : 0u);
+    const uint32_t* p = a.tok_wait + (mine ? (uint32_t)perm[tb + lane] : 0u);
     const uint64_t t0 = wall_clock64();
     while (true) {
       const uint32_t v = mine ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.tok_expect;
@@ -918,7 +941,7 @@ __device__ __forceinline__ uint32_t h2_scale(uint32_t w, float s) {
 
 template <int TC>
 __device__ __forceinline__ void wg_inv_rms(const FusedArgs& a, const float (&ss)[TC], float (&inv)[TC]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_v() & 63, wave = tid_v() >> 6;
 #pragma unroll
   for (int t = 0; t < TC; ++t) {
     const float S = wave_incl_scan_f(ss[t]);
@@ -953,7 +976,7 @@ __device__ __forceinline__ void xpre_load(const FusedArgs& a, const int32_t* per
   const int32_t n8 = a.xcols / 8;
 #pragma unroll
   for (int j = 0; j < 4 / TC; ++j) {
-    const int32_t c0 = 8 * ((int32_t)threadIdx.x + j * kFThreads);
+    const int32_t c0 = 8 * ((int32_t)tid_v() + j * kFThreads);
     const int32_t s0 = x_src(a, c0, x_wrap(a));
 #pragma unroll
     for (int t = 0; t < TC; ++t) {
@@ -982,7 +1005,7 @@ __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* sm
     for (int t = 0; t < TC; ++t) ss[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4 / TC; ++j) {
-      if (8 * ((int32_t)threadIdx.x + j * kFThreads) < a.cols) {     // the row itself, not its wrap copy
+      if (8 * ((int32_t)tid_v() + j * kFThreads) < a.cols) {     // the row itself, not its wrap copy
 #pragma unroll
         for (int t = 0; t < TC; ++t) {
           const uint4 v = r.v[j * TC + t];
@@ -994,7 +1017,7 @@ __device__ __forceinline__ void xpre_store(const FusedArgs& a, unsigned char* sm
   }
 #pragma unroll
   for (int j = 0; j < 4 / TC; ++j) {
-    const int32_t i = (int32_t)threadIdx.x + j * kFThreads;
+    const int32_t i = (int32_t)tid_v() + j * kFThreads;
     if (i < n8) {
       uint32_t p[TC][4];
 #pragma unroll
@@ -1033,7 +1056,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
     float ss[TC];
 #pragma unroll
     for (int t = 0; t < TC; ++t) ss[t] = 0.f;
-    for (int32_t i = threadIdx.x; 8 * i < a.cols; i += kFThreads) {     // the row itself, not its wrap copy
+    for (int32_t i = tid_v(); 8 * i < a.cols; i += kFThreads) {     // the row itself, not its wrap copy
       uint32_t p[TC][4];
       load_x_group<TC, LM>(a, tok, 8 * i, vec, false, p);
 #pragma unroll
@@ -1043,7 +1066,7 @@ __device__ __forceinline__ void stage_x(const FusedArgs& a, unsigned char* smem,
     }
     wg_inv_rms<TC>(a, ss, inv);
   }
-  for (int32_t i = threadIdx.x; i < n8; i += kFThreads) {
+  for (int32_t i = tid_v(); i < n8; i += kFThreads) {
     uint32_t p[TC][4];
     load_x_group<TC, LM>(a, tok, 8 * i, vec, x_wrap(a), p);
     if (rms) {
@@ -1295,6 +1318,9 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
 constexpr int kMaxChunks = 16;
 __shared__ Chunk s_chunks[kMaxChunks];
 __shared__ uint32_t s_nchunks, s_nseq, s_next_seq;
+// Rows published per token and not yet counted (layer calls, in-LDS grouping;
+// zero between slices).
+__shared__ uint32_t s_pend[kGroupInLds];
 __shared__ uint64_t s_gnext;
 
 // Fill the chunk table from global row index g (at most kMaxChunks chunks):
@@ -1303,8 +1329,8 @@ __shared__ uint64_t s_gnext;
 // blocks of the round.
 __device__ __forceinline__ void build_chunks(const FusedArgs& a, const uint4* items, uint64_t g, uint64_t g1) {
   static_assert(kMaxChunks <= 64, "one lane per chunk");
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  if (tid_v() < 64) {
+    const int lane = tid_v();
     uint32_t q = (uint32_t)udiv_small(g + vzero(), (uint32_t)a.rows);
     int32_t ra = (int32_t)(g - (uint64_t)q * a.rows);
     uint64_t gg = g;
@@ -1456,7 +1482,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
     // slot is refilled as soon as its codes are decoded, and the loop is
     // unrolled over A and B, so no slot is copied (a copy would wait for the
     // loads still landing in it).
-    const int32_t wave = (int32_t)(threadIdx.x >> 6);
+    const int32_t wave = (int32_t)(tid_v() >> 6);
     Slot A = grab(a, nseq, nch, wave), B = grab(a, nseq, nch, wave + kFWaves);
     for (uint32_t c = 0; c < nch; ++c) {
       const Chunk ch = load_chunk(c);
@@ -1504,7 +1530,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       uint32_t sc[kEpiRegs];
 #pragma unroll
       for (int k = 0; k < kEpiRegs; ++k) {
-        const int32_t i = (int32_t)threadIdx.x + k * kFThreads;   // accumulator slot, row i - 1
+        const int32_t i = (int32_t)tid_v() + k * kFThreads;   // accumulator slot, row i - 1
         const bool live = ch.ok && i >= 1 && i <= R;
         if (a.minmax)     // (w_min, w_max) of the row, one dword
           sc[k] = live ? ((const uint32_t*)a.scales)[ch.scale_base / 2 + ch.ra + i - 1] : 0u;
@@ -1531,7 +1557,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       // accumulator slots [0, R + 1] of tokens t < tc are cleared for the next chunk
 #pragma unroll
       for (int k = 0; k < kEpiRegs; ++k) {
-        const int32_t i = (int32_t)threadIdx.x + k * kFThreads;
+        const int32_t i = (int32_t)tid_v() + k * kFThreads;
         if (i < R + 2 && a.minmax) {
           // y = w_min * S1 + w_max * S2 = ((w_max - w_min) * A + (w_max + w_min) * B) / 2
           const float wmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc[k] & 0xFFFFu));
@@ -1554,7 +1580,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
               v *= s;
               if (a.flags & SBM_F_RELU) v = v > 0.f ? v : 0.f;
               const int64_t o = (int64_t)perm[ch.tb + t] * a.rows + ch.ra + i - 1;
-              if constexpr (LM == 1) {   // h for the down phase: written through to device scope
+              if (lm_out<LM>(a)) {   // read by the next phase: written through to device scope
                 __hip_atomic_store((uint16_t*)a.y + o, __builtin_bit_cast(uint16_t, (_Float16)v), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
               } else if (a.flags & SBM_F_OUT_F32) {
@@ -1579,20 +1605,39 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         }
         cur_q = nx.q;
       }
-      if constexpr (LM == 1) wait_vmem_all();   // this thread's rows of h have reached device scope
+      // Published rows: with the in-LDS grouping their per-token counts are
+      // gathered in LDS and raised once, at the end of the slice, after a
+      // single wait for the stores (a wait per chunk would hold up the next
+      // chunk's blocks); otherwise raised here, once the chunk's rows are stored.
+      const bool pub = lm_out<LM>(a), pend = pub && a.group_in_lds;
+      if (pub && !pend) wait_vmem_all();   // this thread's output rows have reached device scope
       __syncthreads();
-      if constexpr (LM == 1) {
+      if (pub) {
         // every row of the chunk is written: raise its tokens' counts (also
         // for a refused expert, whose rows stay unwritten, so no wait hangs)
-        if (threadIdx.x < ch.nt)
-          __hip_atomic_fetch_add(a.tok_done + perm[ch.tb + threadIdx.x], (uint32_t)(ch.rb - ch.ra), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (tid_v() < ch.nt) {
+          const int32_t t = perm[ch.tb + tid_v()];
+          if (pend) s_pend[t] += (uint32_t)(ch.rb - ch.ra);     // one thread per token of the chunk
+          else __hip_atomic_fetch_add(a.tok_done + t, (uint32_t)(ch.rb - ch.ra), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     const uint64_t gn = s_gnext;
     __syncthreads();      // every wave has read the table before it is rebuilt
     if (gn >= g1) break;
     build_chunks(a, items, gn, g1);
+  }
+  if (lm_out<LM>(a) && a.group_in_lds) {
+    wait_vmem_all();      // every output row of the slice has reached device scope
+    __syncthreads();
+    for (int32_t t = tid_v(); t < a.n_tokens; t += kFThreads) {
+      const uint32_t n = s_pend[t];
+      if (n) {
+        __hip_atomic_fetch_add(a.tok_done + t, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_pend[t] = 0;
+      }
+    }
   }
 }
 
@@ -1620,7 +1665,7 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
   uint32_t* nts = sc + 4 * N;    // item size at an item's first sorted place, else 0
   uint32_t* ks = sc + 5 * N;     // key by sorted place
   const int32_t T = a.n_tokens;
-  const int tid = threadIdx.x;
+  const int tid = tid_v();
   if (tid < N) {
     uint32_t key = kNone;
     if (tid < T && my_id >= 0 && my_id < a.n_experts) key = ((uint32_t)my_id << 8) | (uint32_t)tid;
@@ -1718,11 +1763,11 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
   if (blockIdx.x == 0) {
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
-    for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
+    for (uint32_t q = tid_v(); q < n_items; q += kFThreads)
       if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, image_tag(a)))
         atomicOr(&s_ghdr[3], err);
     __syncthreads();
-    if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
+    if (tid_v() == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
   }
 }
 
@@ -1737,8 +1782,8 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
 __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int32_t my_id) {
   constexpr uint32_t kNone = 0x7FFFFFFFu;   // above every valid key (< 2^30)
   const int32_t T = a.n_tokens;
-  if (threadIdx.x < 64) {
-    const uint32_t lane = threadIdx.x;
+  if (tid_v() < 64) {
+    const uint32_t lane = tid_v();
     const bool valid = (int32_t)lane < T && my_id >= 0 && my_id < a.n_experts;
     const uint32_t key = valid ? (((uint32_t)my_id << 6) | lane) : kNone;
     uint32_t* ks = sc + 64;                 // keys by lane, then by sorted place
@@ -1817,11 +1862,11 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
   if (blockIdx.x == 0) {
     // descriptors of the touched experts; workgroup 0 alone writes the error word
     const uint32_t n_items = s_ghdr[0];
-    for (uint32_t q = threadIdx.x; q < n_items; q += kFThreads)
+    for (uint32_t q = tid_v(); q < n_items; q += kFThreads)
       if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, image_tag(a)))
         atomicOr(&s_ghdr[3], err);
     __syncthreads();
-    if (threadIdx.x == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
+    if (tid_v() == 0) a.ws[0] = (((uint32_t)T - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
   }
 }
 
@@ -1896,40 +1941,98 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
 }
 
 // ------------------------------------------------------------ layer calls
-// Up projection, ReLU and down projection of the same routed tokens in one
-// launch ([QMoE] "The GPU Decoding Kernel": the experts are FFNs whose two
-// matrices are multiplied in turn; doing both here saves the second launch,
-// its prologue and the first phase's tail).  Every workgroup runs its up
-// slice, then its down slice; the down phase stages a token's h only once all
-// up rows of that token are written (per-token counts raised by the up
-// chunks, h written and read coherently at device scope, so no cache-wide
-// writeback or invalidation is needed).  All workgroups are resident (one
-// per CU, at most the CU count), and every wait is bounded.
+// Several projections in one launch ([QMoE] "The GPU Decoding Kernel": the
+// experts are FFNs whose two matrices are multiplied in turn, layer after
+// layer).  Phase p is layer p / 2's up projection (ReLU) when p is even, its
+// down projection when p is odd; a layer's up phase reads the previous
+// layer's output scaled to unit RMS per token (the glue between layers).
+// Every workgroup runs its slice of each phase in turn.  A phase's tokens are
+// grouped, its chunk table is built and its first code blocks are requested
+// as soon as the workgroup has finished the previous phase; only the staging
+// of a token's activations waits, until every input row of that token is
+// written (per-token counts raised by the previous phase's chunks, rows
+// written and read coherently at device scope, so no cache-wide writeback or
+// invalidation is needed).  A workgroup's next slice covers about the same
+// experts as its last one, so it mostly waits for its neighbours, not for the
+// slowest workgroup of the launch.  All workgroups are resident (one per CU,
+// at most the CU count), and every wait is bounded.
 // Sync area at the start of the layer workspace (uint32 words): [0] the
 // finished call's error word, [1] the running error word, [2] workgroups
-// done, [16 ..) one count per token.  The last workgroup to finish publishes
-// the error word and clears the rest, so a call leaves the area ready for
-// the next one (the caller zeroes it once, before the first call).
+// done, [16 ..) one count per token and phase (all phases but the last).
+// The last workgroup to finish publishes the error word and clears the rest,
+// so a call leaves the area ready for the next one (the caller zeroes it
+// once, before the first call).
 constexpr uint32_t kSyncHdr = 16;
+constexpr int kMaxLayers = 32;
+struct LayerProj {
+  const uint16_t* codes;
+  const uint32_t* row_off;
+  const uint32_t* bstart;
+  const uint16_t* scales;
+  const sbm_matrix_desc* experts;
+};
+struct LayerTab {
+  LayerProj up[kMaxLayers], dn[kMaxLayers];
+  uint16_t* h;            // [n_layers][T][up rows]: every layer's h
+  uint16_t* y;            // [n_layers][T][down rows]: every layer's output (the input of the next)
+  uint32_t ws_words;      // words of workspace per phase (grouping state)
+  int32_t n_layers;
+};
+static_assert(2 * sizeof(FusedArgs) + sizeof(LayerTab) + sizeof(void*) <= 4096, "kernel arguments within 4 KB");
 __shared__ uint32_t s_last;
 
-// One phase of a layer call: LM 1 the up projection, LM 2 the down projection.
-template <int LM>
-__device__ __forceinline__ void ffn_phase(const FusedArgs& a, unsigned char* smem, int32_t my_id, bool image_ok,
-                                          uint32_t split7, uint32_t* sync) {
+// Arguments of phase p from the up and down templates (which hold layer 0's
+// arrays and the shape, plan, flags and buffers of every layer).
+__device__ __forceinline__ FusedArgs phase_args(const FusedArgs& up, const FusedArgs& dn, const LayerTab& tab, int p,
+                                                uint32_t* sync) {
+  const int l = p >> 1, n_ph = 2 * tab.n_layers;
+  const bool is_up = (p & 1) == 0;
+  FusedArgs a = is_up ? up : dn;
+  const LayerProj& lp = is_up ? tab.up[l] : tab.dn[l];
+  a.codes = lp.codes;
+  a.row_off = lp.row_off;
+  a.bstart = lp.bstart;
+  a.scales = lp.scales;
+  a.experts = lp.experts;
+  a.ids = up.ids + (int64_t)l * up.n_tokens;
+  a.ws = up.ws + (uint64_t)p * tab.ws_words;
+  const uint64_t hl = (uint64_t)l * (uint64_t)up.n_tokens * (uint64_t)up.rows;    // layer l's h
+  const uint64_t yl = (uint64_t)l * (uint64_t)up.n_tokens * (uint64_t)dn.rows;    // layer l's output
+  if (is_up) {
+    a.y = tab.h + hl;
+    if (l > 0) {
+      a.x = tab.y + (yl - (uint64_t)up.n_tokens * (uint64_t)dn.rows);
+      a.flags = (a.flags & ~SBM_F_IN_BF16) | SBM_F_IN_RMS;
+      a.x_bytes = (uint32_t)((uint64_t)a.n_tokens * (uint64_t)a.cols * 2u);
+    }
+  } else {
+    a.x = tab.h + hl;
+    a.y = tab.y + yl;
+  }
+  a.lm = (p + 1 < n_ph ? 1u : 0u) | (p > 0 ? 2u : 0u);
+  a.tok_done = sync + kSyncHdr + (uint64_t)p * (uint64_t)a.n_tokens;
+  a.tok_wait = sync + kSyncHdr + (uint64_t)(p > 0 ? p - 1 : 0) * (uint64_t)a.n_tokens;
+  a.tok_expect = (uint32_t)(is_up ? dn.rows : up.rows);
+  return a;
+}
+
+// One phase: group the tokens (in LDS, or read the grouping launch's result),
+// then run this workgroup's slice.
+__device__ __forceinline__ void stack_phase(const FusedArgs& a, int p, unsigned char* smem, int32_t my_id,
+                                            bool image_ok, uint32_t split7, uint32_t* sync) {
   const int32_t* perm;
   const uint4* items;
   uint64_t g0, g1;
   if (a.group_in_lds) {
     if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
-    else group_lds(a, (uint32_t*)smem, (int32_t)threadIdx.x < a.n_tokens ? my_id : -1);
+    else group_lds(a, (uint32_t*)smem, (int32_t)tid_v() < a.n_tokens ? my_id : -1);
     g0 = s_slice[0];
     g1 = s_slice[1];
     perm = s_perm;
     items = s_items;
   } else {
     // the grouping launch cut the phase into a.grid slices; the layer launch
-    // may hold more workgroups (the other phase's count)
+    // may hold more workgroups (another phase's count)
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
     const bool mine = (int32_t)blockIdx.x < a.grid;
@@ -1938,40 +2041,63 @@ __device__ __forceinline__ void ffn_phase(const FusedArgs& a, unsigned char* sme
     perm = (const int32_t*)(a.ws + L.perm);
     items = (const uint4*)(a.ws + L.items);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && tid_v() == 0) {
     // this thread wrote (or the grouping kernel before this launch wrote) the
-    // phase's word: the id count once, the flag bits of both phases
+    // phase's word: invalid ids counted once per layer, the flag bits of all phases
     uint32_t w = a.ws[0];
-    if (LM == 2) w &= ~kErrCountMask;
+    if (p & 1) w &= ~kErrCountMask;
     if (!image_ok) w = (w & ~kErrDict) | kErrBadImage;
     if (w) __hip_atomic_fetch_or(sync + 1, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (image_ok && g0 < g1) run_slice<false, false, 3, LM>(a, smem, perm, items, g0, g1, split7);
+  if (blockIdx.x == 0 && image_ok && lm_out<3>(a)) {
+    // a token whose expert id is out of range gets no rows in this layer:
+    // its count is raised at once, so the next phase does not wait for it
+    // (its output is invalid, and the error word counts it)
+    for (int32_t t = tid_v(); t < a.n_tokens; t += kFThreads) {
+      const int32_t e = a.ids[t];
+      if (e < 0 || e >= a.n_experts)
+        __hip_atomic_fetch_add(a.tok_done + t, (uint32_t)a.rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (image_ok && g0 < g1) run_slice<false, false, 3, 3>(a, smem, perm, items, g0, g1, split7);
   __syncthreads();      // the grouping's LDS is rebuilt by the next phase
 }
 
 template <int DUMMY>
-__global__ __launch_bounds__(kFThreads) void ffn_kernel(const FusedArgs up, const FusedArgs dn, uint32_t* sync) {
+__global__ __launch_bounds__(kFThreads) void stack_kernel(const FusedArgs up, const FusedArgs dn, const LayerTab tab,
+                                                          uint32_t* sync) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int32_t tq = (int32_t)threadIdx.x < up.n_tokens ? (int32_t)threadIdx.x : up.n_tokens - 1;
-  const int32_t my_id = up.ids[tq];
+  const int32_t T = up.n_tokens;
+  const int32_t tq = (int32_t)tid_v() < T ? (int32_t)tid_v() : T - 1;
+  int32_t my_id = up.ids[tq];
+  // the next layer's id is requested a layer ahead
+  int32_t next_id = tab.n_layers > 1 ? up.ids[T + tq] : 0;
   const uint4 hdr = *(const uint4*)up.image;
   stage_tables_dma<3>(up.image);
   const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
                         hdr.w == hdr.z + (SBM_DICT_ENTRIES - hdr.z + 7u) / 8u && hdr.w <= kTabEntries;
   const uint32_t split7 = 7u * hdr.z;
-  ffn_phase<1>(up, smem, my_id, image_ok, split7, sync);
-  ffn_phase<2>(dn, smem, my_id, image_ok, split7, sync);
+  for (int32_t t = tid_v(); t < kGroupInLds; t += kFThreads) s_pend[t] = 0;   // read after the grouping's barriers
+  for (int p = 0; p < 2 * tab.n_layers; ++p) {
+    if (p > 0 && (p & 1) == 0) {
+      const int l = p >> 1;
+      my_id = next_id;
+      if (l + 1 < tab.n_layers) next_id = up.ids[(int64_t)(l + 1) * T + tq];
+    }
+    const FusedArgs a = phase_args(up, dn, tab, p, sync);
+    stack_phase(a, p, smem, my_id, image_ok, split7, sync);
+  }
   wait_vmem_all();        // every store and count of this workgroup is complete
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (tid_v() == 0)
     s_last = __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (s_last) {
     // the other workgroups are done: publish the error word, clear the counts
-    for (int32_t t = threadIdx.x; t < up.n_tokens; t += kFThreads)
+    const int32_t n_cnt = (2 * tab.n_layers - 1) * T;
+    for (int32_t t = tid_v(); t < n_cnt; t += kFThreads)
       __hip_atomic_store(sync + kSyncHdr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
+    if (tid_v() == 0) {
       const uint32_t err = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(sync, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1987,7 +2113,7 @@ struct DevInfo {
   // static LDS of the fused-kernel instances, per image kind: the largest over
   // the instances one call may launch (3-slot or 4-slot image)
   int static_lds[2] = {};
-  int ffn_static_lds = 0;
+  int stack_static_lds = 0;
   bool attr_set = false;
   void* scratch = nullptr;   // device address of this device's copy of `scratch`
 };
@@ -2047,11 +2173,11 @@ static int dev_info(DevInfo** out, bool want_scratch = false) {
     }
     {
       hipFuncAttributes fa;
-      if ((e = hipFuncGetAttributes(&fa, (const void*)ffn_kernel<0>)) != hipSuccess)
+      if ((e = hipFuncGetAttributes(&fa, (const void*)stack_kernel<0>)) != hipSuccess)
         return fail(SBM_EHIP, "hipFuncGetAttributes: %s", hipGetErrorString(e));
-      di.ffn_static_lds = (int)fa.sharedSizeBytes;
-      e = hipFuncSetAttribute((const void*)ffn_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              di.max_lds - di.ffn_static_lds);
+      di.stack_static_lds = (int)fa.sharedSizeBytes;
+      e = hipFuncSetAttribute((const void*)stack_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              di.max_lds - di.stack_static_lds);
       if (e != hipSuccess) return fail(SBM_EHIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
     di.attr_set = true;
@@ -2288,49 +2414,76 @@ int sbm_moe_fused_decode_matvec_noalloc(const uint16_t* codes, const uint32_t* r
 
 static size_t align16(size_t b) { return (b + 15u) & ~(size_t)15u; }
 
-size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
-  if (n_experts < 0 || n_tokens < 0) return 0;
-  return align16(((size_t)kSyncHdr + (size_t)n_tokens) * 4u) + 2u * align16(sbm_workspace_bytes(n_experts, n_tokens));
+size_t sbm_layers_workspace_bytes(int32_t n_layers, int32_t n_experts, int32_t n_tokens) {
+  if (n_layers <= 0 || n_experts < 0 || n_tokens < 0) return 0;
+  const size_t phases = 2u * (size_t)n_layers;
+  return align16(((size_t)kSyncHdr + phases * (size_t)n_tokens) * 4u) +
+         phases * align16(sbm_workspace_bytes(n_experts, n_tokens));
 }
 
-int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, const void* dict_image,
-                      const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens, uint16_t* h, void* y,
-                      uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens) {
+  return sbm_layers_workspace_bytes(1, n_experts, n_tokens);
+}
+
+}  // extern "C"
+
+// n_layers layers of (up, ReLU, down) in one launch: the layer call is n_layers = 1.
+static int layers_call(const sbm_projection* up, const sbm_projection* down, int32_t n_layers,
+                       const void* dict_image, const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens,
+                       uint16_t* h, void* y, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (!up || !down) return fail(SBM_EINVAL, "null projection");
+  if (n_layers <= 0 || n_layers > kMaxLayers)
+    return fail(SBM_EINVAL, "n_layers=%d outside 1..%d (longer stacks: one call per %d layers)", n_layers,
+                kMaxLayers, kMaxLayers);
   if (n_tokens < 0 || n_tokens > (int32_t)kErrCountMask) return fail(SBM_EINVAL, "bad n_tokens=%d", n_tokens);
-  if (up->n_experts <= 0 || up->n_experts > (1 << 24) || up->n_experts != down->n_experts)
-    return fail(SBM_EINVAL, "the projections must hold the same experts (%d, %d)", up->n_experts, down->n_experts);
-  for (const sbm_projection* p : {up, down}) {
-    if (p->rows <= 0 || p->rows > (1 << 24) || p->cols <= 0) return fail(SBM_EINVAL, "bad shape %d x %d", p->rows, p->cols);
-    if (p->cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", p->cols);
-    if (p->cols < kSmallCols)
-      return fail(SBM_EINVAL, "cols=%d: the layer call needs rows of at least %d columns (use two "
-                  "sbm_moe_fused_decode_matvec calls)", p->cols, kSmallCols);
-    if ((uint64_t)p->rows * (uint64_t)p->cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
-      return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const sbm_projection* u = up + l;
+    const sbm_projection* d = down + l;
+    if (u->n_experts <= 0 || u->n_experts > (1 << 24) || u->n_experts != d->n_experts ||
+        u->n_experts != up->n_experts)
+      return fail(SBM_EINVAL, "layer %d: the projections must hold the same experts as layer 0 (%d, %d, %d)", l,
+                  u->n_experts, d->n_experts, up->n_experts);
+    for (const sbm_projection* q : {u, d}) {
+      if (q->rows <= 0 || q->rows > (1 << 24) || q->cols <= 0)
+        return fail(SBM_EINVAL, "bad shape %d x %d", q->rows, q->cols);
+      if (q->cols & 1) return fail(SBM_EODD_WIDTH, "cols=%d is odd", q->cols);
+      if (q->cols < kSmallCols)
+        return fail(SBM_EINVAL, "cols=%d: the layer call needs rows of at least %d columns (use two "
+                    "sbm_moe_fused_decode_matvec calls)", q->cols, kSmallCols);
+      if ((uint64_t)q->rows * (uint64_t)q->cols * 6u + (uint64_t)SBM_BLOCK * 28u * 6u >= (1ull << 30))
+        return fail(SBM_ERANGE, "rows*cols too large for 30-bit positions");
+      if (!q->codes || !q->row_off || !q->bstart || !q->scales || !q->experts)
+        return fail(SBM_EINVAL, "null pointer");
+    }
+    if (u->rows != up->rows || u->cols != up->cols || d->rows != down->rows || d->cols != down->cols)
+      return fail(SBM_EINVAL, "layer %d: every layer must have layer 0's shapes", l);
   }
   if (up->rows != down->cols)
     return fail(SBM_EINVAL, "up rows (%d) must equal down cols (%d): h is their common width", up->rows, down->cols);
+  if (n_layers > 1 && down->rows != up->cols)
+    return fail(SBM_EINVAL, "down rows (%d) must equal up cols (%d): each layer's output feeds the next",
+                down->rows, up->cols);
   if (flags & ~(SBM_F_OUT_F32 | SBM_F_IN_RMS | SBM_F_IN_BF16))
     return fail(SBM_EINVAL, "unknown or unsupported flags 0x%x", flags);
-  if ((uint64_t)n_tokens * (uint64_t)down->cols * 2u >= (1ull << 31)) return fail(SBM_ERANGE, "h too large");
+  if (n_layers > 1 && (flags & SBM_F_OUT_F32))
+    return fail(SBM_EINVAL, "SBM_F_OUT_F32: one layer only (every layer's fp16 output feeds the next)");
+  if ((uint64_t)n_tokens * (uint64_t)std::max(down->cols, up->cols) * 2u >= (1ull << 31))
+    return fail(SBM_ERANGE, "activations too large");
   if (n_tokens == 0) return SBM_OK;
-  for (const sbm_projection* p : {up, down})
-    if (!p->codes || !p->row_off || !p->bstart || !p->scales || !p->experts) return fail(SBM_EINVAL, "null pointer");
   if (!dict_image || !x || !expert_ids || !h || !y || !workspace) return fail(SBM_EINVAL, "null pointer");
   if ((uintptr_t)workspace & 15u) return fail(SBM_EINVAL, "workspace must be 16-byte aligned");
-  const size_t need = sbm_ffn_workspace_bytes(up->n_experts, n_tokens);
+  const size_t need = sbm_layers_workspace_bytes(n_layers, up->n_experts, n_tokens);
   if (workspace_bytes < need) return fail(SBM_ENOSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   DevInfo* di = nullptr;
   int st = dev_info(&di);
   if (st) return st;
   Plan pu, pd;
-  if (!make_plan(up->cols, di->max_lds, di->ffn_static_lds, &pu) ||
-      !make_plan(down->cols, di->max_lds, di->ffn_static_lds, &pd))
+  if (!make_plan(up->cols, di->max_lds, di->stack_static_lds, &pu) ||
+      !make_plan(down->cols, di->max_lds, di->stack_static_lds, &pd))
     return fail(SBM_ERANGE, "a token row does not fit in %d bytes of LDS", di->max_lds);
-  // Each phase is cut into as many slices as its rows fill at 64 rows per
-  // workgroup (as a projection call is), at most one per CU; the launch holds
-  // the larger count, and workgroups past a phase's count skip that phase.
+  // Each phase is cut into as many slices as its rows fill at kRowsPerGroup
+  // rows per workgroup (as a projection call is), at most one per CU; the
+  // launch holds the larger count, and workgroups past a phase's count skip it.
   auto phase_grid = [&](const sbm_projection* p, const Plan& pl) {
     const int64_t max_items = (int64_t)std::min(p->n_experts, n_tokens) + n_tokens / pl.tcmax + 1;
     const int64_t g = (max_items * p->rows + kRowsPerGroup - 1) / kRowsPerGroup;
@@ -2338,28 +2491,62 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
   };
   const int32_t grid_u = phase_grid(up, pu), grid_d = phase_grid(down, pd), grid = std::max(grid_u, grid_d);
   uint32_t* sync = (uint32_t*)workspace;
-  unsigned char* wsu = (unsigned char*)workspace + align16(((size_t)kSyncHdr + (size_t)n_tokens) * 4u);
-  unsigned char* wsd = wsu + align16(sbm_workspace_bytes(up->n_experts, n_tokens));
+  const size_t phase_bytes = align16(sbm_workspace_bytes(up->n_experts, n_tokens));
+  unsigned char* ws0 = (unsigned char*)workspace + align16(((size_t)kSyncHdr + 2u * (size_t)n_layers *
+                                                                                   (size_t)n_tokens) * 4u);
   FusedArgs ua, da;
   fill_args(ua, up->codes, up->row_off, up->bstart, up->scales, up->experts, up->n_experts, up->rows, up->cols,
-            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & (SBM_F_IN_RMS | SBM_F_IN_BF16)), wsu, pu,
+            dict_image, x, expert_ids, n_tokens, h, SBM_F_RELU | (flags & (SBM_F_IN_RMS | SBM_F_IN_BF16)), ws0, pu,
             grid_u);
   fill_args(da, down->codes, down->row_off, down->bstart, down->scales, down->experts, down->n_experts, down->rows,
-            down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, wsd, pd, grid_d);
-  ua.tok_done = da.tok_done = sync + kSyncHdr;
+            down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, ws0 + phase_bytes, pd, grid_d);
   ua.sync_err = da.sync_err = sync + 1;
-  da.tok_expect = (uint32_t)up->rows;
   da.x_bytes = (uint32_t)((uint64_t)n_tokens * (uint64_t)down->cols * 2u);
+  LayerTab tab;
+  memset(&tab, 0, sizeof(tab));
+  for (int32_t l = 0; l < n_layers; ++l) {
+    tab.up[l] = LayerProj{up[l].codes, up[l].row_off, up[l].bstart, up[l].scales, up[l].experts};
+    tab.dn[l] = LayerProj{down[l].codes, down[l].row_off, down[l].bstart, down[l].scales, down[l].experts};
+  }
+  tab.h = h;
+  tab.y = (uint16_t*)y;
+  tab.ws_words = (uint32_t)(phase_bytes / 4u);
+  tab.n_layers = n_layers;
   hipStream_t s = (hipStream_t)stream;
   if (!ua.group_in_lds) {
-    if ((st = launch_group(ua, s))) return st;
-    if ((st = launch_group(da, s))) return st;
+    // more tokens than the in-kernel grouping takes: one grouping launch per
+    // phase, each into its phase's part of the workspace
+    for (int32_t p = 0; p < 2 * n_layers; ++p) {
+      FusedArgs g = (p & 1) ? da : ua;
+      const LayerProj& lp = (p & 1) ? tab.dn[p >> 1] : tab.up[p >> 1];
+      g.experts = lp.experts;
+      g.ids = expert_ids + (int64_t)(p >> 1) * n_tokens;
+      g.ws = (uint32_t*)(ws0 + (size_t)p * phase_bytes);
+      if ((st = launch_group(g, s))) return st;
+    }
   }
   const uint32_t lds = std::max<uint32_t>(std::max(pu.lds_total, pd.lds_total), kGroupScratch);
-  hipLaunchKernelGGL(ffn_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, ua, da, sync);
+  hipLaunchKernelGGL(stack_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, ua, da, tab, sync);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SBM_EHIP, "layer launch: %s", hipGetErrorString(e));
   return SBM_OK;
+}
+
+extern "C" {
+
+int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, const void* dict_image,
+                      const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens, uint16_t* h, void* y,
+                      uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return layers_call(up, down, 1, dict_image, x, expert_ids, n_tokens, h, y, flags, workspace, workspace_bytes,
+                     stream);
+}
+
+int sbm_moe_fused_layers(const sbm_projection* up, const sbm_projection* down, int32_t n_layers,
+                         const void* dict_image, const uint16_t* x, const int32_t* expert_ids, int32_t n_tokens,
+                         uint16_t* h, uint16_t* y, uint32_t flags, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return layers_call(up, down, n_layers, dict_image, x, expert_ids, n_tokens, h, y, flags, workspace,
+                     workspace_bytes, stream);
 }
 
 int sbm_workspace_error(const void* workspace, uint32_t* out_error, void* stream) {

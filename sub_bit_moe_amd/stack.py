@@ -135,7 +135,8 @@ class Runner:
     """Preallocated buffers for repeated passes (minmax: the stack's scales
     are (w_min, w_max) pairs; deterministic: fixed-point row accumulators)."""
 
-    def __init__(self, st: Stack, minmax: bool = False, layer: bool = False, deterministic: bool = False):
+    def __init__(self, st: Stack, minmax: bool = False, layer: bool = False, deterministic: bool = False,
+                 layers: bool = False):
         import torch
         c = st.cfg
         dev = st.x0.device
@@ -143,6 +144,13 @@ class Runner:
         self.minmax = minmax
         self.det = deterministic
         self.layer = layer and not minmax and not deterministic   # one launch per layer (sbm_moe_fused_ffn)
+        # one launch for all layers (sbm_moe_fused_layers, up to 32 layers per launch)
+        self.layers = layers and not minmax and not deterministic and not self.layer
+        self.ws_layers = (api.alloc_layers_workspace(min(c.n_layers, 32), c.n_experts, c.n_tokens, dev)
+                          if self.layers else None)
+        if self.layers:     # every layer's h and output
+            self.h_all = torch.empty(c.n_layers, c.n_tokens, c.d_ff, dtype=torch.float16, device=dev)
+            self.y_all = torch.empty(c.n_layers, c.n_tokens, c.d_model, dtype=torch.float16, device=dev)
         self.ws_ffn = api.alloc_ffn_workspace(c.n_experts, c.n_tokens, dev) if self.layer else None
         # a layer call reads x while other workgroups already write y: consecutive layers alternate buffers
         self.y2 = [torch.empty(c.n_tokens, c.d_model, dtype=torch.float16, device=dev) for _ in range(2)]
@@ -166,6 +174,20 @@ class Runner:
         nothing else."""
         st = self.st
         x = st.x0
+        if self.layers:
+            # up to 32 layers per launch; every layer's h and y are kept
+            L = st.cfg.n_layers
+            for l0 in range(0, L, 32):
+                l1 = min(L, l0 + 32)
+                api.moe_fused_layers(st.up[l0:l1], st.down[l0:l1], st.image, x, st.routes[l0:l1],
+                                     h=self.h_all[l0:l1], y=self.y_all[l0:l1], workspace=self.ws_layers,
+                                     in_rms=l0 > 0)
+                x = self.y_all[l1 - 1]
+            if keep is not None:
+                for l in range(L):
+                    keep[l] = ((st.x0 if l == 0 else self.y_all[l - 1]).clone(), self.h_all[l].clone(),
+                               self.y_all[l].clone())
+            return x
         for l in range(st.cfg.n_layers):
             ids = st.routes[l]
             if self.layer:
