@@ -2018,14 +2018,24 @@ __device__ __forceinline__ FusedArgs phase_args(const FusedArgs& up, const Fused
 
 // One phase: group the tokens (in LDS, or read the grouping launch's result),
 // then run this workgroup's slice.
-__device__ __forceinline__ void stack_phase(const FusedArgs& a, int p, unsigned char* smem, int32_t my_id,
-                                            bool image_ok, uint32_t split7, uint32_t* sync) {
+// Expert ids of the current and the next layer, by token (in-LDS grouping).
+__shared__ int32_t s_ids[2][kGroupInLds];
+
+__device__ __forceinline__ void stack_phase(const FusedArgs& a, int p, unsigned char* smem, bool image_ok,
+                                            uint32_t split7, uint32_t* sync, int32_t n_layers) {
   const int32_t* perm;
   const uint4* items;
   uint64_t g0, g1;
+  const int32_t l = p >> 1;
   if (a.group_in_lds) {
+    const int32_t t = (int32_t)tid_v();
+    const int32_t my_id = t < a.n_tokens ? s_ids[l & 1][t] : -1;
+    // an up phase requests the next layer's ids, stored once the grouping is done
+    const bool fetch = (p & 1) == 0 && l + 1 < n_layers && t < a.n_tokens;
+    const int32_t next_id = fetch ? a.ids[a.n_tokens + t] : 0;
     if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
-    else group_lds(a, (uint32_t*)smem, (int32_t)tid_v() < a.n_tokens ? my_id : -1);
+    else group_lds(a, (uint32_t*)smem, my_id);
+    if (fetch) s_ids[(l + 1) & 1][t] = next_id;     // the other layer's slot, read after later barriers
     g0 = s_slice[0];
     g1 = s_slice[1];
     perm = s_perm;
@@ -2067,11 +2077,7 @@ template <int DUMMY>
 __global__ __launch_bounds__(kFThreads) void stack_kernel(const FusedArgs up, const FusedArgs dn, const LayerTab tab,
                                                           uint32_t* sync) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int32_t T = up.n_tokens;
-  const int32_t tq = (int32_t)tid_v() < T ? (int32_t)tid_v() : T - 1;
-  int32_t my_id = up.ids[tq];
-  // the next layer's id is requested a layer ahead
-  int32_t next_id = tab.n_layers > 1 ? up.ids[T + tq] : 0;
+  if (up.group_in_lds && (int32_t)tid_v() < up.n_tokens) s_ids[0][tid_v()] = up.ids[tid_v()];
   const uint4 hdr = *(const uint4*)up.image;
   stage_tables_dma<3>(up.image);
   const bool image_ok = hdr.x == kImageMagic && hdr.y == kImageVersion && hdr.z <= SBM_DICT_ENTRIES &&
@@ -2079,13 +2085,8 @@ __global__ __launch_bounds__(kFThreads) void stack_kernel(const FusedArgs up, co
   const uint32_t split7 = 7u * hdr.z;
   for (int32_t t = tid_v(); t < kGroupInLds; t += kFThreads) s_pend[t] = 0;   // read after the grouping's barriers
   for (int p = 0; p < 2 * tab.n_layers; ++p) {
-    if (p > 0 && (p & 1) == 0) {
-      const int l = p >> 1;
-      my_id = next_id;
-      if (l + 1 < tab.n_layers) next_id = up.ids[(int64_t)(l + 1) * T + tq];
-    }
     const FusedArgs a = phase_args(up, dn, tab, p, sync);
-    stack_phase(a, p, smem, my_id, image_ok, split7, sync);
+    stack_phase(a, p, smem, image_ok, split7, sync, tab.n_layers);
   }
   wait_vmem_all();        // every store and count of this workgroup is complete
   __syncthreads();
@@ -2094,7 +2095,7 @@ __global__ __launch_bounds__(kFThreads) void stack_kernel(const FusedArgs up, co
   __syncthreads();
   if (s_last) {
     // the other workgroups are done: publish the error word, clear the counts
-    const int32_t n_cnt = (2 * tab.n_layers - 1) * T;
+    const int32_t n_cnt = (2 * tab.n_layers - 1) * up.n_tokens;
     for (int32_t t = tid_v(); t < n_cnt; t += kFThreads)
       __hip_atomic_store(sync + kSyncHdr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid_v() == 0) {
