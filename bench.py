@@ -8,12 +8,13 @@ compressed artefact, ~1.57 T parameters).  One step = one pass of 64 fp16
 N(0,1) tokens through all 30 layers (top-1 Zipf(1.1) routing per layer:
 up + ReLU, down; the RMS glue between layers runs inside the next up
 projection, and once after the last layer), captured once in a HIP graph
-and replayed.
+and replayed.  The pass runs the library's multi-layer call (all 30 layers
+in one launch); the same pass with two launches per layer is timed beside it.
 
 Metric: compressed bytes (codewords + block starts + row scales of every
 touched (expert, matrix)) read per second.  Also reported: bf16-equivalent
-bytes per second, the fused kernel's roofline (HIP events around each launch
-on its stream), and the oracle's throughput on a bounded CPU sample.
+bytes per second, the fused kernel's roofline (HIP events around its launches
+on their stream), and the oracle's throughput on a bounded CPU sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
 """
@@ -36,13 +37,14 @@ def log(msg):
 
 
 def measured_traffic():
-    """Calibrated HBM bytes per fused launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    """Calibrated HBM bytes per launch of the one-launch pass from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel source."""
     import glob
     import hashlib
     src = os.path.join(ROOT, "sub_bit_moe_amd", "csrc", "sbm_gpu.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "fused_kernel_traffic_*.md"))):
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "stack_kernel_traffic_*.md"))):
         for line in open(f):
             if line.startswith("traffic_bytes_per_launch"):
                 kv = dict(t.split("=") for t in line.split()[1:])
@@ -52,14 +54,15 @@ def measured_traffic():
 
 
 def measured_lds():
-    """LDS and VALU occupancy of the fused kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    """LDS and VALU occupancy of the one-launch pass's kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel source."""
     import glob
     import hashlib
     import re
     src = os.path.join(ROOT, "sub_bit_moe_amd", "csrc", "sbm_gpu.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "fused_kernel_lds_*.md"))):
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "stack_kernel_lds_*.md"))):
         text = open(f).read()
         if f"sha256[:16] = {sha}" not in text:
             continue
@@ -502,6 +505,60 @@ def _graph_time_us(fn, n_calls, warmup=2):
     return 1e3 * e0.elapsed_time(e1) / n_calls
 
 
+def time_pass(run, steps, warmup):
+    """One pass (run.run(): every layer, then the glue) captured in a graph:
+    mean ms over steps replays bracketed by events, and the sorted per-replay
+    times of a second loop (events between replays)."""
+    import torch
+    run.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    del g
+    return ms, per
+
+
+def time_launches(run, n_launch, steps, warmup):
+    """Average duration of the pass's fused launches (run.run_layers(), no
+    glue) replayed back to back in a graph, HIP events on the launch stream."""
+    import torch
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        run.run_layers()
+    for _ in range(warmup):
+        gk.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for _ in range(steps):
+        gk.replay()
+    k1.record(stream)
+    torch.cuda.synchronize()
+    del gk
+    return 1e3 * k0.elapsed_time(k1) / (steps * n_launch)
+
+
 def per_matrix_table(n_calls: int = 200, gb: float = 1.1):
     """The QMoE page's per-layer kernel comparison (Figure 5, left) on MI355X:
     for each Switch matrix shape, one token through the fused decode + matvec
@@ -670,76 +727,52 @@ def main():
     st = S.build(cfg, dev, log=lambda m: log(m) if ("30/" in m or m.startswith("layer 1/")) else None)
     log(f"stack generated in {time.time() - t0:.1f} s: {st.stored_bytes() / 1e9:.1f} GB stored, "
         f"{st.n_params() / 1e12:.3f} T params, {8 * st.stored_bytes() / st.n_params():.3f} bit/param")
-    run = S.Runner(st)
-    run.run()
-    torch.cuda.synchronize()
-    # capture one pass in a graph
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run.run()
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    # per-replay spread (a separate loop, outside the timed region above)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    ev[0].record()
-    for i in range(args.steps):
-        g.replay()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    # The headline pass: all layers in one launch of the multi-layer call
+    # (sbm_moe_fused_layers; up to 32 layers per launch), then the glue on the
+    # last output.  Beside it, the same pass with two launches per layer.
+    run = S.Runner(st, layers=True)
+    run2 = S.Runner(st)
+    ms, per = time_pass(run, args.steps, args.warmup)
+    ms2, per2 = time_pass(run2, args.steps, args.warmup)
     comp, bf16 = st.pass_bytes()
     value = comp / (ms * 1e-3) / 1e9
-    log(f"pass {ms:.3f} ms, {value:.1f} GB/s compressed, {bf16 / (ms * 1e-3) / 1e9:.1f} GB/s bf16-equivalent")
+    log(f"pass {ms:.3f} ms, {value:.1f} GB/s compressed, {bf16 / (ms * 1e-3) / 1e9:.1f} GB/s bf16-equivalent "
+        f"(two launches per layer: {ms2:.3f} ms)")
 
-    # The fused kernel alone: the pass's 2 x layers fused launches captured
-    # without the glue and replayed back to back; HIP events on the launch
-    # stream bracket the replays, so the average launch duration is the
-    # kernel's own (graph replays leave no gaps between kernels).
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk):
-        run.run_layers()
-    for _ in range(args.warmup):
-        gk.replay()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for _ in range(args.steps):
-        gk.replay()
-    k1.record(stream)
-    torch.cuda.synchronize()
-    n_launch = 2 * cfg.n_layers
-    launch_us = 1e3 * k0.elapsed_time(k1) / (args.steps * n_launch)
+    # The kernels alone: the pass's fused launches captured without the glue
+    # and replayed back to back; HIP events on the launch stream bracket the
+    # replays, so the average launch duration is the kernel's own.
+    n_launch = (cfg.n_layers + 31) // 32
+    launch_us = time_launches(run, n_launch, args.steps, args.warmup)
+    launch2_us = time_launches(run2, 2 * cfg.n_layers, args.steps, args.warmup)
     bytes_per_launch = comp / n_launch
     achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
     traffic, traffic_src = measured_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "traffic_source": traffic_src,
-                "kernel": "sbm::fused_kernel (token grouping inside; 2 launches per layer)",
+                "kernel": f"sbm::stack_kernel ({cfg.n_layers} layers of up + down in {n_launch} launch"
+                          f"{'es' if n_launch > 1 else ''}; token grouping inside)",
                 "avg_launch_us": round(launch_us, 2),
                 "bytes_per_launch": int(bytes_per_launch),
+                "avg_projection_us": round(launch_us * n_launch / (2 * cfg.n_layers), 2),
                 "binding_unit": "LDS gathers (64 random per 1024 codewords), not HBM",
                 "lds_counters": measured_lds()}
+    two_launch = {"ms_per_step": round(ms2, 4), "GBps": round(comp / (ms2 * 1e-3) / 1e9, 1),
+                  "kernel": "sbm::fused_kernel (two launches per layer)", "avg_launch_us": round(launch2_us, 2),
+                  "bytes_per_launch": int(comp / (2 * cfg.n_layers)),
+                  "pass_time_vs_one_launch": round(ms2 / ms, 4)}
+    log(f"one launch: {launch_us:.1f} us ({roofline['avg_projection_us']} us per projection); "
+        f"two per layer: {launch2_us:.2f} us per launch")
     minmax = None
     if not args.no_minmax:
         log("pass on the per-row (w_min, w_max) grid ...")
-        minmax = minmax_pass(st, args.steps, args.warmup, launch_us)
+        minmax = minmax_pass(st, args.steps, args.warmup, launch2_us)
         log(f"min/max grid: {minmax['avg_launch_us']} us per launch, {minmax['GBps']} GB/s")
     det = None
     if not args.no_det:
         log("pass with fixed-point row accumulators (SBM_F_DETERMINISTIC) ...")
-        det = deterministic_pass(st, args.steps, args.warmup, launch_us)
+        det = deterministic_pass(st, args.steps, args.warmup, launch2_us)
         log(f"deterministic: {det['avg_launch_us']} us per launch, bit-identical replays: {det['replays_bit_identical']}")
     dmatch = None
     if not args.no_dict_match:
@@ -757,7 +790,7 @@ def main():
     fusion = None
     if not args.no_fusion_baselines:
         log("fusion baselines (layer 0: unfused decode -> bf16 -> GEMM, dense bf16 GEMM) ...")
-        fusion = fusion_baselines(st, run)
+        fusion = fusion_baselines(st, run2)
         log(f"layer 0: fused {fusion['fused_us']} us, unfused {fusion['unfused_decode_dense_gemm_us']} us, "
             f"dense bf16 {fusion['dense_bf16_gemm_us']} us")
     permat = None
@@ -803,6 +836,7 @@ def main():
         "pct_of_measured_copy": round(100 * value / peaks["device_copy_GBps"], 2) if peaks else None,
         "measured_peaks": peaks,
         "roofline": roofline,
+        "two_launches_per_layer": two_launch,
         "cpu_baseline": cpu,
         "fusion_baselines": fusion,
         "minmax_grid": minmax,
