@@ -521,6 +521,18 @@ struct BlockCodes {
 };
 
 // Everything a workgroup needs about one chunk: rows [ra, rb) of item q.
+// The slice of workgroup b among n.  Workgroups are dealt to the 8 XCDs in
+// turn (b mod 8), so this numbering gives each XCD a run of consecutive slices:
+// the items of one expert, which all decode its codes, then mostly run on one
+// XCD at about the same time and read the codes again from its L2.  A
+// permutation of [0, n); workgroups b >= n (a launch holding more workgroups
+// than this phase has slices) keep b, an empty slice.
+__device__ __forceinline__ uint32_t xcd_slice(uint32_t b, uint32_t n) {
+  if (b >= n) return b;
+  const uint32_t x = b & 7u, per = n >> 3, extra = n & 7u;
+  return x * per + (x < extra ? x : extra) + (b >> 3);
+}
+
 struct Chunk {
   uint32_t q, tb, nt;     // nt: token count (without the MFMA flag)
   int32_t ra, rb;
@@ -1738,8 +1750,8 @@ __device__ __forceinline__ void group_lds(const FusedArgs& a, uint32_t* sc, int3
     const uint32_t n_items = __builtin_amdgcn_readlane(ci, 63), wtot = __builtin_amdgcn_readlane(wi, 63);
     const uint32_t F = a.item_cost;
     const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
-    const uint64_t u[2] = {slice_div(wall * blockIdx.x, (uint32_t)a.grid),
-                           slice_div(wall * (blockIdx.x + 1), (uint32_t)a.grid)};
+    const uint32_t sl = xcd_slice(blockIdx.x, (uint32_t)a.grid);
+    const uint64_t u[2] = {slice_div(wall * sl, (uint32_t)a.grid), slice_div(wall * (sl + 1), (uint32_t)a.grid)};
     uint32_t qi = ci - c, wq = wi - w0 - w1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1836,7 +1848,8 @@ __device__ __forceinline__ void group_wave(const FusedArgs& a, uint32_t* sc, int
     const uint32_t F = a.item_cost;
     const uint64_t rows = (uint64_t)a.rows, wall = (uint64_t)wtot * rows + (uint64_t)n_items * F;
     // lane h computes u_h, then both are broadcast
-    const uint64_t uh = slice_div(wall * (blockIdx.x + (lane & 1u) + vzero()), (uint32_t)a.grid);
+    const uint64_t uh = slice_div(wall * (xcd_slice(blockIdx.x, (uint32_t)a.grid) + (lane & 1u) + vzero()),
+                                  (uint32_t)a.grid);
     const uint64_t u[2] = {
         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)uh, 0) |
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uh >> 32), 0) << 32),
@@ -1930,8 +1943,9 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs a) {
     if (a.err_out && blockIdx.x == 0 && threadIdx.x == 0) *a.err_out = a.ws[0];
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
-    g0 = bounds[blockIdx.x];
-    g1 = bounds[blockIdx.x + 1];
+    const uint32_t sl = xcd_slice(blockIdx.x, (uint32_t)a.grid);
+    g0 = bounds[sl];
+    g1 = bounds[sl + 1];
     perm = (const int32_t*)(a.ws + L.perm);
     items = (const uint4*)(a.ws + L.items);
   }
@@ -2046,8 +2060,9 @@ __device__ __forceinline__ void stack_phase(const FusedArgs& a, int p, unsigned 
     const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
     const uint64_t* bounds = (const uint64_t*)(a.ws + L.bounds);
     const bool mine = (int32_t)blockIdx.x < a.grid;
-    g0 = mine ? bounds[blockIdx.x] : 0;
-    g1 = mine ? bounds[blockIdx.x + 1] : 0;
+    const uint32_t sl = mine ? xcd_slice(blockIdx.x, (uint32_t)a.grid) : 0u;
+    g0 = mine ? bounds[sl] : 0;
+    g1 = mine ? bounds[sl + 1] : 0;
     perm = (const int32_t*)(a.ws + L.perm);
     items = (const uint4*)(a.ws + L.items);
   }
