@@ -75,6 +75,24 @@ def measured_lds():
     return None
 
 
+def lds_ceiling(st, comp: float, lds):
+    """The format's LDS ceiling at one token per expert, for comparison with
+    `achieved`: 64 random LDS gathers per 1024 codewords (one table read and
+    three slot reads per codeword), each taking the LDS-busy cycles per LDS
+    instruction that the committed counter summary measured (7.4 if there is
+    none for this source), on 256 CUs at 2.4 GHz, times this pass's algorithmic
+    bytes per codeword."""
+    c = st.cfg
+    words = 0
+    for l in range(c.n_layers):
+        for e in st.touched(l):
+            words += int(st.up[l].host_desc[int(e)].n_codes) + int(st.down[l].host_desc[int(e)].n_codes)
+    cyc = lds["lds_busy_cycles_per_instr"] if lds else 7.4
+    codewords_per_s = 256 * 2.4e9 * 1024 / (64 * cyc)
+    gbps = codewords_per_s * (comp / words) / 1e9
+    return {"GBps": round(gbps, 1), "cycles_per_gather": cyc, "bytes_per_codeword": round(comp / words, 4)}
+
+
 def cpu_baseline(st, n_mats: int = 4, budget_s: float = 12.0):
     """The oracle (pure Python/numpy, fp64) decoding and multiplying a bounded
     sample of the same workload: the first n_mats touched matrices of layer 0,
@@ -758,6 +776,8 @@ def main():
                 "avg_projection_us": round(launch_us * n_launch / (2 * cfg.n_layers), 2),
                 "binding_unit": "LDS gathers (64 random per 1024 codewords), not HBM",
                 "lds_counters": measured_lds()}
+    roofline["lds_ceiling"] = lds_ceiling(st, comp, roofline["lds_counters"])
+    roofline["lds_ceiling"]["frac"] = round(achieved / roofline["lds_ceiling"]["GBps"], 4)
     two_launch = {"ms_per_step": round(ms2, 4), "GBps": round(comp / (ms2 * 1e-3) / 1e9, 1),
                   "kernel": "sbm::fused_kernel (two launches per layer)", "avg_launch_us": round(launch2_us, 2),
                   "bytes_per_launch": int(comp / (2 * cfg.n_layers)),
