@@ -724,7 +724,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(experts would shard expert-parallel; see the design notes). Run with --gpus 1.",
+              "(experts would shard expert-parallel, with one all-to-all of tokens each way per layer). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     import torch
