@@ -8,7 +8,7 @@ most probable candidate, records it when its length is 1..28, and pushes its
 extensions by one more *pair* of symbols.  Codeword = position in the table,
 the table being ordered from most to least probable.
 
-Readings taken where the page is silent (each also listed in the design notes):
+Readings taken where the page is silent:
   * Extension is by pairs, so only even lengths 2..28 exist.
   * Equal probabilities: every sequence with z zeros and n nonzeros has the
     same probability ("class" (L, n), L = z + n).  Within a class the order is
