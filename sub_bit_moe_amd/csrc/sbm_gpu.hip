@@ -351,13 +351,11 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh_tot, uint32_t* tota
   return out;
 }
 
-__global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
-                                                         int32_t E, int32_t titem, int32_t rows, int32_t cols,
-                                                         int32_t grid, uint32_t item_cost, int32_t mfma, int32_t minmax,
-                                                         const sbm_matrix_desc* __restrict__ experts,
-                                                         const DictImage* __restrict__ image,
-                                                         uint32_t* __restrict__ ws) {
-  __shared__ uint32_t sh_tot[kWaves + 1];
+__shared__ uint32_t sh_tot[kWaves + 1];
+__device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int32_t T, int32_t E, int32_t titem,
+                                           int32_t rows, int32_t cols, int32_t grid, uint32_t item_cost,
+                                           int32_t mfma, int32_t minmax, const sbm_matrix_desc* __restrict__ experts,
+                                           const DictImage* __restrict__ image, uint32_t* __restrict__ ws) {
   const WsLayout L = ws_layout(E, T);
   uint32_t* hdr = ws;
   uint32_t* cnt = ws + L.cnt;
@@ -438,6 +436,15 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restri
   const uint64_t wall = (uint64_t)carry * (uint64_t)rows + (uint64_t)n_items * item_cost;
   for (int g = threadIdx.x; g <= grid; g += kThreads)
     bounds[g] = weighted_boundary(items, n_items, carry, rows, item_cost, wall * (uint64_t)g / (uint64_t)grid);
+}
+
+__global__ __launch_bounds__(kThreads) void group_kernel(const int32_t* __restrict__ ids, int32_t T,
+                                                         int32_t E, int32_t titem, int32_t rows, int32_t cols,
+                                                         int32_t grid, uint32_t item_cost, int32_t mfma, int32_t minmax,
+                                                         const sbm_matrix_desc* __restrict__ experts,
+                                                         const DictImage* __restrict__ image,
+                                                         uint32_t* __restrict__ ws) {
+  group_body(ids, T, E, titem, rows, cols, grid, item_cost, mfma, minmax, experts, image, ws);
 }
 
 // ------------------------------------------------------------ fused kernel
@@ -2122,6 +2129,16 @@ __global__ __launch_bounds__(kFThreads) void stack_kernel(const FusedArgs up, co
   }
 }
 
+// Layer calls of more than kGroupInLds tokens: workgroup p groups phase p into
+// its part of the workspace (the tables group_kernel writes), one launch for
+// every phase of the call.
+__global__ __launch_bounds__(kThreads) void stack_group_kernel(const FusedArgs up, const FusedArgs dn,
+                                                               const LayerTab tab, uint32_t* sync) {
+  const FusedArgs a = phase_args(up, dn, tab, (int)blockIdx.x, sync);
+  group_body(a.ids, a.n_tokens, a.n_experts, a.titem, a.rows, a.cols, a.grid, a.item_cost, 0, a.minmax, a.experts,
+             a.image, a.ws);
+}
+
 // ------------------------------------------------------------ host entries
 struct DevInfo {
   int cus = 0;
@@ -2530,16 +2547,11 @@ static int layers_call(const sbm_projection* up, const sbm_projection* down, int
   tab.n_layers = n_layers;
   hipStream_t s = (hipStream_t)stream;
   if (!ua.group_in_lds) {
-    // more tokens than the in-kernel grouping takes: one grouping launch per
-    // phase, each into its phase's part of the workspace
-    for (int32_t p = 0; p < 2 * n_layers; ++p) {
-      FusedArgs g = (p & 1) ? da : ua;
-      const LayerProj& lp = (p & 1) ? tab.dn[p >> 1] : tab.up[p >> 1];
-      g.experts = lp.experts;
-      g.ids = expert_ids + (int64_t)(p >> 1) * n_tokens;
-      g.ws = (uint32_t*)(ws0 + (size_t)p * phase_bytes);
-      if ((st = launch_group(g, s))) return st;
-    }
+    // more tokens than the in-kernel grouping takes: every phase grouped by
+    // one launch, each into its phase's part of the workspace
+    hipLaunchKernelGGL(stack_group_kernel, dim3((unsigned)(2 * n_layers)), dim3(kThreads), 0, s, ua, da, tab, sync);
+    const hipError_t ge = hipGetLastError();
+    if (ge != hipSuccess) return fail(SBM_EHIP, "grouping launch: %s", hipGetErrorString(ge));
   }
   const uint32_t lds = std::max<uint32_t>(std::max(pu.lds_total, pd.lds_total), kGroupScratch);
   hipLaunchKernelGGL(stack_kernel<0>, dim3((unsigned)grid), dim3(kFThreads), lds, s, ua, da, tab, sync);
