@@ -1628,7 +1628,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
       // gathered in LDS and raised once, at the end of the slice, after a
       // single wait for the stores (a wait per chunk would hold up the next
       // chunk's blocks); otherwise raised here, once the chunk's rows are stored.
-      const bool pub = lm_out<LM>(a), pend = pub && a.group_in_lds;
+      const bool pub = lm_out<LM>(a), pend = pub && a.n_tokens <= kGroupInLds;
       if (pub && !pend) wait_vmem_all();   // this thread's output rows have reached device scope
       __syncthreads();
       if (pub) {
@@ -1647,7 +1647,7 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
     if (gn >= g1) break;
     build_chunks(a, items, gn, g1);
   }
-  if (lm_out<LM>(a) && a.group_in_lds) {
+  if (lm_out<LM>(a) && a.n_tokens <= kGroupInLds) {
     wait_vmem_all();      // every output row of the slice has reached device scope
     __syncthreads();
     for (int32_t t = tid_v(); t < a.n_tokens; t += kFThreads) {
@@ -2139,6 +2139,39 @@ __global__ __launch_bounds__(kThreads) void stack_group_kernel(const FusedArgs u
              a.image, a.ws);
 }
 
+// Layer calls of several layers and at most kGroupInLds tokens: workgroup p
+// groups phase p in LDS (as the projection kernel does) and writes the tables
+// the layer launch then reads from the workspace (token order, items, the
+// bounds of every slice), so no workgroup of the layer launch groups.
+__global__ __launch_bounds__(kFThreads) void stack_plan_kernel(const FusedArgs up, const FusedArgs dn,
+                                                              const LayerTab tab, uint32_t* sync) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const FusedArgs a = phase_args(up, dn, tab, (int)blockIdx.x, sync);
+  const int32_t t = (int32_t)tid_v();
+  const int32_t my_id = t < a.n_tokens ? a.ids[t] : -1;
+  if (a.n_tokens <= 64) group_wave(a, (uint32_t*)smem, my_id);
+  else group_lds(a, (uint32_t*)smem, my_id);
+  __syncthreads();
+  const uint32_t n_items = s_ghdr[0], wtot = s_ghdr[1];
+  // the phase's error word (the grouping writes it in workgroup 0 only):
+  // tokens with an id out of range, descriptors that disagree with the call
+  for (uint32_t q = (uint32_t)t; q < n_items; q += kFThreads)
+    if (const uint32_t err = desc_err(a.experts[s_items[q].x], a.rows, a.cols, a.minmax, image_tag(a)))
+      atomicOr(&s_ghdr[3], err);
+  __syncthreads();
+  if (t == 0) a.ws[0] = (((uint32_t)a.n_tokens - s_ghdr[2]) & kErrCountMask) | s_ghdr[3];
+  const WsLayout L = ws_layout(a.n_experts, a.n_tokens);
+  int32_t* perm = (int32_t*)(a.ws + L.perm);
+  uint4* items = (uint4*)(a.ws + L.items);
+  uint64_t* bounds = (uint64_t*)(a.ws + L.bounds);
+  for (int32_t i = t; i < a.n_tokens; i += kFThreads) perm[i] = s_perm[i];
+  for (uint32_t q = (uint32_t)t; q < n_items; q += kFThreads) items[q] = s_items[q];
+  const uint64_t wall = (uint64_t)wtot * (uint64_t)a.rows + (uint64_t)n_items * a.item_cost;
+  for (int32_t g = t; g <= a.grid; g += kFThreads)
+    bounds[g] = weighted_boundary(s_items, n_items, wtot, a.rows, a.item_cost,
+                                  wall * (uint64_t)g / (uint64_t)a.grid);
+}
+
 // ------------------------------------------------------------ host entries
 struct DevInfo {
   int cus = 0;
@@ -2546,7 +2579,15 @@ static int layers_call(const sbm_projection* up, const sbm_projection* down, int
   tab.ws_words = (uint32_t)(phase_bytes / 4u);
   tab.n_layers = n_layers;
   hipStream_t s = (hipStream_t)stream;
-  if (!ua.group_in_lds) {
+  if (ua.group_in_lds && n_layers > 1) {
+    // every phase grouped ahead by one launch (the layer launch then groups
+    // nothing; with one layer, grouping inside the layer launch is faster)
+    hipLaunchKernelGGL(stack_plan_kernel, dim3((unsigned)(2 * n_layers)), dim3(kFThreads), kGroupScratch, s, ua, da,
+                       tab, sync);
+    const hipError_t pe = hipGetLastError();
+    if (pe != hipSuccess) return fail(SBM_EHIP, "grouping launch: %s", hipGetErrorString(pe));
+    ua.group_in_lds = da.group_in_lds = 0;
+  } else if (!ua.group_in_lds) {
     // more tokens than the in-kernel grouping takes: every phase grouped by
     // one launch, each into its phase's part of the workspace
     hipLaunchKernelGGL(stack_group_kernel, dim3((unsigned)(2 * n_layers)), dim3(kThreads), 0, s, ua, da, tab, sync);
