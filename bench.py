@@ -770,7 +770,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "traffic_source": traffic_src,
                 "kernel": f"sbm::stack_kernel ({cfg.n_layers} layers of up + down in {n_launch} launch"
-                          f"{'es' if n_launch > 1 else ''}; token grouping inside)",
+                          f"{'es' if n_launch > 1 else ''}; the timed region also holds the planning launch "
+                          f"sbm::stack_plan_kernel that groups every phase, ~6 us)",
                 "avg_launch_us": round(launch_us, 2),
                 "bytes_per_launch": int(bytes_per_launch),
                 "avg_projection_us": round(launch_us * n_launch / (2 * cfg.n_layers), 2),
