@@ -293,7 +293,8 @@ size_t sbm_ffn_workspace_bytes(int32_t n_experts, int32_t n_tokens);
  * decoded on the fly as in sbm_moe_fused_decode_matvec.  The down rows of a
  * token start once all of its up rows are written (per-token counts in the
  * workspace; h is written and read coherently at device scope), so a layer
- * takes one launch instead of two.  up, down: host structs of device arrays
+ * takes one launch instead of two (with more than 128 tokens, after a
+ * grouping launch).  up, down: host structs of device arrays
  * with the same experts; up->rows == down->cols; both cols even and >= 512
  * (narrower rows: two sbm_moe_fused_decode_matvec calls).  x: device fp16
  * (bf16 with SBM_F_IN_BF16) [n_tokens x up->cols]; h: device fp16
@@ -316,7 +317,7 @@ int sbm_moe_fused_ffn(const sbm_projection* up, const sbm_projection* down, cons
 /* Workspace bytes of sbm_moe_fused_layers. */
 size_t sbm_layers_workspace_bytes(int32_t n_layers, int32_t n_experts, int32_t n_tokens);
 
-/* [QMoE] "The GPU Decoding Kernel" for n_layers MoE layers in one launch: for
+/* [QMoE] "The GPU Decoding Kernel" for n_layers MoE layers in one layer launch: for
  * l = 0 .. n_layers-1 and every token t with e = expert_ids[l * n_tokens + t],
  *   x_0 = x,  x_l = y_{l-1} / rms(y_{l-1}) per token for l >= 1
  *   h[t, :]   = relu( W_up_{l,e} x_l[t, :] )
@@ -324,9 +325,11 @@ size_t sbm_layers_workspace_bytes(int32_t n_layers, int32_t n_experts, int32_t n
  * as sbm_moe_fused_ffn computes each layer (the RMS scaling between layers is
  * the one SBM_F_IN_RMS applies; with the flag, layer 0's input is scaled too).
  * Every layer's routing is an input.  A workgroup prepares each projection
- * (token grouping, chunk table, first code blocks) while the previous one is
- * still finishing elsewhere, and starts a token's rows as soon as that
- * token's input rows are all written.  up, down: arrays of n_layers host
+ * (chunk table, first code blocks) while the previous one is still finishing
+ * elsewhere, and starts a token's rows as soon as that token's input rows are
+ * all written.  The tokens of every projection are grouped by a short launch
+ * before the layer launch (with one layer and at most 128 tokens, inside the
+ * layer launch instead), all on `stream`.  up, down: arrays of n_layers host
  * structs (1 <= n_layers <= 32; longer stacks: one call per 32 layers), all
  * layers of layer 0's shapes, up->rows == down->cols and down->rows ==
  * up->cols when n_layers > 1, cols even and >= 512.  expert_ids: device int32
