@@ -1624,8 +1624,8 @@ __device__ __forceinline__ void run_slice(const FusedArgs& a, unsigned char* sme
         }
         cur_q = nx.q;
       }
-      // Published rows: with the in-LDS grouping their per-token counts are
-      // gathered in LDS and raised once, at the end of the slice, after a
+      // Published rows: with at most kGroupInLds tokens their per-token counts
+      // are gathered in LDS and raised once, at the end of the slice, after a
       // single wait for the stores (a wait per chunk would hold up the next
       // chunk's blocks); otherwise raised here, once the chunk's rows are stored.
       const bool pub = lm_out<LM>(a), pend = pub && a.n_tokens <= kGroupInLds;
