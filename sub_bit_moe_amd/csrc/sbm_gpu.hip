@@ -1337,8 +1337,8 @@ __device__ __attribute__((noinline)) void mfma_chunk(const FusedArgs& a, unsigne
 constexpr int kMaxChunks = 16;
 __shared__ Chunk s_chunks[kMaxChunks];
 __shared__ uint32_t s_nchunks, s_nseq, s_next_seq;
-// Rows published per token and not yet counted (layer calls, in-LDS grouping;
-// zero between slices).
+// Rows published per token and not yet counted (layer calls of at most
+// kGroupInLds tokens; zero between slices).
 __shared__ uint32_t s_pend[kGroupInLds];
 __shared__ uint64_t s_gnext;
 
