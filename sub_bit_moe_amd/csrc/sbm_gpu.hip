@@ -83,6 +83,7 @@ constexpr int kMaxGrid = 1024;    // fused-kernel workgroups with precomputed sl
 // items could hold, at most one per CU.
 constexpr int64_t kRowsPerGroup = 16;
 constexpr int kItemChangeBlocks = 20;   // measured: a chunk change costs ~16 one-token blocks
+constexpr int kLayerItemChangeBlocks = 24;   // the same in a layer call's phases (best of 12..48 measured)
 // Heavy experts (at least kMfmaMinTokens tokens) take the dense-tile MFMA path:
 // items of up to kMfmaMaxTokens tokens, flagged in the item's token-count word.
 constexpr uint32_t kItemMfma = 0x80000000u;
@@ -2567,6 +2568,10 @@ static int layers_call(const sbm_projection* up, const sbm_projection* down, int
   fill_args(da, down->codes, down->row_off, down->bstart, down->scales, down->experts, down->n_experts, down->rows,
             down->cols, dict_image, h, expert_ids, n_tokens, y, flags & SBM_F_OUT_F32, ws0 + phase_bytes, pd, grid_d);
   ua.sync_err = da.sync_err = sync + 1;
+  // a layer call's phases weigh an item change a little more (its staging
+  // waits for other workgroups' rows)
+  ua.item_cost = ua.item_cost * kLayerItemChangeBlocks / kItemChangeBlocks;
+  da.item_cost = da.item_cost * kLayerItemChangeBlocks / kItemChangeBlocks;
   da.x_bytes = (uint32_t)((uint64_t)n_tokens * (uint64_t)down->cols * 2u);
   LayerTab tab;
   memset(&tab, 0, sizeof(tab));
