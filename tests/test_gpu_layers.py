@@ -157,10 +157,12 @@ def _oracle_rows(cfg, layer, e, mat, rsel, inp):
     return P.oracle_matvec_from_symbols(sym, sc, np.asarray(inp, np.float16)[None, :])[0]
 
 
-@pytest.mark.parametrize("T", [20, 150])
+@pytest.mark.parametrize("T", [20, 100, 150])
 def test_layers_error_paths(dev, odict, T):
     """Out-of-range ids (counted once per layer, no rows); a damaged image
-    (nothing computed, bit 31); the workspace is left ready either way."""
+    (nothing computed, bit 31); the workspace is left ready either way.  T =
+    20 and 100: the planning launch's one-wave and workgroup grouping; 150:
+    the grouping kernel."""
     from sub_bit_moe_amd import api
     L, E, d, f = 2, 4, 512, 768
     ups, downs, su, sd, image = _host_layers(odict, dev, L, E, d, f, 31)
